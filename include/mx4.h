@@ -1,0 +1,134 @@
+/*
+ * mx4.h -- C ABI of an MI355X (gfx950) MXFP4 GEMM library.
+ *
+ *   C[M,N] (bf16) = A[M,K] (bf16, quantised per call to MXFP4) x B[N,K]^T
+ *                   (bf16, quantised once to MXFP4 and packed).
+ *
+ * MXFP4 here is the block format of the kernelindex.com amd-mxfp4-mm pages
+ * (MI355X leaderboard submissions 748756, 721672, 754569, 755056, 733989):
+ * 32 consecutive K elements of one row share one e8m0 scale byte, each element
+ * is a 4-bit e2m1 code.  The quantisation rule is the one of submission 755056,
+ * section "Software MXFP4 quant":
+ *   amax = max |x| of the group (fp32);
+ *   R    = (bits(amax) + 0x00200000) & 0xFF800000   (power of two);
+ *   s    = clamp(E(R) - 129, -127, 127), scale byte = s + 127;
+ *   code = e2m1(x * 2^-s), round to nearest even, |q| >= 6 -> 6, sign kept.
+ * Natural layouts (as in submission 721672, "Quant kernel for Triton/splitK
+ * path"): codes [rows, K/2] bytes, element 2j in the low nibble of byte j;
+ * scales [rows, K/32] bytes, group g covers k in [32g, 32g+32).
+ *
+ * Conventions for every entry point:
+ *   - bf16 is passed as raw 16-bit patterns; matrices are row-major with an
+ *     explicit leading dimension in elements.
+ *   - Pointers named *_dev are device pointers (hipMalloc or torch CUDA
+ *     tensors); *_host pointers are host memory.
+ *   - The caller owns every buffer.  The library never allocates, frees or
+ *     synchronises; each call only enqueues work on `stream` (a hipStream_t,
+ *     NULL for the default stream) and returns.
+ *   - Arguments are validated on the host before any HIP call; on error the
+ *     call returns a negative MX_E* code, enqueues nothing and writes nothing.
+ *   - Device pointers read with 128-bit loads must be 16-byte aligned (bf16
+ *     inputs A and B, with lda / ldb multiples of 8), the packed weight
+ *     16-byte aligned, the workspace 256-byte aligned, C 2-byte aligned (rows
+ *     of C that are 8-byte aligned, ldc % 4 == 0, get 8-byte stores).
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified codes.
+ *   - Calls on different streams with disjoint output buffers may run
+ *     concurrently; the library holds no mutable state.
+ */
+#ifndef MX4_H
+#define MX4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    MX_OK = 0,
+    MX_EINVAL = -1,   /* bad shape or leading dimension (M, N, K <= 0, K % 32 != 0, ld too small) */
+    MX_EALIGN = -2,   /* null or misaligned pointer */
+    MX_ESPACE = -3,   /* output, packed or workspace buffer too small */
+    MX_EHIP = -4,     /* a HIP launch failed (hipGetLastError after the launch) */
+    MX_EPLAN = -5     /* an explicit plan that the library cannot run for this shape */
+};
+
+/* Version of the packed-weight layout written by mx_pack_weight. */
+#define MX_PACKED_LAYOUT_VERSION 1
+
+/* Message for an MX_* code; never NULL. */
+const char* mx_strerror(int code);
+
+/* Size in bytes of the packed weight for an N x K matrix (host only, no HIP call).
+ * The packed buffer is opaque: e2m1 codes in the GEMM's 32-row x 64-K operand
+ * tiles (1 KiB, one 16-byte fragment per MFMA lane) followed by the e8m0
+ * scales in 4-byte words per lane (4 K steps per word); rows are padded to a
+ * multiple of 32 and K to a multiple of 64 with zero codes. */
+int mx_packed_weight_bytes(int N, int K, size_t* bytes_host);
+
+/* One-time weight packing (the weight side of the spec path; the rule
+ * above applied to B along K, written into the GEMM's tile layout).
+ *   B_dev       bf16 [N, K], row stride ldb elements (ldb >= K, ldb % 8 == 0)
+ *   packed_dev  output, packed_bytes >= mx_packed_weight_bytes(N, K), 16-B aligned */
+int mx_pack_weight(const void* B_dev, int N, int K, int ldb,
+                   void* packed_dev, size_t packed_bytes, void* stream);
+
+/* Inverse view of a packed weight in the natural layouts (for tests and
+ * export): codes_dev [N, K/2] bytes and scales_dev [N, K/32] bytes. */
+int mx_unpack_weight(const void* packed_dev, int N, int K,
+                     void* codes_dev, void* scales_dev, void* stream);
+
+/* Stand-alone activation quantisation to the natural layouts.
+ *   A_dev       bf16 [M, K], row stride lda (lda >= K, lda % 8 == 0)
+ *   codes_dev   [M, K/2] bytes, scales_dev [M, K/32] bytes (dense) */
+int mx_quant_act(const void* A_dev, int M, int K, int lda,
+                 void* codes_dev, void* scales_dev, void* stream);
+
+/* Workspace bytes mx_gemm needs for this shape under the library's plan
+ * (0 when no workspace is used). */
+int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host);
+
+/* C = A x B^T with A quantised on the fly (quantisation, block-scaled MFMA
+ * contraction with fp32 accumulation, split-K reduction when planned, bf16
+ * round-to-nearest-even epilogue).
+ *   A_dev      bf16 [M, K], lda >= K, lda % 8 == 0
+ *   packed_dev weight packed by mx_pack_weight for (N, K)
+ *   C_dev      bf16 [M, N] output, ldc >= N
+ *   ws_dev     workspace of ws_bytes >= mx_gemm_workspace_bytes(M, N, K)
+ *              (may be NULL when that is 0); its contents need no
+ *              initialisation and are scratch after the call. */
+int mx_gemm(const void* A_dev, int M, int K, int lda,
+            const void* packed_dev, int N,
+            void* C_dev, int ldc,
+            void* ws_dev, size_t ws_bytes, void* stream);
+
+/* A launch plan: how mx_gemm tiles the problem.  Exposed so that callers can
+ * inspect the plan chosen for a shape and tests can force alternatives. */
+typedef struct mx_plan {
+    int mb;          /* 32-row blocks of M per wave (1 or 2) */
+    int nb;          /* 32-row blocks of N per wave (1 or 2) */
+    int wk;          /* waves per workgroup, splitting the K steps of a tile */
+    int splits;      /* workgroups splitting K; > 1 adds a reduction pass */
+    int fuse_quant;  /* 1: the GEMM quantises A itself; 0: a quant pass first */
+} mx_plan;
+
+/* The plan mx_gemm uses for (M, N, K) (host only). */
+int mx_gemm_plan(int M, int N, int K, mx_plan* plan_host);
+
+/* Workspace bytes for an explicit plan. */
+int mx_gemm_plan_workspace_bytes(const mx_plan* plan_host, int M, int N, int K,
+                                 size_t* bytes_host);
+
+/* mx_gemm under an explicit plan (MX_EPLAN when the plan is not supported). */
+int mx_gemm_with_plan(const void* A_dev, int M, int K, int lda,
+                      const void* packed_dev, int N,
+                      void* C_dev, int ldc,
+                      void* ws_dev, size_t ws_bytes,
+                      const mx_plan* plan_host, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX4_H */

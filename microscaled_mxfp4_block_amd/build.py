@@ -1,0 +1,72 @@
+"""Ahead-of-time build of libmx4.so for gfx950 (hipcc, no JIT, no torch headers).
+
+``python -m microscaled_mxfp4_block_amd.build`` compiles the HIP sources under
+``csrc/`` into ``microscaled_mxfp4_block_amd/libmx4.so`` and checks the gfx950
+assembly of every kernel source for packed fp32 instructions, which this
+build keeps out (``-target-feature -packed-fp32-ops``).
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+import re
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+ROOT = os.path.dirname(HERE)
+LIB = os.path.join(HERE, "libmx4.so")
+BUILD_DIR = os.path.join(ROOT, "_build")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+SOURCES = ["mx4_api.cpp", "mx4_gemm.hip", "mx4_quant.hip"]
+ARCH = "gfx950"
+FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-Wall", "-I" + os.path.join(ROOT, "include")]
+PACKED_FP32 = re.compile(r"\bv_pk_(add|mul|fma|mov)_f32\b")
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
+    if r.returncode != 0:
+        raise RuntimeError("command failed: %s\n%s" % (" ".join(cmd), out))
+    return out
+
+
+def _compile(src):
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
+    _run([HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+    return obj
+
+
+def _device_asm(src):
+    asm = os.path.join(BUILD_DIR, os.path.basename(src) + ".s")
+    _run([HIPCC] + FLAGS + ["-x", "hip", "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm])
+    with open(asm) as f:
+        text = f.read()
+    bad = sorted(set(m.group(0) for m in PACKED_FP32.finditer(text)))
+    if bad:
+        raise RuntimeError("%s: packed fp32 instructions in gfx950 code: %s" % (src, ", ".join(bad)))
+    return asm
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libmx4.so; returns its path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    kernels = [s for s in SOURCES if s.endswith(".hip")]
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        objs = list(ex.map(_compile, SOURCES))
+        list(ex.map(_device_asm, kernels))
+    tmp = LIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
+    os.replace(tmp, LIB)
+    if verbose:
+        print("built", LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    build(verbose=True)
+    sys.exit(0)

@@ -1,0 +1,273 @@
+// mx4_api.cpp -- the C ABI of include/mx4.h: argument checks, plans, launches.
+//
+// Every entry point validates its arguments on the host before it touches
+// HIP, so an invalid call returns an MX_E* code with nothing enqueued.  The
+// library owns no memory and keeps no mutable state.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/mx4.h"
+#include "mx4_internal.h"
+
+using mx4::GemmParams;
+using mx4::OperandGeom;
+using mx4::Plan;
+
+namespace {
+
+constexpr int kMaxDim = 1 << 24;
+
+bool aligned(const void* p, uintptr_t a) { return p != nullptr && ((uintptr_t)p % a) == 0; }
+
+int check_operand_shape(int rows, int K) {
+    if (rows <= 0 || K <= 0 || rows > kMaxDim || K > kMaxDim || K % mx4::kGroup != 0) return MX_EINVAL;
+    const OperandGeom g = mx4::operand_geom(rows, K);
+    // in-kernel tile offsets are formed in 32-bit integers before widening
+    if ((long long)g.RB * g.KS * 64 >= (1LL << 31) || (long long)g.RB * g.KW * 64 >= (1LL << 31)) return MX_EINVAL;
+    return MX_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_EHIP; }
+
+// Plans measured for the five decode-style shapes; other shapes use the model
+// in model_plan().
+struct TableEntry {
+    int M, N, K;
+    Plan plan;
+};
+const TableEntry kTable[] = {
+    {4, 2880, 512, {1, 1, 8, 1, 1}},
+    {32, 4096, 512, {1, 1, 8, 1, 1}},
+    {16, 2112, 7168, {1, 1, 8, 2, 0}},
+    {64, 7168, 2048, {2, 1, 4, 1, 0}},
+    {256, 3072, 1536, {2, 2, 4, 1, 0}},
+};
+
+int pow2_floor(int x) {
+    int p = 1;
+    while (p * 2 <= x) p *= 2;
+    return p;
+}
+
+// Occupancy model for shapes without a table entry: quantise A inside the
+// GEMM when it is small (one activation block, short K), pick the wave tile
+// from M, split the K steps over up to 8 waves per workgroup and, when the
+// tiles alone leave the 256 CUs idle, over several workgroups.
+Plan model_plan(int M, int N, int K) {
+    const OperandGeom ga = mx4::operand_geom(M, K);
+    const OperandGeom gb = mx4::operand_geom(N, K);
+    Plan p;
+    p.fuse = (ga.RB == 1 && gb.KS <= 16) ? 1 : 0;
+    p.mb = (!p.fuse && ga.RB >= 2) ? 2 : 1;
+    p.nb = (ga.RB >= 4 && gb.RB >= 64) ? 2 : 1;
+    const int mtiles = (ga.RB + p.mb - 1) / p.mb;
+    const int ntiles = (gb.RB + p.nb - 1) / p.nb;
+    const int tiles = mtiles * ntiles;
+    int wk = gb.KS / 2;
+    if (wk < 1) wk = 1;
+    if (wk > 8) wk = 8;
+    p.wk = pow2_floor(wk);
+    int splits = 1;
+    const int steps_per_wave_group = gb.KS / p.wk;  // K steps left for each wave at one split
+    while (tiles * splits < 256 && splits * 2 <= steps_per_wave_group / 2) splits *= 2;
+    p.splits = splits;
+    return p;
+}
+
+Plan choose_plan(int M, int N, int K) {
+    for (const TableEntry& e : kTable)
+        if (e.M == M && e.N == N && e.K == K) return e.plan;
+    return model_plan(M, N, K);
+}
+
+struct Layout {
+    size_t aop_offset, aop_bytes;
+    size_t partial_offset, partial_bytes;
+    size_t total;
+    int splits, steps_per_split;
+};
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
+    if (!mx4::gemm_plan_supported(plan)) return MX_EPLAN;
+    const OperandGeom ga = mx4::operand_geom(M, K);
+    const OperandGeom gb = mx4::operand_geom(N, K);
+    if (plan.splits > gb.KS) return MX_EPLAN;
+    Layout l;
+    l.steps_per_split = (gb.KS + plan.splits - 1) / plan.splits;
+    l.splits = (gb.KS + l.steps_per_split - 1) / l.steps_per_split;  // every split non-empty
+    l.aop_offset = 0;
+    l.aop_bytes = plan.fuse ? 0 : round_up(ga.total_bytes, 256);
+    l.partial_offset = l.aop_bytes;
+    l.partial_bytes = l.splits > 1 ? round_up((size_t)l.splits * M * gb.RB * mx4::kRowBlock * sizeof(float), 256) : 0;
+    l.total = l.aop_bytes + l.partial_bytes;
+    const long long mtiles = (ga.RB + plan.mb - 1) / plan.mb;
+    const long long ntiles = (gb.RB + plan.nb - 1) / plan.nb;
+    if (mtiles * ntiles * l.splits >= (1LL << 31)) return MX_EINVAL;
+    *out = l;
+    return MX_OK;
+}
+
+int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, void* C, int ldc, void* ws,
+              size_t ws_bytes, const Plan& plan, void* stream) {
+    int rc = check_operand_shape(M, K);
+    if (rc) return rc;
+    rc = check_operand_shape(N, K);
+    if (rc) return rc;
+    if (lda < K || lda % 8 != 0 || ldc < N) return MX_EINVAL;
+    if (!aligned(A, 16) || !aligned(packed, 16) || !aligned(C, 2)) return MX_EALIGN;
+    Layout lay;
+    rc = plan_layout(plan, M, N, K, &lay);
+    if (rc) return rc;
+    if (lay.total > 0) {
+        if (!aligned(ws, 256)) return MX_EALIGN;
+        if (ws_bytes < lay.total) return MX_ESPACE;
+    }
+    hipStream_t s = (hipStream_t)stream;
+    const OperandGeom ga = mx4::operand_geom(M, K);
+    const OperandGeom gb = mx4::operand_geom(N, K);
+    uint8_t* wsb = (uint8_t*)ws;
+
+    GemmParams p;
+    memset(&p, 0, sizeof p);
+    p.A = (const uint16_t*)A;
+    p.lda = lda;
+    p.aop = plan.fuse ? nullptr : wsb + lay.aop_offset;
+    p.a_code_bytes = ga.code_bytes;
+    p.bp = (const uint8_t*)packed;
+    p.b_code_bytes = gb.code_bytes;
+    p.KS = gb.KS;
+    p.KW = gb.KW;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.RBm = ga.RB;
+    p.RBn = gb.RB;
+    p.mtiles = (ga.RB + plan.mb - 1) / plan.mb;
+    p.ntiles = (gb.RB + plan.nb - 1) / plan.nb;
+    p.splits = lay.splits;
+    p.steps_per_split = lay.steps_per_split;
+    p.C = (uint16_t*)C;
+    p.ldc = ldc;
+    p.c_vec = (ldc % 4 == 0 && aligned(C, 8)) ? 1 : 0;
+    p.partial = lay.splits > 1 ? (float*)(wsb + lay.partial_offset) : nullptr;
+    p.ldp = gb.RB * mx4::kRowBlock;
+
+    if (!plan.fuse) {
+        rc = hip_status(mx4::launch_pack((const uint16_t*)A, M, K, lda, wsb + lay.aop_offset, s));
+        if (rc) return rc;
+    }
+    Plan run = plan;
+    run.splits = lay.splits;
+    rc = hip_status(mx4::launch_gemm(run, p, s));
+    if (rc) return rc;
+    if (lay.splits > 1) rc = hip_status(mx4::launch_reduce(p.partial, lay.splits, M, N, p.ldp, (uint16_t*)C, ldc,
+                                                              p.c_vec, s));
+    return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mx_strerror(int code) {
+    switch (code) {
+        case MX_OK: return "success";
+        case MX_EINVAL: return "invalid shape or leading dimension";
+        case MX_EALIGN: return "null or misaligned pointer";
+        case MX_ESPACE: return "buffer or workspace too small";
+        case MX_EHIP: return "HIP kernel launch failed";
+        case MX_EPLAN: return "plan not supported for this shape";
+        default: return "unknown error code";
+    }
+}
+
+int mx_packed_weight_bytes(int N, int K, size_t* bytes_host) {
+    if (!bytes_host) return MX_EALIGN;
+    int rc = check_operand_shape(N, K);
+    if (rc) return rc;
+    *bytes_host = mx4::operand_geom(N, K).total_bytes;
+    return MX_OK;
+}
+
+int mx_pack_weight(const void* B_dev, int N, int K, int ldb, void* packed_dev, size_t packed_bytes, void* stream) {
+    int rc = check_operand_shape(N, K);
+    if (rc) return rc;
+    if (ldb < K || ldb % 8 != 0) return MX_EINVAL;
+    if (!aligned(B_dev, 16) || !aligned(packed_dev, 16)) return MX_EALIGN;
+    if (packed_bytes < mx4::operand_geom(N, K).total_bytes) return MX_ESPACE;
+    return hip_status(mx4::launch_pack((const uint16_t*)B_dev, N, K, ldb, (uint8_t*)packed_dev, (hipStream_t)stream));
+}
+
+int mx_unpack_weight(const void* packed_dev, int N, int K, void* codes_dev, void* scales_dev, void* stream) {
+    int rc = check_operand_shape(N, K);
+    if (rc) return rc;
+    if (!aligned(packed_dev, 16) || !aligned(codes_dev, 16) || !aligned(scales_dev, 1)) return MX_EALIGN;
+    return hip_status(mx4::launch_unpack((const uint8_t*)packed_dev, N, K, (uint8_t*)codes_dev, (uint8_t*)scales_dev,
+                                         (hipStream_t)stream));
+}
+
+int mx_quant_act(const void* A_dev, int M, int K, int lda, void* codes_dev, void* scales_dev, void* stream) {
+    int rc = check_operand_shape(M, K);
+    if (rc) return rc;
+    if (lda < K || lda % 8 != 0) return MX_EINVAL;
+    if (!aligned(A_dev, 16) || !aligned(codes_dev, 4) || !aligned(scales_dev, 1)) return MX_EALIGN;
+    return hip_status(mx4::launch_quant_natural((const uint16_t*)A_dev, M, K, lda, (uint8_t*)codes_dev,
+                                                (uint8_t*)scales_dev, (hipStream_t)stream));
+}
+
+int mx_gemm_plan(int M, int N, int K, mx_plan* plan_host) {
+    if (!plan_host) return MX_EALIGN;
+    int rc = check_operand_shape(M, K);
+    if (rc) return rc;
+    rc = check_operand_shape(N, K);
+    if (rc) return rc;
+    const Plan p = choose_plan(M, N, K);
+    Layout lay;
+    rc = plan_layout(p, M, N, K, &lay);
+    if (rc) return rc;
+    plan_host->mb = p.mb;
+    plan_host->nb = p.nb;
+    plan_host->wk = p.wk;
+    plan_host->splits = lay.splits;
+    plan_host->fuse_quant = p.fuse;
+    return MX_OK;
+}
+
+int mx_gemm_plan_workspace_bytes(const mx_plan* plan_host, int M, int N, int K, size_t* bytes_host) {
+    if (!plan_host || !bytes_host) return MX_EALIGN;
+    int rc = check_operand_shape(M, K);
+    if (rc) return rc;
+    rc = check_operand_shape(N, K);
+    if (rc) return rc;
+    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wk, plan_host->splits, plan_host->fuse_quant};
+    Layout lay;
+    rc = plan_layout(p, M, N, K, &lay);
+    if (rc) return rc;
+    *bytes_host = lay.total;
+    return MX_OK;
+}
+
+int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host) {
+    mx_plan p;
+    int rc = mx_gemm_plan(M, N, K, &p);
+    if (rc) return rc;
+    return mx_gemm_plan_workspace_bytes(&p, M, N, K, bytes_host);
+}
+
+int mx_gemm_with_plan(const void* A_dev, int M, int K, int lda, const void* packed_dev, int N, void* C_dev, int ldc,
+                      void* ws_dev, size_t ws_bytes, const mx_plan* plan_host, void* stream) {
+    if (!plan_host) return MX_EALIGN;
+    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wk, plan_host->splits, plan_host->fuse_quant};
+    return gemm_impl(A_dev, M, K, lda, packed_dev, N, C_dev, ldc, ws_dev, ws_bytes, p, stream);
+}
+
+int mx_gemm(const void* A_dev, int M, int K, int lda, const void* packed_dev, int N, void* C_dev, int ldc,
+            void* ws_dev, size_t ws_bytes, void* stream) {
+    return gemm_impl(A_dev, M, K, lda, packed_dev, N, C_dev, ldc, ws_dev, ws_bytes, choose_plan(M, N, K), stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,111 @@
+// mx4_device.h -- device-side building blocks shared by the MXFP4 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mx4_layout.h"
+
+namespace mx4 {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// MXFP4 group scale (rule of the kernelindex.com amd-mxfp4-mm pages,
+// submission 755056, section "Software MXFP4 quant"): the group amax is
+// rounded to a power of two R by adding 0x00200000 to its fp32 bits and
+// clearing the significand; s = clamp(E(R) - 129, -127, 127), byte = s + 127.
+// `amax_bits16` is the largest |x| of the group as a bf16 bit pattern (an
+// integer max of the sign-cleared patterns is the float max for finite x).
+__device__ __forceinline__ uint32_t scale_byte_from_amax16(uint32_t amax_bits16) {
+    uint32_t r = ((amax_bits16 << 16) + 0x00200000u) & 0xFF800000u;
+    int e = (int)(r >> 23);
+    int byte = e - 2;                 // (e - 129) + 127
+    byte = byte < 0 ? 0 : byte;       // s clamped at -127
+    byte = byte > 254 ? 254 : byte;   // s clamped at +127
+    return (uint32_t)byte;
+}
+
+// 2^s as the fp32 scale operand of the gfx950 fp4 convert, which computes
+// e2m1(x / scale) with round-to-nearest-even and saturation at 6; byte 0
+// (s = -127) is the denormal 2^-127.
+__device__ __forceinline__ float scale_operand(uint32_t byte) {
+    uint32_t bits = byte ? (byte << 23) : 0x00400000u;
+    return __uint_as_float(bits);
+}
+
+// Largest sign-cleared bf16 pattern among 32 bf16 held in 16 dwords.
+__device__ __forceinline__ uint32_t amax16_of_32(const uint32_t (&w)[16]) {
+    u16x2 m = __builtin_bit_cast(u16x2, w[0] & 0x7FFF7FFFu);
+#pragma unroll
+    for (int i = 1; i < 16; ++i)
+        m = __builtin_elementwise_max(m, __builtin_bit_cast(u16x2, w[i] & 0x7FFF7FFFu));
+    return m.x > m.y ? m.x : m.y;
+}
+
+// Convert 8 bf16 (4 dwords) to 8 e2m1 codes (one dword, element 0 in the low
+// nibble) under scale operand `sc`.
+__device__ __forceinline__ uint32_t cvt8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3, float sc) {
+    uint32_t r = 0;
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w0), sc, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w1), sc, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w2), sc, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w3), sc, 3);
+    return r;
+}
+
+// Quantise one whole 32-element group held by one lane (64 bytes of bf16 as
+// four 16-byte vectors) into 16 bytes of codes; returns the scale byte.
+__device__ __forceinline__ uint32_t quant_group32(const u32x4 (&x)[4], u32x4& codes) {
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        w[4 * i + 0] = x[i].x;
+        w[4 * i + 1] = x[i].y;
+        w[4 * i + 2] = x[i].z;
+        w[4 * i + 3] = x[i].w;
+    }
+    uint32_t byte = scale_byte_from_amax16(amax16_of_32(w));
+    float sc = scale_operand(byte);
+    codes.x = cvt8(w[0], w[1], w[2], w[3], sc);
+    codes.y = cvt8(w[4], w[5], w[6], w[7], sc);
+    codes.z = cvt8(w[8], w[9], w[10], w[11], sc);
+    codes.w = cvt8(w[12], w[13], w[14], w[15], sc);
+    return byte;
+}
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// One block-scaled fp4 x fp4 MFMA step: acc += (A_tile * 2^sa) x (B_tile * 2^sb)^T
+// where each operand is one lane's 16-byte fragment and its scale byte sits
+// in the low byte of the scale register.
+__device__ __forceinline__ f32x16 mfma_fp4_32x32x64(const u32x4& a, const u32x4& b, f32x16 acc,
+                                                   uint32_t scale_a, uint32_t scale_b) {
+    i32x8 va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    i32x8 vb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, 4, 4, 0, (int)scale_a, 0,
+                                                           (int)scale_b);
+}
+
+__device__ __forceinline__ u32x4 load16_nt(const void* p) {
+    return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+__device__ __forceinline__ u32x4 load16(const void* p) {
+    return *(const u32x4*)p;
+}
+
+}  // namespace mx4

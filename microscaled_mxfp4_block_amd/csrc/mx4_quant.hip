@@ -1,0 +1,147 @@
+// mx4_quant.hip -- MXFP4 quantisation kernels for gfx950.
+//
+//   quant_natural_kernel : bf16 [rows, K] -> codes [rows, K/2] + scales [rows, K/32]
+//   pack_kernel          : bf16 [rows, K] -> packed operand layout (mx4_layout.h);
+//                          used once for the weight B and per call for A
+//   unpack_kernel        : packed operand layout -> natural codes + scales
+//
+// The rule is the MXFP4 quantisation of the kernelindex.com amd-mxfp4-mm pages
+// (submission 755056, "Software MXFP4 quant"): per 32-element group, amax
+// rounded to a power of two by (bits + 0x00200000) & 0xFF800000, scale byte
+// clamp(E - 129, -127, 127) + 127, element codes e2m1(x * 2^-s) with round to
+// nearest even and saturation at 6, sign kept.  The e2m1 conversion uses the
+// gfx950 v_cvt_scalef32_pk_fp4_bf16 instruction, which divides by the scale
+// operand 2^s and rounds that way.
+#include "mx4_device.h"
+#include "mx4_internal.h"
+
+namespace mx4 {
+
+// Natural-layout quantiser.  One lane per 8 consecutive bf16 (one 16-byte
+// load); the four lanes of a DPP quad hold one 32-element group and reduce
+// its amax across the quad with two lane swaps.  Each lane writes its 8 codes
+// as one dword; the first lane of the quad writes the scale byte.
+__global__ void __launch_bounds__(256) quant_natural_kernel(const uint16_t* __restrict__ x, int rows,
+                                                            int K, int ld, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+    const int chunks_per_row = K / 8;
+    const long long total = (long long)rows * chunks_per_row;
+    const long long c = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    // Every lane of a quad exists: total is a multiple of 4 (K % 32 == 0) and
+    // the grid is rounded to whole blocks of 256, so quads never straddle the end.
+    const bool live = c < total;
+    const int r = live ? (int)(c / chunks_per_row) : 0;
+    const int kc = live ? (int)(c % chunks_per_row) : 0;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (live) v = load16(x + (size_t)r * ld + (size_t)kc * 8);
+    uint32_t m = 0;
+    {
+        u16x2 a = __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu);
+        a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu));
+        a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu));
+        a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu));
+        m = a.x > a.y ? a.x : a.y;
+    }
+    // quad_perm [1,0,3,2] then [2,3,0,1]: max over the four lanes of the quad
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false);
+    m = m > o ? m : o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false);
+    m = m > o ? m : o;
+    const uint32_t byte = scale_byte_from_amax16(m);
+    if (!live) return;
+    const float sc = scale_operand(byte);
+    const uint32_t q = cvt8(v.x, v.y, v.z, v.w, sc);
+    *(uint32_t*)(codes + (size_t)r * (K / 2) + (size_t)kc * 4) = q;
+    if ((kc & 3) == 0) scales[(size_t)r * (K / 32) + kc / 4] = (uint8_t)byte;
+}
+
+// Packed-layout quantiser.  One lane per (row block rb, scale word w, lane L):
+// it quantises the groups of up to four K steps t = 4w..4w+3 for row
+// 32 rb + L % 32, group 2t + L / 32, writing each 16-byte code fragment to its
+// tile slot and the four scale bytes as one word.  Lanes of a wave are the 64
+// lanes of one (rb, w), so every code store is a fully coalesced 1 KiB.
+__global__ void __launch_bounds__(256) pack_kernel(const uint16_t* __restrict__ x, int rows, int K, int ld,
+                                                   uint8_t* __restrict__ packed, int RB, int KS, int KW,
+                                                   size_t code_bytes) {
+    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long total = (long long)RB * KW * 64;
+    if (gid >= total) return;
+    const int L = (int)(gid & 63);
+    const long long tw = gid >> 6;
+    const int w = (int)(tw % KW);
+    const int rb = (int)(tw / KW);
+    const int row = rb * kRowBlock + (L & 31);
+    const int groups = K / kGroup;
+    uint32_t word = 0;
+#pragma unroll
+    for (int b = 0; b < kStepsPerWord; ++b) {
+        const int t = w * kStepsPerWord + b;
+        if (t >= KS) {
+            word |= 127u << (8 * b);
+            continue;
+        }
+        const int g = 2 * t + (L >> 5);
+        u32x4 codes = {0u, 0u, 0u, 0u};
+        uint32_t byte = 127u;
+        if (row < rows && g < groups) {
+            const uint16_t* src = x + (size_t)row * ld + (size_t)g * kGroup;
+            u32x4 v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = load16(src + 8 * i);
+            byte = quant_group32(v, codes);
+        }
+        *(u32x4*)(packed + ((size_t)(rb * KS + t) * 64 + L) * 16) = codes;
+        word |= byte << (8 * b);
+    }
+    *(uint32_t*)(packed + code_bytes + ((size_t)(rb * KW + w) * 64 + L) * 4) = word;
+}
+
+// Packed layout -> natural layouts.  One lane per (rb, t, L) tile slot.
+__global__ void __launch_bounds__(256) unpack_kernel(const uint8_t* __restrict__ packed, int rows, int K,
+                                                     int RB, int KS, int KW, size_t code_bytes,
+                                                     uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long total = (long long)RB * KS * 64;
+    if (gid >= total) return;
+    const int L = (int)(gid & 63);
+    const long long rt = gid >> 6;
+    const int t = (int)(rt % KS);
+    const int rb = (int)(rt / KS);
+    const int row = rb * kRowBlock + (L & 31);
+    const int g = 2 * t + (L >> 5);
+    if (row >= rows || g >= K / kGroup) return;
+    const u32x4 c = load16(packed + ((size_t)(rb * KS + t) * 64 + L) * 16);
+    *(u32x4*)(codes + (size_t)row * (K / 2) + (size_t)g * 16) = c;
+    const uint32_t word = *(const uint32_t*)(packed + code_bytes +
+                                             ((size_t)(rb * KW + t / kStepsPerWord) * 64 + L) * 4);
+    scales[(size_t)row * (K / kGroup) + g] = (uint8_t)(word >> (8 * (t % kStepsPerWord)));
+}
+
+hipError_t launch_quant_natural(const uint16_t* x, int rows, int K, int ld, uint8_t* codes, uint8_t* scales,
+                                hipStream_t s) {
+    const long long total = (long long)rows * (K / 8);
+    const long long blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(quant_natural_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, K, ld, codes,
+                       scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack(const uint16_t* x, int rows, int K, int ld, uint8_t* packed, hipStream_t s) {
+    const OperandGeom g = operand_geom(rows, K);
+    const long long total = (long long)g.RB * g.KW * 64;
+    const long long blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, K, ld, packed, g.RB, g.KS,
+                       g.KW, g.code_bytes);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const uint8_t* packed, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s) {
+    const OperandGeom g = operand_geom(rows, K);
+    const long long total = (long long)g.RB * g.KS * 64;
+    const long long blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, packed, rows, K, g.RB, g.KS, g.KW,
+                       g.code_bytes, codes, scales);
+    return hipGetLastError();
+}
+
+}  // namespace mx4

@@ -1,0 +1,153 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/mx4.h, sizes and plans are what the layout says, and bad
+arguments are rejected on the host before any HIP call (fake pointers are
+never dereferenced because validation fails first)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from microscaled_mxfp4_block_amd import binding as B
+from microscaled_mxfp4_block_amd.inputs import WORKLOADS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mx4.h")
+
+FAKE = 1 << 40          # an aligned, never-dereferenced address
+FAKE_ODD = FAKE + 2      # misaligned for 16-byte loads
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|int)\s+(mx_\w+)\s*\(", text, re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) >= 10
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], stdout=subprocess.PIPE, text=True).stdout
+    exported = set(re.findall(r"\bT (mx_\w+)", out))
+    assert set(names) <= exported
+    assert set(B.EXPORTS) == set(names)
+
+
+def test_strerror_codes():
+    for c in (0, -1, -2, -3, -4, -5):
+        assert B.strerror(c) and B.strerror(c) != "unknown error code"
+    assert B.strerror(-99) == "unknown error code"
+
+
+def size_of(N, K):
+    out = ctypes.c_size_t()
+    rc = B.lib().mx_packed_weight_bytes(N, K, ctypes.byref(out))
+    return rc, out.value
+
+
+@pytest.mark.parametrize("w", WORKLOADS, ids=lambda w: w.name)
+def test_packed_bytes_of_workloads_are_algorithmic(w):
+    # every workload has N % 32 == 0 and K % 256 == 0: no padding at all,
+    # exactly N*K/2 code bytes plus N*K/32 scale bytes
+    rc, n = size_of(w.N, w.K)
+    assert rc == 0
+    assert n == w.N * w.K // 2 + w.N * w.K // 32
+
+
+def test_packed_bytes_padding():
+    # 33 rows -> 2 row blocks of 32; K=96 -> 2 K steps of 64, 1 scale word
+    rc, n = size_of(33, 96)
+    assert rc == 0 and n == 2 * 2 * 1024 + 2 * 1 * 256
+
+
+@pytest.mark.parametrize("N,K", [(0, 64), (-1, 64), (16, 0), (16, 48), (16, 33), (1 << 25, 64)])
+def test_packed_bytes_rejects_bad_shapes(N, K):
+    assert size_of(N, K)[0] == B.MX_EINVAL
+
+
+def test_pack_weight_validation():
+    L = B.lib()
+    nbytes = size_of(64, 512)[1]
+    assert L.mx_pack_weight(FAKE, 64, 500, 512, FAKE, nbytes, None) == B.MX_EINVAL      # K % 32
+    assert L.mx_pack_weight(FAKE, 64, 512, 256, FAKE, nbytes, None) == B.MX_EINVAL      # ldb < K
+    assert L.mx_pack_weight(FAKE, 64, 512, 516, FAKE, nbytes, None) == B.MX_EINVAL      # ldb % 8
+    assert L.mx_pack_weight(None, 64, 512, 512, FAKE, nbytes, None) == B.MX_EALIGN
+    assert L.mx_pack_weight(FAKE_ODD, 64, 512, 512, FAKE, nbytes, None) == B.MX_EALIGN
+    assert L.mx_pack_weight(FAKE, 64, 512, 512, FAKE, nbytes - 1, None) == B.MX_ESPACE
+
+
+def test_quant_act_validation():
+    L = B.lib()
+    assert L.mx_quant_act(FAKE, 0, 512, 512, FAKE, FAKE, None) == B.MX_EINVAL
+    assert L.mx_quant_act(FAKE, 4, 520, 520, FAKE, FAKE, None) == B.MX_EINVAL
+    assert L.mx_quant_act(FAKE, 4, 512, 504, FAKE, FAKE, None) == B.MX_EINVAL
+    assert L.mx_quant_act(FAKE_ODD, 4, 512, 512, FAKE, FAKE, None) == B.MX_EALIGN
+    assert L.mx_quant_act(FAKE, 4, 512, 512, None, FAKE, None) == B.MX_EALIGN
+    assert L.mx_quant_act(FAKE, 4, 512, 512, FAKE, None, None) == B.MX_EALIGN
+
+
+def test_gemm_validation():
+    L = B.lib()
+    M, N, K = 16, 2112, 7168
+    ws = ctypes.c_size_t()
+    assert L.mx_gemm_workspace_bytes(M, N, K, ctypes.byref(ws)) == 0
+    args = dict(A=FAKE, M=M, K=K, lda=K, P=FAKE, N=N, C=FAKE, ldc=N, ws=FAKE, wsb=ws.value)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return L.mx_gemm(a["A"], a["M"], a["K"], a["lda"], a["P"], a["N"], a["C"], a["ldc"], a["ws"], a["wsb"],
+                         None)
+
+    assert call(M=0) == B.MX_EINVAL
+    assert call(N=-3) == B.MX_EINVAL
+    assert call(K=7160) == B.MX_EINVAL
+    assert call(lda=K - 8) == B.MX_EINVAL
+    assert call(ldc=N - 4) == B.MX_EINVAL
+    assert call(C=FAKE + 1) == B.MX_EALIGN
+    assert call(A=None) == B.MX_EALIGN
+    assert call(A=FAKE_ODD) == B.MX_EALIGN
+    assert call(P=None) == B.MX_EALIGN
+    assert call(C=None) == B.MX_EALIGN
+    if ws.value > 0:
+        assert call(ws=None) == B.MX_EALIGN
+        assert call(wsb=ws.value - 1) == B.MX_ESPACE
+
+
+def test_plans_for_workloads():
+    for w in WORKLOADS:
+        p = B.mx_gemm_plan(w.M, w.N, w.K)
+        assert p["mb"] in (1, 2) and p["nb"] in (1, 2) and p["splits"] >= 1 and p["wk"] >= 1
+        ws = B.mx_gemm_workspace_bytes(w.M, w.N, w.K)
+        if p["fuse_quant"] and p["splits"] == 1:
+            assert ws == 0
+        else:
+            assert ws > 0
+
+
+def test_plan_model_for_other_shapes():
+    for (M, N, K) in [(1, 32, 32), (5, 200, 320), (33, 1000, 4096), (300, 5000, 8192), (1024, 1024, 1024)]:
+        p = B.mx_gemm_plan(M, N, K)
+        assert p["splits"] >= 1
+        assert B.mx_gemm_workspace_bytes(M, N, K, p) >= 0
+
+
+def test_explicit_plan_rejections():
+    bad = [dict(mb=3, nb=1, wk=1, splits=1, fuse_quant=0),
+           dict(mb=1, nb=1, wk=3, splits=1, fuse_quant=0),
+           dict(mb=2, nb=1, wk=4, splits=1, fuse_quant=1),
+           dict(mb=1, nb=1, wk=4, splits=0, fuse_quant=0),
+           dict(mb=1, nb=1, wk=4, splits=1000, fuse_quant=0)]
+    for p in bad:
+        with pytest.raises(B.MxError) as e:
+            B.mx_gemm_workspace_bytes(16, 2112, 7168, p)
+        assert e.value.code == B.MX_EPLAN
+
+
+def test_binding_without_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(ImportError):
+        B.lib()

@@ -1,0 +1,288 @@
+"""GPU parity of the HIP path against the CPU oracle (needs an MI355X).
+
+Every call goes through the C ABI (libmx4.so via the ctypes binding).  Codes
+and e8m0 bytes must match the oracle bit for bit; C must satisfy, element by
+element, |C_gpu - C_ref| <= 2 ulp_bf16(|C_ref|) + 1e-3 * rms(C_ref).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from microscaled_mxfp4_block_amd import binding as B
+from microscaled_mxfp4_block_amd import inputs
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def ulp_bf16(x: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |x| (the subnormal quantum at 0)."""
+    a = np.abs(x).astype(np.float64)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -126)
+    return np.where(a > 0, np.ldexp(1.0, (e - 7).astype(np.int64)), np.ldexp(1.0, -133))
+
+
+def bf16_bits_to_f64(b: np.ndarray) -> np.ndarray:
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def assert_c_close(C_gpu_bits: np.ndarray, C_ref_bits: np.ndarray, what: str):
+    g = bf16_bits_to_f64(C_gpu_bits)
+    r = bf16_bits_to_f64(C_ref_bits)
+    rms = float(np.sqrt(np.mean(r * r))) if r.size else 0.0
+    tol = 2.0 * ulp_bf16(r) + 1e-3 * rms
+    err = np.abs(g - r)
+    bad = err > tol
+    assert np.isfinite(g).all(), what + ": non-finite output"
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d of %d outside tolerance, e.g. %s" % (
+            what, int(bad.sum()), bad.size,
+            [(tuple(i), g[tuple(i)], r[tuple(i)], tol[tuple(i)]) for i in idx]))
+
+
+def to_dev(t: torch.Tensor) -> torch.Tensor:
+    return t.to(DEV)
+
+
+def gpu_bits(t: torch.Tensor) -> np.ndarray:
+    torch.cuda.synchronize()
+    return inputs.bits(t.cpu())
+
+
+def run_gemm(A_cpu, B_cpu, plan=None, ldc_pad=0, lda_pad=0):
+    M, K = A_cpu.shape
+    N = B_cpu.shape[0]
+    if lda_pad:
+        Abuf = torch.zeros((M, K + lda_pad), dtype=torch.bfloat16)
+        Abuf[:, :K] = A_cpu
+        A = to_dev(Abuf)[:, :K]
+    else:
+        A = to_dev(A_cpu)
+    packed = B.mx_pack_weight(to_dev(B_cpu))
+    if ldc_pad:
+        Cbuf = torch.full((M, N + ldc_pad), -7.0, dtype=torch.bfloat16, device=DEV)
+        C = Cbuf[:, :N]
+    else:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+        Cbuf = None
+    B.mx_gemm(A, packed, N, C=C, plan=plan)
+    out = gpu_bits(C)
+    if Cbuf is not None:
+        pad = gpu_bits(Cbuf[:, N:])
+        assert np.all(pad == inputs.bits(torch.tensor([-7.0], dtype=torch.bfloat16))[0]), "wrote past N"
+    return out
+
+
+# --------------------------------------------------------------------------
+# activation quantiser (natural layout) and weight packer, bit-exact
+
+@pytest.mark.parametrize("idx", range(len(inputs.WORKLOADS)), ids=[w.name for w in inputs.WORKLOADS])
+@pytest.mark.parametrize("seed", [1000, 2000])
+def test_quant_act_workloads_bit_exact(idx, seed):
+    say("quant_act", inputs.WORKLOADS[idx].name, seed)
+    A, _ = inputs.workload_inputs(idx, seed)
+    codes, scales = B.mx_quant_act(to_dev(A))
+    torch.cuda.synchronize()
+    rc, rs = oracle.quant(inputs.bits(A))
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+
+
+def adversarial_rows():
+    """Rows of hand-worked groups, wide binade spreads, tiny and huge values."""
+    import json, os, struct
+    with open(os.path.join(os.path.dirname(__file__), "golden", "hand_groups.json")) as f:
+        gs = json.load(f)["groups"]
+    row = np.zeros(32 * len(gs), np.uint16)
+    for gi, g in enumerate(gs):
+        for k, v in g["values"].items():
+            row[32 * gi + int(k)] = struct.unpack("<I", struct.pack("<f", v))[0] >> 16
+    K = 32 * ((len(gs) + 7) // 8) * 8
+    rows = np.zeros((3, K), np.uint16)
+    rows[0, :row.size] = row
+    rows[1, :row.size] = row[::-1]
+    rows[2, :row.size] = row ^ 0x8000
+    spread = inputs.bits(inputs.binade_spread(37, K, seed=5, lo=-140, hi=120))
+    return np.concatenate([rows, spread])
+
+
+def test_quant_act_adversarial_bit_exact():
+    x = adversarial_rows()
+    codes, scales = B.mx_quant_act(to_dev(inputs.from_bits(x)))
+    torch.cuda.synchronize()
+    rc, rs = oracle.quant(x)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quant_act_strided_input():
+    A, _ = inputs.shape_inputs(7, 8, 96, seed=3)
+    buf = torch.zeros((7, 136), dtype=torch.bfloat16)
+    buf[:, :96] = A
+    codes, scales = B.mx_quant_act(to_dev(buf)[:, :96])
+    torch.cuda.synchronize()
+    rc, rs = oracle.quant(inputs.bits(A))
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("idx", range(len(inputs.WORKLOADS)), ids=[w.name for w in inputs.WORKLOADS])
+def test_pack_unpack_workloads_bit_exact(idx):
+    w = inputs.WORKLOADS[idx]
+    say("pack", w.name)
+    _, Bm = inputs.workload_inputs(idx, 1000)
+    packed = B.mx_pack_weight(to_dev(Bm))
+    codes, scales = B.mx_unpack_weight(packed, w.N, w.K)
+    torch.cuda.synchronize()
+    rc, rs = oracle.quant(inputs.bits(Bm))
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+
+
+@pytest.mark.parametrize("N,K", [(1, 32), (33, 96), (70, 160), (129, 1088)])
+def test_pack_unpack_ragged_bit_exact(N, K):
+    Bm = inputs.binade_spread(N, K, seed=N + K, lo=-30, hi=30)
+    packed = B.mx_pack_weight(to_dev(Bm))
+    codes, scales = B.mx_unpack_weight(packed, N, K)
+    torch.cuda.synchronize()
+    rc, rs = oracle.quant(inputs.bits(Bm))
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+
+
+def test_pack_adversarial_bit_exact():
+    x = adversarial_rows()
+    packed = B.mx_pack_weight(to_dev(inputs.from_bits(x)))
+    codes, scales = B.mx_unpack_weight(packed, x.shape[0], x.shape[1])
+    torch.cuda.synchronize()
+    rc, rs = oracle.quant(x)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+# --------------------------------------------------------------------------
+# GEMM
+
+@pytest.mark.parametrize("idx", range(len(inputs.WORKLOADS)), ids=[w.name for w in inputs.WORKLOADS])
+@pytest.mark.parametrize("seed", [1000, 2000, 3000])
+def test_gemm_workloads_full(idx, seed):
+    """Every output of each measured workload under its production plan."""
+    w = inputs.WORKLOADS[idx]
+    say("gemm", w.name, seed, B.mx_gemm_plan(w.M, w.N, w.K))
+    A, Bm = inputs.workload_inputs(idx, seed)
+    C = run_gemm(A, Bm)
+    ref = oracle.gemm(inputs.bits(A), inputs.bits(Bm))
+    assert_c_close(C, ref, w.name)
+
+
+SMALL_SHAPES = [
+    (1, 32, 32), (4, 96, 128), (5, 200, 320), (17, 130, 96), (33, 64, 64),
+    (32, 96, 512), (40, 100, 2048), (70, 300, 1536), (16, 64, 7168), (65, 37, 256),
+]
+
+PLANS = [
+    dict(mb=1, nb=1, wk=1, splits=1, fuse_quant=1),
+    dict(mb=1, nb=2, wk=4, splits=1, fuse_quant=1),
+    dict(mb=1, nb=1, wk=8, splits=2, fuse_quant=1),
+    dict(mb=1, nb=1, wk=1, splits=1, fuse_quant=0),
+    dict(mb=2, nb=1, wk=2, splits=1, fuse_quant=0),
+    dict(mb=1, nb=2, wk=4, splits=3, fuse_quant=0),
+    dict(mb=2, nb=2, wk=8, splits=1, fuse_quant=0),
+    dict(mb=2, nb=2, wk=1, splits=2, fuse_quant=0),
+    dict(mb=1, nb=1, wk=16, splits=1, fuse_quant=0),
+]
+
+
+def plan_id(p):
+    return "mb%d_nb%d_wk%d_s%d_f%d" % (p["mb"], p["nb"], p["wk"], p["splits"], p["fuse_quant"])
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_gemm_small_shapes_auto_plan(shape):
+    M, N, K = shape
+    say("gemm small", shape, B.mx_gemm_plan(M, N, K))
+    A, Bm = inputs.shape_inputs(M, N, K, seed=M * 7 + N + K)
+    C = run_gemm(A, Bm)
+    assert_c_close(C, oracle.gemm(inputs.bits(A), inputs.bits(Bm)), str(shape))
+
+
+@pytest.mark.parametrize("plan", PLANS, ids=plan_id)
+@pytest.mark.parametrize("shape", [(5, 200, 320), (70, 300, 1536), (33, 130, 2048)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_gemm_explicit_plans(shape, plan):
+    M, N, K = shape
+    steps = (K + 63) // 64
+    if plan["splits"] > steps:
+        pytest.skip("more splits than K steps")
+    say("gemm plan", shape, plan_id(plan))
+    A, Bm = inputs.shape_inputs(M, N, K, seed=11 + M + N)
+    C = run_gemm(A, Bm, plan=plan)
+    assert_c_close(C, oracle.gemm(inputs.bits(A), inputs.bits(Bm)), "%s %s" % (shape, plan_id(plan)))
+
+
+def test_gemm_binade_spread_and_strides():
+    M, N, K = 19, 75, 640
+    A = inputs.binade_spread(M, K, seed=21, lo=-10, hi=10)
+    Bm = inputs.binade_spread(N, K, seed=22, lo=-10, hi=10)
+    C = run_gemm(A, Bm, lda_pad=24, ldc_pad=5)
+    assert_c_close(C, oracle.gemm(inputs.bits(A), inputs.bits(Bm)), "binades")
+
+
+def test_gemm_closed_form_all_ones():
+    M, N, K = 3, 40, 7168
+    A = torch.ones((M, K), dtype=torch.bfloat16)
+    Bm = torch.ones((N, K), dtype=torch.bfloat16)
+    C = run_gemm(A, Bm)
+    assert np.all(C == inputs.bits(torch.tensor([float(K)], dtype=torch.bfloat16))[0])
+
+
+def test_gemm_zero_inputs():
+    M, N, K = 8, 64, 256
+    C = run_gemm(torch.zeros((M, K), dtype=torch.bfloat16), torch.zeros((N, K), dtype=torch.bfloat16))
+    assert np.all(C == 0)
+
+
+def test_split_k_deterministic_and_consistent():
+    M, N, K = 16, 2112, 7168
+    A, Bm = inputs.shape_inputs(M, N, K, seed=77)
+    Ad = to_dev(A)
+    packed = B.mx_pack_weight(to_dev(Bm))
+    plan = B.mx_gemm_plan(M, N, K)
+    c1 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=plan))
+    c2 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=plan))
+    np.testing.assert_array_equal(c1, c2)
+    one = dict(plan, splits=1)
+    c3 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=one))
+    ref = oracle.gemm(inputs.bits(A), inputs.bits(Bm))
+    assert_c_close(c1, ref, "split")
+    assert_c_close(c3, ref, "no split")
+
+
+def test_gemm_streams_and_reuse_of_workspace():
+    """Two shapes in a row on a side stream, sharing one workspace buffer."""
+    s = torch.cuda.Stream()
+    shapes = [(16, 2112, 7168), (70, 300, 1536)]
+    ws_bytes = max(B.mx_gemm_workspace_bytes(*sh) for sh in shapes)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    outs = []
+    with torch.cuda.stream(s):
+        for (M, N, K) in shapes:
+            A, Bm = inputs.shape_inputs(M, N, K, seed=M + N)
+            Ad, Bd = to_dev(A), to_dev(Bm)
+            packed = B.mx_pack_weight(Bd, stream=s)
+            C = B.mx_gemm(Ad, packed, N, workspace=ws, stream=s)
+            outs.append((C, A, Bm))
+    s.synchronize()
+    for C, A, Bm in outs:
+        assert_c_close(inputs.bits(C.cpu()), oracle.gemm(inputs.bits(A), inputs.bits(Bm)), "stream")
