@@ -8,10 +8,11 @@ data) resident in HBM; the timed loop rotates over enough copies of A, the
 packed weight and C that the working set (>= 1 GiB) cannot sit in the 256 MB
 Infinity Cache, so every call streams its weight from HBM ("cold").
 
-Printed: one JSON line with the end-to-end µs per call (value), the GEMM
-kernel's event-timed duration against the HBM roofline, the oracle timed on
-the host cores (cpu_baseline) and the same figures for the other four
-workloads (per_workload).
+Printed: one JSON line with the end-to-end µs per call (value, wall clock
+over the timed region), the GEMM kernel's average launch time (HIP events on
+the launch stream over the same region; one launch per call) against the HBM
+roofline, the oracle timed on the host cores (cpu_baseline) and the same
+figures for the other four workloads (per_workload).
 """
 from __future__ import annotations
 
@@ -80,7 +81,7 @@ class Setup:
         self.As = [A0] + [A0.clone() for _ in range(self.copies - 1)]
         self.Ps = [P0] + [P0.clone() for _ in range(self.copies - 1)]
         self.Cs = [torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev) for _ in range(self.copies)]
-        self.ws = [torch.empty(max(ws_bytes, 256), dtype=torch.uint8, device=dev) for _ in range(self.copies)]
+        self.ws = [torch.zeros(max(ws_bytes, 256), dtype=torch.uint8, device=dev) for _ in range(self.copies)]
         stream = torch.cuda.current_stream().cuda_stream
         self.args = [(a.data_ptr(), w.M, w.K, w.K, p.data_ptr(), w.N, c.data_ptr(), w.N, s.data_ptr(), s.numel(),
                       stream) for a, p, c, s in zip(self.As, self.Ps, self.Cs, self.ws)]
@@ -94,47 +95,22 @@ class Setup:
 
 
 def time_loop(torch, st, steps, warmup, rotate=True):
-    """End-to-end: `steps` back-to-back calls between two synchronisations."""
+    """`steps` back-to-back mx_gemm calls between two synchronisations.
+    Returns (wall-clock µs per call, event-timed µs per launch): HIP events
+    recorded on the launch stream bracket the whole timed region."""
     for i in range(warmup):
         st.call(i if rotate else 0)
     torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    e0.record()
     for i in range(steps):
         st.call(i if rotate else 0)
+    e1.record()
     torch.cuda.synchronize()
-    return (time.perf_counter() - t0) / steps * 1e6
-
-
-def time_graph(torch, st, calls, replays=5, rotate=True):
-    """GPU time per call without host dispatch in the way: `calls` mx_gemm
-    calls (rotating buffers) captured into one HIP graph, replayed; events on
-    the replay stream bracket each replay.  Returns the mean and the minimum
-    over replays of the per-call time in µs."""
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        stream = s.cuda_stream
-        args = [a[:-1] + (stream,) for a in st.args]
-        torch.cuda.synchronize()
-        with torch.cuda.graph(g, stream=s):
-            for i in range(calls):
-                rc = st.fn(*args[(i if rotate else 0) % st.copies])
-                if rc:
-                    raise RuntimeError("mx_gemm returned %d under capture" % rc)
-    torch.cuda.synchronize()
-    per = []
-    for _ in range(replays + 1):
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(s)
-        g.replay()
-        b.record(s)
-        torch.cuda.synchronize()
-        per.append(a.elapsed_time(b) * 1e3 / calls)
-    per = per[1:]   # first replay uploads the graph
-    del g
-    return statistics.mean(per), min(per)
+    wall = (time.perf_counter() - t0) / steps * 1e6
+    return wall, e0.elapsed_time(e1) * 1e3 / steps
 
 
 def cpu_baseline(idx, inputs, seconds=10.0):
@@ -212,23 +188,19 @@ def main():
         w = st.w
         print("workload %s plan %s copies %d" % (w.name, st.plan, st.copies), file=sys.stderr, flush=True)
         steps = args.steps if idx == HEADLINE else max(200, args.steps // 4)
-        e2e_cold = time_loop(torch, st, steps, args.warmup)
-        e2e_hot = time_loop(torch, st, steps, args.warmup, rotate=False)
-        calls = min(st.copies, 500)
-        gpu_cold_mean, gpu_cold_min = time_graph(torch, st, calls)
-        gpu_hot_mean, _ = time_graph(torch, st, calls, rotate=False)
+        e2e_cold, gpu_cold = time_loop(torch, st, steps, args.warmup)
+        e2e_hot, gpu_hot = time_loop(torch, st, steps, args.warmup, rotate=False)
         nbytes = algorithmic_bytes(w.M, w.N, w.K)
         flops = 2.0 * w.M * w.N * w.K
         rec = {
             "M": w.M, "N": w.N, "K": w.K, "plan": st.plan,
-            "launches_per_call": 1 + (0 if st.plan["fuse_quant"] else 1) + (1 if st.plan["splits"] > 1 else 0),
+            "launches_per_call": 1,
             "us_per_call_e2e_cold": round(e2e_cold, 3), "us_per_call_e2e_hot": round(e2e_hot, 3),
-            "gpu_us_cold": round(gpu_cold_mean, 3), "gpu_us_cold_min": round(gpu_cold_min, 3),
-            "gpu_us_hot": round(gpu_hot_mean, 3),
-            "algorithmic_bytes": nbytes, "gbps_cold": round(nbytes / gpu_cold_mean / 1e3, 1),
-            "hbm_frac_cold": round(nbytes / gpu_cold_mean / 1e3 / HBM_PEAK_GBS, 4),
-            "tflops_cold": round(flops / gpu_cold_mean / 1e6, 2),
-            "mfma_frac_cold": round(flops / gpu_cold_mean / 1e6 / FP4_PEAK_TFLOPS, 5),
+            "gpu_us_cold": round(gpu_cold, 3), "gpu_us_hot": round(gpu_hot, 3),
+            "algorithmic_bytes": nbytes, "gbps_cold": round(nbytes / gpu_cold / 1e3, 1),
+            "hbm_frac_cold": round(nbytes / gpu_cold / 1e3 / HBM_PEAK_GBS, 4),
+            "tflops_cold": round(flops / gpu_cold / 1e6, 2),
+            "mfma_frac_cold": round(flops / gpu_cold / 1e6 / FP4_PEAK_TFLOPS, 5),
         }
         per_workload[w.name] = rec
         print(json.dumps({w.name: rec}), file=sys.stderr, flush=True)
@@ -264,7 +236,7 @@ def main():
             "unit": "GB/s",
             "frac": round(nbytes / rec["gpu_us_cold"] / 1e3 / HBM_PEAK_GBS, 4),
             "traffic": load_traffic(w.name),
-            "kernel": "gemm_kernel (one launch per call for this plan)",
+            "kernel": "mx4::gemm_kernel (the only launch of a call)",
             "kernel_us": rec["gpu_us_cold"],
             "bytes_per_launch": nbytes,
         },

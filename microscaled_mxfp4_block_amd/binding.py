@@ -30,8 +30,8 @@ EXPORTS = [
 
 
 class MxPlan(ctypes.Structure):
-    _fields_ = [("mb", ctypes.c_int), ("nb", ctypes.c_int), ("wk", ctypes.c_int),
-                ("splits", ctypes.c_int), ("fuse_quant", ctypes.c_int)]
+    _fields_ = [("mb", ctypes.c_int), ("nb", ctypes.c_int), ("wn", ctypes.c_int), ("wk", ctypes.c_int),
+                ("splits", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -155,6 +155,12 @@ def mx_gemm_workspace_bytes(M: int, N: int, K: int, plan: Optional[dict] = None)
     return out.value
 
 
+def new_workspace(M: int, N: int, K: int, plan: Optional[dict] = None, device="cuda") -> torch.Tensor:
+    """A zero-filled workspace for mx_gemm on this shape (and plan)."""
+    nbytes = mx_gemm_workspace_bytes(M, N, K, plan)
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
 def mx_gemm(A: torch.Tensor, packed: torch.Tensor, N: int, C: Optional[torch.Tensor] = None,
             workspace: Optional[torch.Tensor] = None, plan: Optional[dict] = None, stream=None) -> torch.Tensor:
     """C[M, N] (bf16) = A x B^T with A quantised on the fly and B packed by mx_pack_weight."""
@@ -165,8 +171,7 @@ def mx_gemm(A: torch.Tensor, packed: torch.Tensor, N: int, C: Optional[torch.Ten
     if (Mc, Nc) != (M, N):
         raise ValueError("C must be [%d, %d]" % (M, N))
     if workspace is None:
-        ws_bytes = mx_gemm_workspace_bytes(M, N, K, plan)
-        workspace = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=A.device)
+        workspace = new_workspace(M, N, K, plan, device=A.device)
     s = _stream(stream)
     if plan is None:
         rc = lib().mx_gemm(_ptr(A), M, K, lda, _ptr(packed), N, _ptr(C), ldc, _ptr(workspace),

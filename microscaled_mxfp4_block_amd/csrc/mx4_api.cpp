@@ -35,14 +35,14 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_EHIP; }
 // in model_plan().
 struct TableEntry {
     int M, N, K;
-    Plan plan;
+    Plan plan;   // mb, nb, wn, wk, splits
 };
 const TableEntry kTable[] = {
-    {4, 2880, 512, {1, 1, 8, 1, 1}},
-    {32, 4096, 512, {1, 1, 8, 1, 1}},
-    {16, 2112, 7168, {1, 1, 8, 2, 0}},
-    {64, 7168, 2048, {2, 1, 4, 1, 0}},
-    {256, 3072, 1536, {2, 2, 4, 1, 0}},
+    {4, 2880, 512, {1, 1, 1, 8, 1}},
+    {32, 4096, 512, {1, 1, 1, 8, 1}},
+    {16, 2112, 7168, {1, 1, 1, 8, 4}},
+    {64, 7168, 2048, {1, 1, 2, 8, 1}},
+    {256, 3072, 1536, {2, 1, 2, 4, 1}},
 };
 
 int pow2_floor(int x) {
@@ -51,45 +51,15 @@ int pow2_floor(int x) {
     return p;
 }
 
-// Occupancy model for shapes without a table entry: quantise A inside the
-// GEMM when it is small (one activation block, short K), pick the wave tile
-// from M, split the K steps over up to 8 waves per workgroup and, when the
-// tiles alone leave the 256 CUs idle, over several workgroups.
-Plan model_plan(int M, int N, int K) {
-    const OperandGeom ga = mx4::operand_geom(M, K);
-    const OperandGeom gb = mx4::operand_geom(N, K);
-    Plan p;
-    p.fuse = (ga.RB == 1 && gb.KS <= 16) ? 1 : 0;
-    p.mb = (!p.fuse && ga.RB >= 2) ? 2 : 1;
-    p.nb = (ga.RB >= 4 && gb.RB >= 64) ? 2 : 1;
-    const int mtiles = (ga.RB + p.mb - 1) / p.mb;
-    const int ntiles = (gb.RB + p.nb - 1) / p.nb;
-    const int tiles = mtiles * ntiles;
-    int wk = gb.KS / 2;
-    if (wk < 1) wk = 1;
-    if (wk > 8) wk = 8;
-    p.wk = pow2_floor(wk);
-    int splits = 1;
-    const int steps_per_wave_group = gb.KS / p.wk;  // K steps left for each wave at one split
-    while (tiles * splits < 256 && splits * 2 <= steps_per_wave_group / 2) splits *= 2;
-    p.splits = splits;
-    return p;
-}
-
-Plan choose_plan(int M, int N, int K) {
-    for (const TableEntry& e : kTable)
-        if (e.M == M && e.N == N && e.K == K) return e.plan;
-    return model_plan(M, N, K);
-}
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-    size_t aop_offset, aop_bytes;
+    size_t counter_bytes;
     size_t partial_offset, partial_bytes;
     size_t total;
     int splits, steps_per_split;
+    int mtiles, ntiles;
 };
-
-size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     if (!mx4::gemm_plan_supported(plan)) return MX_EPLAN;
@@ -99,16 +69,53 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     Layout l;
     l.steps_per_split = (gb.KS + plan.splits - 1) / plan.splits;
     l.splits = (gb.KS + l.steps_per_split - 1) / l.steps_per_split;  // every split non-empty
-    l.aop_offset = 0;
-    l.aop_bytes = plan.fuse ? 0 : round_up(ga.total_bytes, 256);
-    l.partial_offset = l.aop_bytes;
-    l.partial_bytes = l.splits > 1 ? round_up((size_t)l.splits * M * gb.RB * mx4::kRowBlock * sizeof(float), 256) : 0;
-    l.total = l.aop_bytes + l.partial_bytes;
-    const long long mtiles = (ga.RB + plan.mb - 1) / plan.mb;
-    const long long ntiles = (gb.RB + plan.nb - 1) / plan.nb;
-    if (mtiles * ntiles * l.splits >= (1LL << 31)) return MX_EINVAL;
+    if ((l.steps_per_split + plan.wk - 1) / plan.wk > mx4::kStepsPerWaveMax) return MX_EPLAN;
+    if (mx4::gemm_lds_bytes(plan, l.steps_per_split) > mx4::kLdsBudget) return MX_EPLAN;
+    l.mtiles = (ga.RB + plan.mb - 1) / plan.mb;
+    l.ntiles = (gb.RB + plan.nb * plan.wn - 1) / (plan.nb * plan.wn);
+    if ((long long)l.mtiles * l.ntiles * l.splits >= (1LL << 31)) return MX_EINVAL;
+    if (l.splits > 1) {
+        if ((long long)l.mtiles * l.ntiles > mx4::kMaxSplitTiles) return MX_EPLAN;
+        l.counter_bytes = mx4::kCounterRegionBytes;
+        l.partial_offset = l.counter_bytes;
+        l.partial_bytes = round_up((size_t)l.splits * M * gb.RB * mx4::kRowBlock * sizeof(float), 256);
+    } else {
+        l.counter_bytes = l.partial_offset = l.partial_bytes = 0;
+    }
+    l.total = l.counter_bytes + l.partial_bytes;
     *out = l;
     return MX_OK;
+}
+
+// Model for shapes without a table entry.  Two 32-row M blocks per
+// workgroup when M allows, one N block per wave, 8 waves along K (fewer for
+// short K); then the fewest K splits that keep every wave within its register
+// budget and the activation slice within the LDS budget, doubled while the
+// tiles leave most of the 256 CUs idle and the fp32 partials stay small next
+// to the weight.
+Plan model_plan(int M, int N, int K) {
+    const OperandGeom ga = mx4::operand_geom(M, K);
+    const OperandGeom gb = mx4::operand_geom(N, K);
+    Plan p;
+    p.mb = ga.RB >= 2 ? 2 : 1;
+    p.nb = 1;
+    p.wn = 1;
+    p.wk = pow2_floor(gb.KS < 8 ? gb.KS : 8);
+    p.splits = 1;
+    Layout l;
+    while (p.splits < gb.KS && plan_layout(p, M, N, K, &l) != MX_OK) ++p.splits;
+    const long long tiles = (long long)((ga.RB + p.mb - 1) / p.mb) * gb.RB;
+    const double weight = (double)N * K * 0.5;
+    while (tiles * p.splits < 128 && p.splits * 2 <= gb.KS &&
+           (double)M * N * 4.0 * 2 * p.splits * 2 <= 0.25 * weight)
+        p.splits *= 2;
+    return p;
+}
+
+Plan choose_plan(int M, int N, int K) {
+    for (const TableEntry& e : kTable)
+        if (e.M == M && e.N == N && e.K == K) return e.plan;
+    return model_plan(M, N, K);
 }
 
 int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, void* C, int ldc, void* ws,
@@ -126,7 +133,6 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
         if (!aligned(ws, 256)) return MX_EALIGN;
         if (ws_bytes < lay.total) return MX_ESPACE;
     }
-    hipStream_t s = (hipStream_t)stream;
     const OperandGeom ga = mx4::operand_geom(M, K);
     const OperandGeom gb = mx4::operand_geom(N, K);
     uint8_t* wsb = (uint8_t*)ws;
@@ -135,8 +141,6 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     memset(&p, 0, sizeof p);
     p.A = (const uint16_t*)A;
     p.lda = lda;
-    p.aop = plan.fuse ? nullptr : wsb + lay.aop_offset;
-    p.a_code_bytes = ga.code_bytes;
     p.bp = (const uint8_t*)packed;
     p.b_code_bytes = gb.code_bytes;
     p.KS = gb.KS;
@@ -146,8 +150,8 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     p.K = K;
     p.RBm = ga.RB;
     p.RBn = gb.RB;
-    p.mtiles = (ga.RB + plan.mb - 1) / plan.mb;
-    p.ntiles = (gb.RB + plan.nb - 1) / plan.nb;
+    p.mtiles = lay.mtiles;
+    p.ntiles = lay.ntiles;
     p.splits = lay.splits;
     p.steps_per_split = lay.steps_per_split;
     p.C = (uint16_t*)C;
@@ -155,18 +159,11 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     p.c_vec = (ldc % 4 == 0 && aligned(C, 8)) ? 1 : 0;
     p.partial = lay.splits > 1 ? (float*)(wsb + lay.partial_offset) : nullptr;
     p.ldp = gb.RB * mx4::kRowBlock;
+    p.counters = lay.splits > 1 ? (int*)wsb : nullptr;
 
-    if (!plan.fuse) {
-        rc = hip_status(mx4::launch_pack((const uint16_t*)A, M, K, lda, wsb + lay.aop_offset, s));
-        if (rc) return rc;
-    }
     Plan run = plan;
     run.splits = lay.splits;
-    rc = hip_status(mx4::launch_gemm(run, p, s));
-    if (rc) return rc;
-    if (lay.splits > 1) rc = hip_status(mx4::launch_reduce(p.partial, lay.splits, M, N, p.ldp, (uint16_t*)C, ldc,
-                                                              p.c_vec, s));
-    return rc;
+    return hip_status(mx4::launch_gemm(run, p, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -231,9 +228,9 @@ int mx_gemm_plan(int M, int N, int K, mx_plan* plan_host) {
     if (rc) return rc;
     plan_host->mb = p.mb;
     plan_host->nb = p.nb;
+    plan_host->wn = p.wn;
     plan_host->wk = p.wk;
     plan_host->splits = lay.splits;
-    plan_host->fuse_quant = p.fuse;
     return MX_OK;
 }
 
@@ -243,7 +240,7 @@ int mx_gemm_plan_workspace_bytes(const mx_plan* plan_host, int M, int N, int K, 
     if (rc) return rc;
     rc = check_operand_shape(N, K);
     if (rc) return rc;
-    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wk, plan_host->splits, plan_host->fuse_quant};
+    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wn, plan_host->wk, plan_host->splits};
     Layout lay;
     rc = plan_layout(p, M, N, K, &lay);
     if (rc) return rc;
@@ -261,7 +258,7 @@ int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host) {
 int mx_gemm_with_plan(const void* A_dev, int M, int K, int lda, const void* packed_dev, int N, void* C_dev, int ldc,
                       void* ws_dev, size_t ws_bytes, const mx_plan* plan_host, void* stream) {
     if (!plan_host) return MX_EALIGN;
-    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wk, plan_host->splits, plan_host->fuse_quant};
+    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wn, plan_host->wk, plan_host->splits};
     return gemm_impl(A_dev, M, K, lda, packed_dev, N, C_dev, ldc, ws_dev, ws_bytes, p, stream);
 }
 

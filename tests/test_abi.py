@@ -119,9 +119,10 @@ def test_gemm_validation():
 def test_plans_for_workloads():
     for w in WORKLOADS:
         p = B.mx_gemm_plan(w.M, w.N, w.K)
-        assert p["mb"] in (1, 2) and p["nb"] in (1, 2) and p["splits"] >= 1 and p["wk"] >= 1
+        assert p["mb"] in (1, 2) and p["nb"] in (1, 2) and p["wn"] in (1, 2, 4)
+        assert p["wk"] in (1, 2, 4, 8) and p["wn"] * p["wk"] <= 16 and p["splits"] >= 1
         ws = B.mx_gemm_workspace_bytes(w.M, w.N, w.K)
-        if p["fuse_quant"] and p["splits"] == 1:
+        if p["splits"] == 1:
             assert ws == 0
         else:
             assert ws > 0
@@ -135,11 +136,13 @@ def test_plan_model_for_other_shapes():
 
 
 def test_explicit_plan_rejections():
-    bad = [dict(mb=3, nb=1, wk=1, splits=1, fuse_quant=0),
-           dict(mb=1, nb=1, wk=3, splits=1, fuse_quant=0),
-           dict(mb=2, nb=1, wk=4, splits=1, fuse_quant=1),
-           dict(mb=1, nb=1, wk=4, splits=0, fuse_quant=0),
-           dict(mb=1, nb=1, wk=4, splits=1000, fuse_quant=0)]
+    bad = [dict(mb=3, nb=1, wn=1, wk=1, splits=1),      # no such tile
+           dict(mb=1, nb=1, wn=1, wk=3, splits=1),      # no such wave count
+           dict(mb=1, nb=1, wn=4, wk=8, splits=4),      # more than 16 waves
+           dict(mb=1, nb=1, wn=1, wk=4, splits=0),
+           dict(mb=1, nb=1, wn=1, wk=4, splits=1000),   # more splits than K steps
+           dict(mb=1, nb=1, wn=1, wk=8, splits=1),      # 14 K steps per wave > register budget
+           dict(mb=2, nb=1, wn=1, wk=8, splits=2)]      # activation slice over the LDS budget
     for p in bad:
         with pytest.raises(B.MxError) as e:
             B.mx_gemm_workspace_bytes(16, 2112, 7168, p)

@@ -192,20 +192,29 @@ SMALL_SHAPES = [
 ]
 
 PLANS = [
-    dict(mb=1, nb=1, wk=1, splits=1, fuse_quant=1),
-    dict(mb=1, nb=2, wk=4, splits=1, fuse_quant=1),
-    dict(mb=1, nb=1, wk=8, splits=2, fuse_quant=1),
-    dict(mb=1, nb=1, wk=1, splits=1, fuse_quant=0),
-    dict(mb=2, nb=1, wk=2, splits=1, fuse_quant=0),
-    dict(mb=1, nb=2, wk=4, splits=3, fuse_quant=0),
-    dict(mb=2, nb=2, wk=8, splits=1, fuse_quant=0),
-    dict(mb=2, nb=2, wk=1, splits=2, fuse_quant=0),
-    dict(mb=1, nb=1, wk=16, splits=1, fuse_quant=0),
+    dict(mb=1, nb=1, wn=1, wk=1, splits=1),
+    dict(mb=1, nb=2, wn=1, wk=4, splits=1),
+    dict(mb=1, nb=1, wn=1, wk=8, splits=2),
+    dict(mb=2, nb=1, wn=2, wk=2, splits=1),
+    dict(mb=1, nb=2, wn=2, wk=4, splits=3),
+    dict(mb=2, nb=2, wn=4, wk=4, splits=1),
+    dict(mb=2, nb=2, wn=1, wk=1, splits=6),
+    dict(mb=1, nb=1, wn=2, wk=8, splits=4),
+    dict(mb=2, nb=1, wn=4, wk=2, splits=2),
 ]
 
 
 def plan_id(p):
-    return "mb%d_nb%d_wk%d_s%d_f%d" % (p["mb"], p["nb"], p["wk"], p["splits"], p["fuse_quant"])
+    return "mb%d_nb%d_wn%d_wk%d_s%d" % (p["mb"], p["nb"], p["wn"], p["wk"], p["splits"])
+
+
+def plan_runs(M, N, K, plan):
+    try:
+        B.mx_gemm_workspace_bytes(M, N, K, plan)
+        return True
+    except B.MxError as e:
+        assert e.code == B.MX_EPLAN
+        return False
 
 
 @pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
@@ -222,9 +231,8 @@ def test_gemm_small_shapes_auto_plan(shape):
                          ids=lambda s: "x".join(map(str, s)))
 def test_gemm_explicit_plans(shape, plan):
     M, N, K = shape
-    steps = (K + 63) // 64
-    if plan["splits"] > steps:
-        pytest.skip("more splits than K steps")
+    if not plan_runs(M, N, K, plan):
+        pytest.skip("plan outside the register / LDS budget for this shape")
     say("gemm plan", shape, plan_id(plan))
     A, Bm = inputs.shape_inputs(M, N, K, seed=11 + M + N)
     C = run_gemm(A, Bm, plan=plan)
@@ -259,14 +267,18 @@ def test_split_k_deterministic_and_consistent():
     Ad = to_dev(A)
     packed = B.mx_pack_weight(to_dev(Bm))
     plan = B.mx_gemm_plan(M, N, K)
-    c1 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=plan))
-    c2 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=plan))
+    assert plan["splits"] > 1
+    ws = B.new_workspace(M, N, K, plan, device=DEV)
+    c1 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=plan, workspace=ws))
+    c2 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=plan, workspace=ws))
     np.testing.assert_array_equal(c1, c2)
-    one = dict(plan, splits=1)
-    c3 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=one))
+    # the arrival counters are back at zero after every call
+    assert int(ws[:256].view(torch.int32).abs().sum().item()) == 0
+    other = dict(plan, splits=2)
+    c3 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=other))
     ref = oracle.gemm(inputs.bits(A), inputs.bits(Bm))
-    assert_c_close(c1, ref, "split")
-    assert_c_close(c3, ref, "no split")
+    assert_c_close(c1, ref, "split %d" % plan["splits"])
+    assert_c_close(c3, ref, "split 2")
 
 
 def test_gemm_streams_and_reuse_of_workspace():
@@ -274,7 +286,7 @@ def test_gemm_streams_and_reuse_of_workspace():
     s = torch.cuda.Stream()
     shapes = [(16, 2112, 7168), (70, 300, 1536)]
     ws_bytes = max(B.mx_gemm_workspace_bytes(*sh) for sh in shapes)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=DEV)
     outs = []
     with torch.cuda.stream(s):
         for (M, N, K) in shapes:
