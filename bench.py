@@ -85,7 +85,7 @@ class Setup:
         stream = torch.cuda.current_stream().cuda_stream
         self.args = [(a.data_ptr(), w.M, w.K, w.K, p.data_ptr(), w.N, c.data_ptr(), w.N, s.data_ptr(), s.numel(),
                       stream) for a, p, c, s in zip(self.As, self.Ps, self.Cs, self.ws)]
-        self.fn = B.lib().mx_gemm
+        self.fn = B.ext().gemm   # CPython fast-call wrapper of mx_gemm
         torch.cuda.synchronize()
 
     def call(self, i):

@@ -86,9 +86,9 @@ int mx_quant_act(const void* A_dev, int M, int K, int lda,
                  void* codes_dev, void* scales_dev, void* stream);
 
 /* Workspace bytes mx_gemm needs for this shape under the library's plan
- * (0 when the plan does not split K).  The workspace holds a fixed 64 KiB
- * region of per-tile arrival counters followed by the fp32 partial sums of
- * the K splits. */
+ * (0 when A is quantised inside the GEMM and K is not split).  The workspace
+ * holds the quantised activation operand and the fp32 partial sums of the K
+ * splits. */
 int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host);
 
 /* C = A x B^T with A quantised on the fly (quantisation, block-scaled MFMA
@@ -98,13 +98,13 @@ int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host);
  *   packed_dev weight packed by mx_pack_weight for (N, K)
  *   C_dev      bf16 [M, N] output, ldc >= N
  *   ws_dev     workspace of ws_bytes >= mx_gemm_workspace_bytes(M, N, K),
- *              256-byte aligned (may be NULL when that is 0).  It must be
- *              zero-filled once before its first use; every completed call
- *              leaves its counters at zero again, so a workspace can be reused
- *              across calls and shapes without clearing.  Calls that overlap
- *              in time (other streams) need separate workspaces.
- * One kernel launch per call: the quantisation of A, the contraction and the
- * reduction of the K splits all run in it. */
+ *              256-byte aligned (may be NULL when that is 0); no
+ *              initialisation needed, scratch after the call.  Calls that
+ *              overlap in time (other streams) need separate workspaces.
+ * Launches per call: 1 (A quantised inside the GEMM), +1 for the quantisation
+ * kernel when the plan has preq, +1 for the split-K reduction when splits > 1.
+ * The split-K reduction sums the partials in split order: results do not
+ * depend on timing. */
 int mx_gemm(const void* A_dev, int M, int K, int lda,
             const void* packed_dev, int N,
             void* C_dev, int ldc,
@@ -115,11 +115,13 @@ int mx_gemm(const void* A_dev, int M, int K, int lda,
  * A workgroup of wn x wk waves owns 32*mb rows of C and 32*nb*wn columns,
  * over K / splits of the reduction; its wk waves share that K range. */
 typedef struct mx_plan {
-    int mb;          /* 32-row blocks of M per workgroup (1 or 2) */
+    int mb;          /* 32-row blocks of M per wave (1 or 2) */
     int nb;          /* 32-column blocks of N per wave (1 or 2) */
     int wn;          /* waves along N per workgroup (1, 2 or 4) */
-    int wk;          /* waves along K per workgroup (1, 2, 4 or 8; wn*wk <= 16) */
-    int splits;      /* workgroups along K; > 1 adds the in-kernel reduction */
+    int wk;          /* waves along K per workgroup (1, 2, 4, 8 or 16; wn*wk <= 16) */
+    int splits;      /* workgroups along K; > 1 adds a reduction kernel */
+    int preq;        /* 1: quantise A in a first kernel into the workspace;
+                        0: each GEMM workgroup quantises its slice of A itself */
 } mx_plan;
 
 /* The plan mx_gemm uses for (M, N, K) (host only). */

@@ -31,7 +31,7 @@ EXPORTS = [
 
 class MxPlan(ctypes.Structure):
     _fields_ = [("mb", ctypes.c_int), ("nb", ctypes.c_int), ("wn", ctypes.c_int), ("wk", ctypes.c_int),
-                ("splits", ctypes.c_int)]
+                ("splits", ctypes.c_int), ("preq", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -44,6 +44,17 @@ class MxError(RuntimeError):
 
 
 _lib = None
+_ext = None
+
+
+def ext():
+    """The CPython fast-call module (_mx4ext) for mx_gemm / mx_gemm_with_plan."""
+    global _ext
+    if _ext is None:
+        lib()   # fails loudly when libmx4.so is missing
+        from . import _mx4ext
+        _ext = _mx4ext
+    return _ext
 
 
 def lib() -> ctypes.CDLL:
@@ -156,9 +167,9 @@ def mx_gemm_workspace_bytes(M: int, N: int, K: int, plan: Optional[dict] = None)
 
 
 def new_workspace(M: int, N: int, K: int, plan: Optional[dict] = None, device="cuda") -> torch.Tensor:
-    """A zero-filled workspace for mx_gemm on this shape (and plan)."""
+    """A workspace for mx_gemm on this shape (and plan)."""
     nbytes = mx_gemm_workspace_bytes(M, N, K, plan)
-    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def mx_gemm(A: torch.Tensor, packed: torch.Tensor, N: int, C: Optional[torch.Tensor] = None,
@@ -174,11 +185,11 @@ def mx_gemm(A: torch.Tensor, packed: torch.Tensor, N: int, C: Optional[torch.Ten
         workspace = new_workspace(M, N, K, plan, device=A.device)
     s = _stream(stream)
     if plan is None:
-        rc = lib().mx_gemm(_ptr(A), M, K, lda, _ptr(packed), N, _ptr(C), ldc, _ptr(workspace),
-                           workspace.numel(), s)
+        rc = ext().gemm(A.data_ptr(), M, K, lda, packed.data_ptr(), N, C.data_ptr(), ldc, workspace.data_ptr(),
+                        workspace.numel(), s)
     else:
-        p = MxPlan(**plan)
-        rc = lib().mx_gemm_with_plan(_ptr(A), M, K, lda, _ptr(packed), N, _ptr(C), ldc, _ptr(workspace),
-                                     workspace.numel(), ctypes.byref(p), s)
+        rc = ext().gemm_with_plan(A.data_ptr(), M, K, lda, packed.data_ptr(), N, C.data_ptr(), ldc,
+                                  workspace.data_ptr(), workspace.numel(), plan["mb"], plan["nb"], plan["wn"],
+                                  plan["wk"], plan["splits"], plan["preq"], s)
     _check(rc, "mx_gemm")
     return C

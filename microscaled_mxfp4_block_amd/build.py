@@ -19,7 +19,9 @@ ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libmx4.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-SOURCES = ["mx4_api.cpp", "mx4_gemm.hip", "mx4_quant.hip"]
+# (source, extra flags, object name): the GEMM is compiled once per K-step budget
+SOURCES = [("mx4_api.cpp", [], "mx4_api"), ("mx4_quant.hip", [], "mx4_quant")] + [
+    ("mx4_gemm.hip", ["-DMX4_KR=%d" % kr], "mx4_gemm_kr%d" % kr) for kr in (1, 2, 4, 8)]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -35,15 +37,17 @@ def _run(cmd):
     return out
 
 
-def _compile(src):
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    _run([HIPCC] + FLAGS + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+def _compile(item):
+    src, extra, name = item
+    obj = os.path.join(BUILD_DIR, name + ".o")
+    _run([HIPCC] + FLAGS + extra + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
     return obj
 
 
-def _device_asm(src):
-    asm = os.path.join(BUILD_DIR, os.path.basename(src) + ".s")
-    _run([HIPCC] + FLAGS + ["-x", "hip", "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm])
+def _device_asm(item):
+    src, extra, name = item
+    asm = os.path.join(BUILD_DIR, name + ".s")
+    _run([HIPCC] + FLAGS + extra + ["-x", "hip", "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm])
     with open(asm) as f:
         text = f.read()
     bad = sorted(set(m.group(0) for m in PACKED_FP32.finditer(text)))
@@ -52,18 +56,32 @@ def _device_asm(src):
     return asm
 
 
+EXT = os.path.join(HERE, "_mx4ext.so")
+
+
+def build_ext():
+    """The CPython fast-call module for the hot entry points (gcc, links libmx4.so)."""
+    import sysconfig
+    inc = sysconfig.get_paths()["include"]
+    tmp = EXT + ".tmp%d" % os.getpid()
+    _run(["gcc", "-O2", "-shared", "-fPIC", "-Wall", "-I" + inc, os.path.join(CSRC, "mx4_pyext.c"),
+          "-o", tmp, "-L" + HERE, "-lmx4", "-Wl,-rpath,$ORIGIN"])
+    os.replace(tmp, EXT)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libmx4.so; returns its path."""
+    """Compile every source and link libmx4.so (plus the fast-call module); returns its path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    kernels = [s for s in SOURCES if s.endswith(".hip")]
+    kernels = [s for s in SOURCES if s[0].endswith(".hip")]
     with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
         objs = list(ex.map(_compile, SOURCES))
         list(ex.map(_device_asm, kernels))
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
     os.replace(tmp, LIB)
+    build_ext()
     if verbose:
-        print("built", LIB)
+        print("built", LIB, "and", EXT)
     return LIB
 
 

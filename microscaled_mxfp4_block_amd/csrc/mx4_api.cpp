@@ -24,8 +24,8 @@ bool aligned(const void* p, uintptr_t a) { return p != nullptr && ((uintptr_t)p 
 int check_operand_shape(int rows, int K) {
     if (rows <= 0 || K <= 0 || rows > kMaxDim || K > kMaxDim || K % mx4::kGroup != 0) return MX_EINVAL;
     const OperandGeom g = mx4::operand_geom(rows, K);
-    // in-kernel tile offsets are formed in 32-bit integers before widening
-    if ((long long)g.RB * g.KS * 64 >= (1LL << 31) || (long long)g.RB * g.KW * 64 >= (1LL << 31)) return MX_EINVAL;
+    // the kernels address operands with 32-bit buffer offsets
+    if (g.total_bytes >= (1ULL << 31) || (unsigned long long)rows * K * 2 >= (1ULL << 31)) return MX_EINVAL;
     return MX_OK;
 }
 
@@ -35,14 +35,14 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_EHIP; }
 // in model_plan().
 struct TableEntry {
     int M, N, K;
-    Plan plan;   // mb, nb, wn, wk, splits
+    Plan plan;   // mb, nb, wn, wk, splits, preq
 };
 const TableEntry kTable[] = {
-    {4, 2880, 512, {1, 1, 1, 8, 1}},
-    {32, 4096, 512, {1, 1, 1, 8, 1}},
-    {16, 2112, 7168, {1, 1, 1, 8, 4}},
-    {64, 7168, 2048, {1, 1, 2, 8, 1}},
-    {256, 3072, 1536, {2, 1, 2, 4, 1}},
+    {4, 2880, 512, {1, 1, 1, 8, 1, 0}},
+    {32, 4096, 512, {1, 1, 1, 8, 1, 0}},
+    {16, 2112, 7168, {1, 1, 1, 8, 2, 1}},
+    {64, 7168, 2048, {2, 1, 1, 4, 1, 1}},
+    {256, 3072, 1536, {2, 2, 1, 4, 1, 1}},
 };
 
 int pow2_floor(int x) {
@@ -54,7 +54,7 @@ int pow2_floor(int x) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
-    size_t counter_bytes;
+    size_t aop_offset, aop_bytes;
     size_t partial_offset, partial_bytes;
     size_t total;
     int splits, steps_per_split;
@@ -74,30 +74,28 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     l.mtiles = (ga.RB + plan.mb - 1) / plan.mb;
     l.ntiles = (gb.RB + plan.nb * plan.wn - 1) / (plan.nb * plan.wn);
     if ((long long)l.mtiles * l.ntiles * l.splits >= (1LL << 31)) return MX_EINVAL;
-    if (l.splits > 1) {
-        if ((long long)l.mtiles * l.ntiles > mx4::kMaxSplitTiles) return MX_EPLAN;
-        l.counter_bytes = mx4::kCounterRegionBytes;
-        l.partial_offset = l.counter_bytes;
-        l.partial_bytes = round_up((size_t)l.splits * M * gb.RB * mx4::kRowBlock * sizeof(float), 256);
-    } else {
-        l.counter_bytes = l.partial_offset = l.partial_bytes = 0;
-    }
-    l.total = l.counter_bytes + l.partial_bytes;
+    l.aop_offset = 0;
+    l.aop_bytes = plan.preq ? round_up(ga.total_bytes, 256) : 0;
+    l.partial_offset = l.aop_bytes;
+    l.partial_bytes = l.splits > 1 ? round_up((size_t)l.splits * M * gb.RB * mx4::kRowBlock * sizeof(float), 256) : 0;
+    l.total = l.aop_bytes + l.partial_bytes;
     *out = l;
     return MX_OK;
 }
 
-// Model for shapes without a table entry.  Two 32-row M blocks per
-// workgroup when M allows, one N block per wave, 8 waves along K (fewer for
-// short K); then the fewest K splits that keep every wave within its register
-// budget and the activation slice within the LDS budget, doubled while the
-// tiles leave most of the 256 CUs idle and the fp32 partials stay small next
-// to the weight.
+// Model for shapes without a table entry: quantise A inside the GEMM while
+// the activation slice of a workgroup is small next to the weight it meets,
+// else in a first kernel; two 32-row M blocks per wave when M allows, one
+// N block per wave, 8 waves along K (fewer for short K); then the fewest K
+// splits that keep every wave within its register budget and the activation
+// slice within LDS, doubled while the tiles leave most of the 256 CUs idle
+// and the fp32 partials stay small next to the weight.
 Plan model_plan(int M, int N, int K) {
     const OperandGeom ga = mx4::operand_geom(M, K);
     const OperandGeom gb = mx4::operand_geom(N, K);
     Plan p;
-    p.mb = ga.RB >= 2 ? 2 : 1;
+    p.preq = (ga.RB > 1 || gb.KS > 16) ? 1 : 0;
+    p.mb = (p.preq && ga.RB >= 2) ? 2 : 1;
     p.nb = 1;
     p.wn = 1;
     p.wk = pow2_floor(gb.KS < 8 ? gb.KS : 8);
@@ -125,6 +123,7 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     rc = check_operand_shape(N, K);
     if (rc) return rc;
     if (lda < K || lda % 8 != 0 || ldc < N) return MX_EINVAL;
+    if ((unsigned long long)M * lda * 2 >= (1ULL << 31)) return MX_EINVAL;
     if (!aligned(A, 16) || !aligned(packed, 16) || !aligned(C, 2)) return MX_EALIGN;
     Layout lay;
     rc = plan_layout(plan, M, N, K, &lay);
@@ -136,13 +135,19 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     const OperandGeom ga = mx4::operand_geom(M, K);
     const OperandGeom gb = mx4::operand_geom(N, K);
     uint8_t* wsb = (uint8_t*)ws;
+    hipStream_t s = (hipStream_t)stream;
 
     GemmParams p;
     memset(&p, 0, sizeof p);
     p.A = (const uint16_t*)A;
     p.lda = lda;
+    p.a_bytes = (uint32_t)((size_t)M * lda * 2);
+    p.aop = plan.preq ? wsb + lay.aop_offset : nullptr;
+    p.aop_bytes = (uint32_t)ga.total_bytes;
+    p.a_code_bytes = (uint32_t)ga.code_bytes;
     p.bp = (const uint8_t*)packed;
-    p.b_code_bytes = gb.code_bytes;
+    p.bp_bytes = (uint32_t)gb.total_bytes;
+    p.b_code_bytes = (uint32_t)gb.code_bytes;
     p.KS = gb.KS;
     p.KW = gb.KW;
     p.M = M;
@@ -159,11 +164,17 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     p.c_vec = (ldc % 4 == 0 && aligned(C, 8)) ? 1 : 0;
     p.partial = lay.splits > 1 ? (float*)(wsb + lay.partial_offset) : nullptr;
     p.ldp = gb.RB * mx4::kRowBlock;
-    p.counters = lay.splits > 1 ? (int*)wsb : nullptr;
 
+    if (plan.preq) {
+        rc = hip_status(mx4::launch_pack((const uint16_t*)A, M, K, lda, wsb + lay.aop_offset, s));
+        if (rc) return rc;
+    }
     Plan run = plan;
     run.splits = lay.splits;
-    return hip_status(mx4::launch_gemm(run, p, (hipStream_t)stream));
+    rc = hip_status(mx4::launch_gemm(run, p, s));
+    if (rc) return rc;
+    if (lay.splits > 1) rc = hip_status(mx4::launch_reduce(p, s));
+    return rc;
 }
 
 }  // namespace
@@ -231,6 +242,7 @@ int mx_gemm_plan(int M, int N, int K, mx_plan* plan_host) {
     plan_host->wn = p.wn;
     plan_host->wk = p.wk;
     plan_host->splits = lay.splits;
+    plan_host->preq = p.preq;
     return MX_OK;
 }
 
@@ -240,7 +252,7 @@ int mx_gemm_plan_workspace_bytes(const mx_plan* plan_host, int M, int N, int K, 
     if (rc) return rc;
     rc = check_operand_shape(N, K);
     if (rc) return rc;
-    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wn, plan_host->wk, plan_host->splits};
+    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wn, plan_host->wk, plan_host->splits, plan_host->preq};
     Layout lay;
     rc = plan_layout(p, M, N, K, &lay);
     if (rc) return rc;
@@ -258,7 +270,7 @@ int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host) {
 int mx_gemm_with_plan(const void* A_dev, int M, int K, int lda, const void* packed_dev, int N, void* C_dev, int ldc,
                       void* ws_dev, size_t ws_bytes, const mx_plan* plan_host, void* stream) {
     if (!plan_host) return MX_EALIGN;
-    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wn, plan_host->wk, plan_host->splits};
+    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wn, plan_host->wk, plan_host->splits, plan_host->preq};
     return gemm_impl(A_dev, M, K, lda, packed_dev, N, C_dev, ldc, ws_dev, ws_bytes, p, stream);
 }
 

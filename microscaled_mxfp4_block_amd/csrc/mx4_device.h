@@ -100,8 +100,34 @@ __device__ __forceinline__ f32x16 mfma_fp4_32x32x64(const u32x4& a, const u32x4&
                                                            (int)scale_b);
 }
 
+// 32 wait states after an MFMA whose result is read next: more than the
+// longest MFMA-result-to-VALU distance of the 32x32x64 scaled MFMA.
+__device__ __forceinline__ void mfma_result_fence(f32x16& acc) {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(acc));
+}
+
 __device__ __forceinline__ u32x4 load16_nt(const void* p) {
     return __builtin_nontemporal_load((const u32x4*)p);
+}
+
+// Buffer resources (gfx9 descriptor, raw 32-bit data format): the base and
+// size live in SGPRs, each load adds a 32-bit lane offset and a wave-uniform
+// offset, and any byte past `bytes` reads as zero.
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr int kBufferDword3 = 0x00020000;
+constexpr int kNonTemporal = 2;   // cache-policy bit: streamed once, do not keep
+
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kBufferDword3);
+}
+
+template <int AUX = 0>
+__device__ __forceinline__ u32x4 bload16(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX);
+}
+
+__device__ __forceinline__ uint32_t bload4(Rsrc r, uint32_t voff, uint32_t soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }
 
 __device__ __forceinline__ u32x4 load16(const void* p) {

@@ -1,35 +1,32 @@
-// mx4_gemm.hip -- single-launch MXFP4 GEMM for gfx950 (MI355X).
+// mx4_gemm.hip -- block-scaled MXFP4 GEMM for gfx950 (MI355X).
 //
 //   C[M,N] = bf16_RNE( sum_k deq(A)[m,k] * deq(B)[n,k] )   (fp32 accumulation)
 //
-// One kernel does the whole call: activation quantisation, the block-scaled
-// fp4 contraction and (for split-K) the reduction of the K partials.  The
-// contraction is what the kernelindex.com amd-mxfp4-mm pages write as
+// The contraction is what the kernelindex.com amd-mxfp4-mm pages write as
 // tl.dot_scaled(a, a_scale, "e2m1", b, b_scale, "e2m1") (e.g. submission
 // 748756, kernel_fused_mxfp4_gemm); here it runs directly on
 // v_mfma_scale_f32_32x32x64_f8f6f4, whose per-lane e8m0 byte scales that
 // lane's 32-element group by 2^(byte-127).
 //
-// Workgroup = WN x WK waves; workgroup tile = (32 MBLK) m x (32 NBLK WN) n
-// over one K split of `steps_per_split` steps of 64.
-//   1. Every wave issues the 128-bit loads of all its weight fragments for
-//      its share of the split (WK waves share the split's K steps) before
-//      anything else, so the one HBM round trip of the weight overlaps the
-//      activation work below.  Weight bytes are read exactly once, straight
-//      into VGPRs (non-temporal: they are never reused).
-//   2. The workgroup quantises the activation slice it needs (its m rows x
-//      its K split) once: one lane per 32-element group, amax is a per-lane
-//      max, scale byte by the bit rule, e2m1 codes by the gfx950 fp4 convert.
-//      The codes land in LDS in MFMA operand order, shared by the WN waves
-//      that use them.
-//   3. K loop: 16-byte LDS reads of the activation fragments, MFMAs against
-//      the weight fragments already in registers.
-//   4. The WK waves add their accumulators through LDS.  With one split the
-//      result is rounded to bf16 and stored.  With several splits each
-//      workgroup writes its fp32 partial tile, then counts itself in on the
-//      tile's arrival counter; the last one to arrive sums the partials of all
-//      splits in split order (deterministic) and stores bf16, and resets the
-//      counter to zero for the next call.
+// Workgroup = WN x WK waves; a wave owns (32 MBLK) m x (32 NBLK) n outputs,
+// the WN waves of a workgroup sit side by side along N and the WK waves
+// share the K steps of the workgroup's K split.
+//   1. Every wave issues the 128-bit loads of all its weight fragments (its
+//      whole share of the split) before anything else: the weight costs one
+//      HBM round trip, read exactly once, straight into VGPRs, non-temporal.
+//   2. The activation operand:
+//      FUSED   the workgroup quantises its activation slice (its m rows x its
+//              K split) itself into LDS, in MFMA lane order: one lane per
+//              32-element group, per-lane amax, scale byte by the bit rule,
+//              e2m1 codes by the gfx950 fp4 convert;
+//      !FUSED  a first kernel (pack_kernel) quantised A into the packed
+//              operand layout in the workspace; each wave loads its
+//              fragments from there (L2-resident) together with step 1.
+//   3. K loop: MFMAs on registers (and 16-byte LDS reads when FUSED).
+//   4. The WK waves add their accumulators through LDS; the result is
+//      rounded to bf16 and stored, or, when K is split over workgroups,
+//      written as fp32 partials that reduce_kernel sums in split order
+//      (deterministic, no atomics).
 #include "mx4_device.h"
 #include "mx4_internal.h"
 
@@ -42,15 +39,6 @@ namespace mx4 {
 __device__ __forceinline__ int xcd_linear(int i, int G) {
     const int q = G / 8, r = G % 8, x = i % 8;
     return x * q + (x < r ? x : r) + i / 8;
-}
-
-// Activation operand in LDS: codes [MBLK][T][64 lanes][16 B], then scale
-// bytes [MBLK][T][64 lanes]; T = K steps of the split.
-__device__ __forceinline__ uint32_t lds_code_off(int mb, int tl, int lane, int T) {
-    return (uint32_t)(((mb * T + tl) * 64 + lane) * 16);
-}
-__device__ __forceinline__ uint32_t lds_scale_off(int mb, int tl, int lane, int T, int mblk) {
-    return (uint32_t)(mblk * T * 64 * 16 + (mb * T + tl) * 64 + lane);
 }
 
 // 4 consecutive bf16 outputs (n0..n0+3) of row m, masked at N.
@@ -68,13 +56,15 @@ __device__ __forceinline__ void store_bf16x4(const GemmParams& p, int m, int n0,
     }
 }
 
-template <int MBLK, int NBLK, int WN, int WK>
-__global__ void __launch_bounds__(64 * WN * WK) gemm_kernel(GemmParams p) {
+template <int MBLK, int NBLK, int WN, int WK, bool FUSED, int KR>
+__global__ void __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(2)))
+gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    __shared__ int last_flag;
     constexpr int NT = 64 * WN * WK;
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    // wave-uniform values in SGPRs: weight and operand base addresses then
+    // stay scalar and each load needs one 32-bit lane offset
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = tid & 63;
     const int wn = wave % WN;
     const int wkk = wave / WN;
@@ -92,69 +82,81 @@ __global__ void __launch_bounds__(64 * WN * WK) gemm_kernel(GemmParams p) {
     const int T = te - tb;
     const int per_wave = (T + WK - 1) / WK;
     const int wb = tb + wkk * per_wave;
-    const int we = min(wb + per_wave, te);
-    const int nsteps = max(we - wb, 0);      // <= kStepsPerWaveMax by the planner
+    const int nsteps = max(min(wb + per_wave, te) - wb, 0);   // <= KR by the planner
+    // Steps s >= nsteps are padding: their loads get a lane offset past every
+    // buffer's end and read zeros, so the load and MFMA sequences below are
+    // the same straight-line code for every wave.
+    constexpr uint32_t kOutOfRange = 0x80000000u;
 
-    // ---- 1. weight fragments of this wave, all in flight at once
-    u32x4 bfrag[kStepsPerWaveMax][NBLK];
-    uint32_t bscale[kStepsPerWaveMax][NBLK];
+    // ---- 1. weight (and pre-quantised activation) fragments, all in flight.
+    // Buffer loads: the wave-uniform part of every offset is a scalar, the
+    // lane part one VGPR; blocks past the operand's end read as zero.
+    const Rsrc rb_ = make_rsrc(p.bp, p.bp_bytes);
+    const Rsrc ra_ = make_rsrc(p.aop, p.aop_bytes);
+    u32x4 bfrag[KR][NBLK];
+    uint32_t bscale[KR][NBLK];
+    u32x4 afrag[FUSED ? 1 : KR][MBLK];
+    uint32_t ascale[FUSED ? 1 : KR][MBLK];
 #pragma unroll
-    for (int s = 0; s < kStepsPerWaveMax; ++s) {
-        if (s < nsteps) {
-            const int t = wb + s;
+    for (int s = 0; s < KR; ++s) {
+        const bool on = s < nsteps;
+        const int t = min(wb + s, p.KS - 1);
+        const uint32_t vcode = on ? (uint32_t)L * 16u : kOutOfRange;
+        const uint32_t vscale = on ? (uint32_t)L * 4u : kOutOfRange;
 #pragma unroll
-            for (int j = 0; j < NBLK; ++j) {
-                const int nb = min(nb0 + j, p.RBn - 1);   // clamped blocks are never stored
-                bfrag[s][j] = load16_nt(p.bp + ((size_t)(nb * p.KS + t) * 64 + L) * 16);
-                bscale[s][j] = *(const uint32_t*)(p.bp + p.b_code_bytes +
-                                                  ((size_t)(nb * p.KW + (t >> 2)) * 64 + L) * 4);
+        for (int j = 0; j < NBLK; ++j) {
+            const int nb = min(nb0 + j, p.RBn - 1);   // clamped blocks are never stored
+            bfrag[s][j] = bload16<kNonTemporal>(rb_, vcode, (uint32_t)(nb * p.KS + t) * 1024u);
+            bscale[s][j] = bload4(rb_, vscale, p.b_code_bytes + (uint32_t)(nb * p.KW + (t >> 2)) * 256u);
+        }
+        if constexpr (!FUSED) {
+#pragma unroll
+            for (int i = 0; i < MBLK; ++i) {
+                const int mb = min(mb0 + i, p.RBm - 1);   // clamped blocks are never stored
+                afrag[s][i] = bload16(ra_, vcode, (uint32_t)(mb * p.KS + t) * 1024u);
+                ascale[s][i] = bload4(ra_, vscale, p.a_code_bytes + (uint32_t)(mb * p.KW + (t >> 2)) * 256u);
             }
         }
     }
 
-    // ---- 2. quantise the activation slice into LDS
-    const int row0 = mb0 * kRowBlock;
-    const int rows = min(p.M - row0, MBLK * kRowBlock);   // >= 1
-    const int G = p.K / kGroup;
-    const int g0 = 2 * tb;
-    const int g1 = min(2 * te, G);
-    const int Gw = g1 - g0;
-    if (rows < MBLK * kRowBlock || g1 < 2 * te) {
-        // padding rows / the missing last group: zero codes and zero scale bytes
-        const int words = MBLK * T * 64 * 17 / 4;
-        for (int i = tid; i < words; i += NT) ((uint32_t*)lds)[i] = 0u;
-        __syncthreads();
-    }
-    {
-        const int units = rows * Gw;
-        constexpr int QREG = 4;   // units per thread whose loads are issued together
-        for (int u0 = 0; u0 < units; u0 += NT * QREG) {
+    // ---- 2. (FUSED) quantise the activation slice into LDS, MFMA lane order:
+    // slot u = (mb * T + tl) * 64 + lane holds row 32 (mb0 + mb) + lane % 32,
+    // group 2 (tb + tl) + lane / 32; codes at 16 u, scale byte at
+    // 16 MBLK T 64 + u.  Rows past M read as zero through the buffer bound
+    // and quantise to zero codes with scale byte 0; a group past K (K % 64
+    // == 32) is zeroed explicitly.
+    if constexpr (FUSED) {
+        const Rsrc rx_ = make_rsrc(p.A, p.a_bytes);
+        const int slots = MBLK * T * 64;
+        const int G = p.K / kGroup;
+        constexpr int QREG = 2;   // slots per thread whose loads are issued together
+        for (int u0 = 0; u0 < slots; u0 += NT * QREG) {
             u32x4 x[QREG][4];
+            bool live[QREG];
 #pragma unroll
             for (int q = 0; q < QREG; ++q) {
                 const int u = u0 + q * NT + tid;
-                if (u < units) {
-                    const int r = u / Gw, g = g0 + u % Gw;
-                    const uint16_t* src = p.A + (size_t)(row0 + r) * p.lda + (size_t)g * kGroup;
+                const int lane = u & 63, mtl = u >> 6;
+                const int row = (mb0 + mtl / T) * kRowBlock + (lane & 31);
+                const int g = 2 * (tb + mtl % T) + (lane >> 5);
+                live[q] = u < slots && g < G;
+                const uint32_t off = live[q] ? (uint32_t)row * (uint32_t)p.lda * 2u + (uint32_t)g * 64u : p.a_bytes;
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) x[q][c] = load16(src + 8 * c);
-                }
+                for (int c = 0; c < 4; ++c) x[q][c] = bload16(rx_, off + 16u * c, 0u);
             }
 #pragma unroll
             for (int q = 0; q < QREG; ++q) {
                 const int u = u0 + q * NT + tid;
-                if (u < units) {
-                    const int r = u / Gw, g = g0 + u % Gw;
+                if (u < slots) {
                     u32x4 codes;
                     const uint32_t byte = quant_group32(x[q], codes);
-                    const int mb = r >> 5, tl = (g >> 1) - tb, lane = (r & 31) + 32 * (g & 1);
-                    *(u32x4*)(lds + lds_code_off(mb, tl, lane, T)) = codes;
-                    lds[lds_scale_off(mb, tl, lane, T, MBLK)] = (uint8_t)byte;
+                    *(u32x4*)(lds + 16 * u) = codes;
+                    lds[16 * slots + u] = (uint8_t)byte;
                 }
             }
         }
+        __syncthreads();
     }
-    __syncthreads();
 
     // ---- 3. K loop over the wave's steps
     f32x16 acc[MBLK][NBLK];
@@ -165,27 +167,40 @@ __global__ void __launch_bounds__(64 * WN * WK) gemm_kernel(GemmParams p) {
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 #pragma unroll
-    for (int s = 0; s < kStepsPerWaveMax; ++s) {
-        if (s < nsteps) {
-            const int t = wb + s;
-            const int tl = t - tb;
-            const int sh = 8 * (t & 3);
-            u32x4 af[MBLK];
-            uint32_t as[MBLK];
+    for (int s = 0; s < KR; ++s) {
+        const int t = wb + s;
+        const int sh = 8 * (t & 3);
+        u32x4 af[MBLK];
+        uint32_t as[MBLK];
 #pragma unroll
-            for (int i = 0; i < MBLK; ++i) {
-                af[i] = *(const u32x4*)(lds + lds_code_off(i, tl, L, T));
-                as[i] = lds[lds_scale_off(i, tl, L, T, MBLK)];
-            }
-#pragma unroll
-            for (int j = 0; j < NBLK; ++j) {
-                const uint32_t bs = bscale[s][j] >> sh;
-#pragma unroll
-                for (int i = 0; i < MBLK; ++i)
-                    acc[i][j] = mfma_fp4_32x32x64(bfrag[s][j], af[i], acc[i][j], bs, as[i]);
+        for (int i = 0; i < MBLK; ++i) {
+            if constexpr (FUSED) {
+                const bool on = s < nsteps;
+                const int u = (i * T + min(t - tb, T - 1)) * 64 + L;
+                const u32x4 a = *(const u32x4*)(lds + 16 * u);
+                af[i] = on ? a : u32x4{0u, 0u, 0u, 0u};
+                as[i] = lds[16 * MBLK * T * 64 + u];
+            } else {
+                af[i] = afrag[s][i];
+                as[i] = ascale[s][i] >> sh;
             }
         }
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j) {
+            const uint32_t bs = bscale[s][j] >> sh;
+#pragma unroll
+            for (int i = 0; i < MBLK; ++i)
+                acc[i][j] = mfma_fp4_32x32x64(bfrag[s][j], af[i], acc[i][j], bs, as[i]);
+        }
     }
+
+    // The epilogue reads the accumulators right after the last MFMA; pad the
+    // MFMA-result-to-VALU distance explicitly (the asm names every
+    // accumulator, so it stays after the MFMAs and before the first read).
+#pragma unroll
+    for (int i = 0; i < MBLK; ++i)
+#pragma unroll
+        for (int j = 0; j < NBLK; ++j) mfma_result_fence(acc[i][j]);
 
     // ---- 4. epilogue
     // lane L, element e of tile (i, j): m = 32 (mb0 + i) + L % 32,
@@ -195,7 +210,7 @@ __global__ void __launch_bounds__(64 * WN * WK) gemm_kernel(GemmParams p) {
     constexpr int E = MBLK * NBLK * 16;       // accumulator floats per lane
     float* red = (float*)lds;
     if constexpr (WK > 1) {
-        __syncthreads();   // every wave is done with the activation operand
+        if constexpr (FUSED) __syncthreads();   // every wave is done with the activation operand
 #pragma unroll
         for (int i = 0; i < MBLK; ++i)
 #pragma unroll
@@ -205,13 +220,35 @@ __global__ void __launch_bounds__(64 * WN * WK) gemm_kernel(GemmParams p) {
         __syncthreads();
     }
     // groups of 4 consecutive n per (i, j, r); the WK waves of column wn share them
-    constexpr int GPW = MBLK * NBLK * 4;
-    const bool partial = p.splits > 1;
-    for (int gi = wkk; gi < GPW; gi += WK) {
-        const int ij = gi >> 2, r = gi & 3;
-        const int i = ij / NBLK, j = ij % NBLK;
-        float v[4];
-        if constexpr (WK > 1) {
+    auto emit = [&](int i, int j, int r, const float (&v)[4]) {
+        const int m = (mb0 + i) * kRowBlock + m_lane;
+        const int nb = nb0 + j;
+        const int n0 = nb * kRowBlock + 8 * r + n_lane;
+        if (m >= p.M || nb >= p.RBn) return;
+        if (p.splits > 1) {
+            const f32x4 pv = {v[0], v[1], v[2], v[3]};
+            *(f32x4*)(p.partial + ((size_t)split * p.M + m) * p.ldp + n0) = pv;
+        } else {
+            store_bf16x4(p, m, n0, v);
+        }
+    };
+    if constexpr (WK == 1) {
+#pragma unroll
+        for (int i = 0; i < MBLK; ++i)
+#pragma unroll
+            for (int j = 0; j < NBLK; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float v[4] = {acc[i][j][4 * r], acc[i][j][4 * r + 1], acc[i][j][4 * r + 2],
+                                        acc[i][j][4 * r + 3]};
+                    emit(i, j, r, v);
+                }
+    } else {
+        constexpr int GPW = MBLK * NBLK * 4;
+        for (int gi = wkk; gi < GPW; gi += WK) {
+            const int ij = gi >> 2, r = gi & 3;
+            const int i = ij / NBLK, j = ij % NBLK;
+            float v[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 float s = 0.0f;
@@ -220,107 +257,125 @@ __global__ void __launch_bounds__(64 * WN * WK) gemm_kernel(GemmParams p) {
                     s += red[(((w2 * WN + wn) * E) + (i * NBLK + j) * 16 + 4 * r + q) * 64 + L];
                 v[q] = s;
             }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = acc[i][j][4 * r + q];
-        }
-        const int m = (mb0 + i) * kRowBlock + m_lane;
-        const int nb = nb0 + j;
-        const int n0 = nb * kRowBlock + 8 * r + n_lane;
-        if (m >= p.M || nb >= p.RBn) continue;
-        if (partial) {
-            const f32x4 pv = {v[0], v[1], v[2], v[3]};
-            *(f32x4*)(p.partial + ((size_t)split * p.M + m) * p.ldp + n0) = pv;
-        } else {
-            store_bf16x4(p, m, n0, v);
+            emit(i, j, r, v);
         }
     }
-    if (!partial) return;
-
-    // ---- split-K finish: the last workgroup of this tile to arrive reduces it
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");   // publish this wave's partial stores
-    __syncthreads();
-    const int tile = nt * p.mtiles + mt;
-    if (tid == 0) {
-        const int old = __hip_atomic_fetch_add(p.counters + tile, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last_flag = (old == p.splits - 1);
-    }
-    __syncthreads();
-    if (!last_flag) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    const int m_base = mb0 * kRowBlock;
-    const int n_base = nt * WN * NBLK * kRowBlock;
-    constexpr int TW4 = WN * NBLK * kRowBlock / 4;   // float4 groups per tile row
-    for (int g = tid; g < MBLK * kRowBlock * TW4; g += NT) {
-        const int m = m_base + g / TW4;
-        const int n0 = n_base + 4 * (g % TW4);
-        if (m >= p.M || n0 >= p.RBn * kRowBlock) continue;
-        f32x4 s = *(const f32x4*)(p.partial + (size_t)m * p.ldp + n0);
-        for (int k = 1; k < p.splits; ++k) {
-            const f32x4 x = *(const f32x4*)(p.partial + ((size_t)k * p.M + m) * p.ldp + n0);
-            s.x += x.x;
-            s.y += x.y;
-            s.z += x.z;
-            s.w += x.w;
-        }
-        const float v[4] = {s.x, s.y, s.z, s.w};
-        store_bf16x4(p, m, n0, v);
-    }
-    if (tid == 0) __hip_atomic_store(p.counters + tile, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
-// Instantiation table: MBLK, NBLK in {1, 2}; WN in {1, 2, 4}; WK in {1, 2, 4, 8}
-// with at most 16 waves (1024 lanes) per workgroup.
+// Instantiation table.  This file is compiled once per K-step budget KR
+// (-DMX4_KR=1, 2, 4 or 8); each object instantiates MBLK, NBLK in {1, 2},
+// WN in {1, 2}, WK in {1, 2, 4, 8, 16} (at most 16 waves), FUSED in {0, 1}.
+
+#ifndef MX4_KR
+#error "compile with -DMX4_KR=<K steps per wave>"
+#endif
 
 typedef void (*GemmFn)(GemmParams);
 
-template <int MBLK, int NBLK, int WN>
-GemmFn pick_wk(int wk) {
+template <int MBLK, int NBLK, int WN, bool FUSED>
+static GemmFn pick_wk(int wk) {
+    constexpr int KR = MX4_KR;
     switch (wk) {
-        case 1: return gemm_kernel<MBLK, NBLK, WN, 1>;
-        case 2: return gemm_kernel<MBLK, NBLK, WN, 2>;
-        case 4: return gemm_kernel<MBLK, NBLK, WN, 4>;
-        case 8: return WN <= 2 ? gemm_kernel<MBLK, NBLK, WN, (WN <= 2 ? 8 : 4)> : nullptr;
+        case 1: return gemm_kernel<MBLK, NBLK, WN, 1, FUSED, KR>;
+        case 2: return gemm_kernel<MBLK, NBLK, WN, 2, FUSED, KR>;
+        case 4: return gemm_kernel<MBLK, NBLK, WN, 4, FUSED, KR>;
+        case 8: return gemm_kernel<MBLK, NBLK, WN, 8, FUSED, KR>;
+        case 16: return WN == 1 ? gemm_kernel<MBLK, NBLK, WN, (WN == 1 ? 16 : 8), FUSED, KR> : nullptr;
         default: return nullptr;
     }
 }
 
-template <int MBLK, int NBLK>
-GemmFn pick_wn(int wn, int wk) {
+template <int MBLK, int NBLK, bool FUSED>
+static GemmFn pick_wn(int wn, int wk) {
     switch (wn) {
-        case 1: return pick_wk<MBLK, NBLK, 1>(wk);
-        case 2: return pick_wk<MBLK, NBLK, 2>(wk);
-        case 4: return pick_wk<MBLK, NBLK, 4>(wk);
+        case 1: return pick_wk<MBLK, NBLK, 1, FUSED>(wk);
+        case 2: return pick_wk<MBLK, NBLK, 2, FUSED>(wk);
         default: return nullptr;
     }
 }
 
-static GemmFn find_kernel(const Plan& plan) {
-    if (plan.mb == 1 && plan.nb == 1) return pick_wn<1, 1>(plan.wn, plan.wk);
-    if (plan.mb == 1 && plan.nb == 2) return pick_wn<1, 2>(plan.wn, plan.wk);
-    if (plan.mb == 2 && plan.nb == 1) return pick_wn<2, 1>(plan.wn, plan.wk);
-    if (plan.mb == 2 && plan.nb == 2) return pick_wn<2, 2>(plan.wn, plan.wk);
+template <bool FUSED>
+static GemmFn pick_tile(const Plan& plan) {
+    if (plan.mb == 1 && plan.nb == 1) return pick_wn<1, 1, FUSED>(plan.wn, plan.wk);
+    if (plan.mb == 1 && plan.nb == 2) return pick_wn<1, 2, FUSED>(plan.wn, plan.wk);
+    if (plan.mb == 2 && plan.nb == 1) return pick_wn<2, 1, FUSED>(plan.wn, plan.wk);
+    if (plan.mb == 2 && plan.nb == 2) return pick_wn<2, 2, FUSED>(plan.wn, plan.wk);
     return nullptr;
 }
 
+#define MX4_CAT2(a, b) a##b
+#define MX4_CAT(a, b) MX4_CAT2(a, b)
+GemmFn MX4_CAT(find_gemm_kr, MX4_KR)(const Plan& plan) {
+    return plan.preq ? pick_tile<false>(plan) : pick_tile<true>(plan);
+}
+
+#if MX4_KR == 1
+// The split-K reduction and the launch helpers live in one object only.
+__global__ void __launch_bounds__(256) reduce_kernel(GemmParams p) {
+    const int n4 = (p.N + 3) / 4;
+    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (gid >= (long long)p.M * n4) return;
+    const int m = (int)(gid / n4);
+    const int n0 = (int)(gid % n4) * 4;
+    f32x4 s = *(const f32x4*)(p.partial + (size_t)m * p.ldp + n0);
+    for (int k = 1; k < p.splits; ++k) {
+        const f32x4 x = *(const f32x4*)(p.partial + ((size_t)k * p.M + m) * p.ldp + n0);
+        s.x += x.x;
+        s.y += x.y;
+        s.z += x.z;
+        s.w += x.w;
+    }
+    const float v[4] = {s.x, s.y, s.z, s.w};
+    store_bf16x4(p, m, n0, v);
+}
+
+GemmFn find_gemm_kr2(const Plan& plan);
+GemmFn find_gemm_kr4(const Plan& plan);
+GemmFn find_gemm_kr8(const Plan& plan);
+
+int gemm_kr_for(int steps_per_wave) {
+    for (int kr = 1; kr <= kStepsPerWaveMax; kr *= 2)
+        if (steps_per_wave <= kr) return kr;
+    return 0;
+}
+
+static GemmFn find_kernel(const Plan& plan, int kr) {
+    switch (kr) {
+        case 1: return find_gemm_kr1(plan);
+        case 2: return find_gemm_kr2(plan);
+        case 4: return find_gemm_kr4(plan);
+        case 8: return find_gemm_kr8(plan);
+        default: return nullptr;
+    }
+}
+
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
-    const size_t a_op = (size_t)plan.mb * steps_per_split * 64 * 17;
+    const size_t a_op = plan.preq ? 0 : (size_t)plan.mb * steps_per_split * 64 * 17;
     const size_t red = plan.wk > 1 ? (size_t)plan.wn * plan.wk * plan.mb * plan.nb * 16 * 64 * 4 : 0;
     return a_op > red ? a_op : red;
 }
 
 bool gemm_plan_supported(const Plan& plan) {
-    return plan.splits >= 1 && find_kernel(plan) != nullptr;
+    return plan.splits >= 1 && find_kernel(plan, 1) != nullptr;
 }
 
 hipError_t launch_gemm(const Plan& plan, const GemmParams& p, hipStream_t s) {
-    GemmFn fn = find_kernel(plan);
+    const int per_wave = (p.steps_per_split + plan.wk - 1) / plan.wk;
+    GemmFn fn = find_kernel(plan, gemm_kr_for(per_wave));
     if (!fn) return hipErrorInvalidValue;
     const long long grid = (long long)p.mtiles * p.ntiles * p.splits;
     const size_t lds = gemm_lds_bytes(plan, p.steps_per_split);
     hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * plan.wn * plan.wk), lds, s, p);
     return hipGetLastError();
 }
+
+hipError_t launch_reduce(const GemmParams& p, hipStream_t s) {
+    const long long total = (long long)p.M * ((p.N + 3) / 4);
+    const long long blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+#endif
 
 }  // namespace mx4

@@ -14,22 +14,21 @@ namespace mx4 {
 constexpr int kStepsPerWaveMax = 8;
 // Largest LDS block the planner gives a workgroup.
 constexpr size_t kLdsBudget = 64 * 1024;
-// The workspace starts with a fixed region of per-tile arrival counters that
-// no shape ever uses for anything else, so counters left at zero by one call
-// are zero for the next call whatever its shape; split-K plans are limited to
-// this many output tiles.
-constexpr size_t kCounterRegionBytes = 64 * 1024;
-constexpr int kMaxSplitTiles = (int)(kCounterRegionBytes / sizeof(int));
 
-// Arguments of the GEMM kernel.  The MFMA's first operand is the weight tile
-// (rows = N), the second the activation tile (rows = M), so each lane's 16
-// outputs are runs of 4 consecutive n for one m.
+// Arguments of the GEMM and reduction kernels.  The MFMA's first operand is
+// the weight tile (rows = N), the second the activation tile (rows = M), so
+// each lane's 16 outputs are runs of 4 consecutive n for one m.
 struct GemmParams {
-    const uint16_t* A;        // bf16 activations [M, lda], quantised in the kernel
+    const uint16_t* A;        // bf16 activations [M, lda] (quantised in the GEMM when fused)
     int lda;
+    uint32_t a_bytes;         // bytes of A a buffer load may touch: M * lda * 2
+    const uint8_t* aop;       // activations quantised into the packed layout (not fused)
+    uint32_t aop_bytes;
+    uint32_t a_code_bytes;
     const uint8_t* bp;        // packed weight
-    size_t b_code_bytes;
-    int KS, KW;               // K steps of 64 and scale words of 4 steps
+    uint32_t bp_bytes;
+    uint32_t b_code_bytes;
+    int KS, KW;               // K steps of 64 and scale words of 4 steps (A and B alike)
     int M, N, K;
     int RBm, RBn;             // 32-row blocks of M and N
     int mtiles, ntiles;       // workgroup tiles along M and N
@@ -40,18 +39,19 @@ struct GemmParams {
     int c_vec;                // 1 when rows of C are 8-byte aligned (ldc % 4 == 0)
     float* partial;           // fp32 partials [splits, M, ldp] when splits > 1
     int ldp;
-    int* counters;            // per-tile arrival counters (zero between calls)
 };
 
-// mb: 32-row M blocks per workgroup; nb: 32-row N blocks per wave;
-// wn x wk waves per workgroup (wn along N, wk along K); splits along K.
+// mb: 32-row M blocks per wave; nb: 32-row N blocks per wave; wn x wk waves
+// per workgroup (wn along N, wk along K); splits along K; preq: quantise A
+// in a separate first kernel instead of inside the GEMM.
 struct Plan {
-    int mb, nb, wn, wk, splits;
+    int mb, nb, wn, wk, splits, preq;
 };
 
 bool gemm_plan_supported(const Plan& p);
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split);
 hipError_t launch_gemm(const Plan& plan, const GemmParams& p, hipStream_t s);
+hipError_t launch_reduce(const GemmParams& p, hipStream_t s);
 
 hipError_t launch_quant_natural(const uint16_t* x, int rows, int K, int ld, uint8_t* codes, uint8_t* scales,
                                 hipStream_t s);

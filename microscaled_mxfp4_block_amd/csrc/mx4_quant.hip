@@ -55,45 +55,35 @@ __global__ void __launch_bounds__(256) quant_natural_kernel(const uint16_t* __re
     if ((kc & 3) == 0) scales[(size_t)r * (K / 32) + kc / 4] = (uint8_t)byte;
 }
 
-// Packed-layout quantiser.  One lane per (row block rb, scale word w, lane L):
-// it quantises the groups of up to four K steps t = 4w..4w+3 for row
-// 32 rb + L % 32, group 2t + L / 32, writing each 16-byte code fragment to its
-// tile slot and the four scale bytes as one word.  Lanes of a wave are the 64
-// lanes of one (rb, w), so every code store is a fully coalesced 1 KiB.
+// Packed-layout quantiser.  One lane per operand slot (rb, t, L): it loads
+// the 64 bytes of row 32 rb + L % 32, group 2t + L / 32 with four 16-byte
+// loads, quantises them, writes the 16-byte code fragment to its slot (the
+// 64 lanes of a wave write one contiguous 1 KiB tile) and its scale byte into
+// byte t % 4 of the lane's scale word.  Every lane does one load round trip.
 __global__ void __launch_bounds__(256) pack_kernel(const uint16_t* __restrict__ x, int rows, int K, int ld,
                                                    uint8_t* __restrict__ packed, int RB, int KS, int KW,
                                                    size_t code_bytes) {
     const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long long total = (long long)RB * KW * 64;
+    const long long total = (long long)RB * KW * kStepsPerWord * 64;
     if (gid >= total) return;
     const int L = (int)(gid & 63);
-    const long long tw = gid >> 6;
-    const int w = (int)(tw % KW);
-    const int rb = (int)(tw / KW);
+    const long long rt = gid >> 6;
+    const int t = (int)(rt % (KW * kStepsPerWord));
+    const int rb = (int)(rt / (KW * kStepsPerWord));
     const int row = rb * kRowBlock + (L & 31);
-    const int groups = K / kGroup;
-    uint32_t word = 0;
+    const int g = 2 * t + (L >> 5);
+    u32x4 codes = {0u, 0u, 0u, 0u};
+    uint32_t byte = 0u;
+    if (row < rows && g < K / kGroup) {
+        const uint16_t* src = x + (size_t)row * ld + (size_t)g * kGroup;
+        u32x4 v[4];
 #pragma unroll
-    for (int b = 0; b < kStepsPerWord; ++b) {
-        const int t = w * kStepsPerWord + b;
-        if (t >= KS) {
-            word |= 127u << (8 * b);
-            continue;
-        }
-        const int g = 2 * t + (L >> 5);
-        u32x4 codes = {0u, 0u, 0u, 0u};
-        uint32_t byte = 127u;
-        if (row < rows && g < groups) {
-            const uint16_t* src = x + (size_t)row * ld + (size_t)g * kGroup;
-            u32x4 v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = load16(src + 8 * i);
-            byte = quant_group32(v, codes);
-        }
-        *(u32x4*)(packed + ((size_t)(rb * KS + t) * 64 + L) * 16) = codes;
-        word |= byte << (8 * b);
+        for (int i = 0; i < 4; ++i) v[i] = load16(src + 8 * i);
+        byte = quant_group32(v, codes);
     }
-    *(uint32_t*)(packed + code_bytes + ((size_t)(rb * KW + w) * 64 + L) * 4) = word;
+    // steps past KS exist only as padding bytes of the last scale word
+    if (t < KS) *(u32x4*)(packed + ((size_t)(rb * KS + t) * 64 + L) * 16) = codes;
+    packed[code_bytes + ((size_t)(rb * KW + t / kStepsPerWord) * 64 + L) * 4 + t % kStepsPerWord] = (uint8_t)byte;
 }
 
 // Packed layout -> natural layouts.  One lane per (rb, t, L) tile slot.
@@ -128,7 +118,7 @@ hipError_t launch_quant_natural(const uint16_t* x, int rows, int K, int ld, uint
 
 hipError_t launch_pack(const uint16_t* x, int rows, int K, int ld, uint8_t* packed, hipStream_t s) {
     const OperandGeom g = operand_geom(rows, K);
-    const long long total = (long long)g.RB * g.KW * 64;
+    const long long total = (long long)g.RB * g.KW * kStepsPerWord * 64;
     const long long blocks = (total + 255) / 256;
     hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, K, ld, packed, g.RB, g.KS,
                        g.KW, g.code_bytes);

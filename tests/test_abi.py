@@ -122,7 +122,7 @@ def test_plans_for_workloads():
         assert p["mb"] in (1, 2) and p["nb"] in (1, 2) and p["wn"] in (1, 2, 4)
         assert p["wk"] in (1, 2, 4, 8) and p["wn"] * p["wk"] <= 16 and p["splits"] >= 1
         ws = B.mx_gemm_workspace_bytes(w.M, w.N, w.K)
-        if p["splits"] == 1:
+        if p["splits"] == 1 and not p["preq"]:
             assert ws == 0
         else:
             assert ws > 0
@@ -136,13 +136,13 @@ def test_plan_model_for_other_shapes():
 
 
 def test_explicit_plan_rejections():
-    bad = [dict(mb=3, nb=1, wn=1, wk=1, splits=1),      # no such tile
-           dict(mb=1, nb=1, wn=1, wk=3, splits=1),      # no such wave count
-           dict(mb=1, nb=1, wn=4, wk=8, splits=4),      # more than 16 waves
-           dict(mb=1, nb=1, wn=1, wk=4, splits=0),
-           dict(mb=1, nb=1, wn=1, wk=4, splits=1000),   # more splits than K steps
-           dict(mb=1, nb=1, wn=1, wk=8, splits=1),      # 14 K steps per wave > register budget
-           dict(mb=2, nb=1, wn=1, wk=8, splits=2)]      # activation slice over the LDS budget
+    bad = [dict(mb=3, nb=1, wn=1, wk=1, splits=1, preq=0),      # no such tile
+           dict(mb=1, nb=1, wn=1, wk=3, splits=1, preq=1),      # no such wave count
+           dict(mb=1, nb=1, wn=4, wk=8, splits=4, preq=0),      # more than 16 waves
+           dict(mb=1, nb=1, wn=1, wk=4, splits=0, preq=1),
+           dict(mb=1, nb=1, wn=1, wk=4, splits=1000, preq=1),   # more splits than K steps
+           dict(mb=1, nb=1, wn=1, wk=8, splits=1, preq=1),      # 14 K steps per wave > register budget
+           dict(mb=2, nb=1, wn=1, wk=8, splits=2, preq=0)]      # activation slice over the LDS budget
     for p in bad:
         with pytest.raises(B.MxError) as e:
             B.mx_gemm_workspace_bytes(16, 2112, 7168, p)
