@@ -40,7 +40,7 @@ struct TableEntry {
 const TableEntry kTable[] = {
     {4, 2880, 512, {1, 1, 1, 4, 1, 0}},
     {32, 4096, 512, {1, 1, 1, 4, 1, 0}},
-    {16, 2112, 7168, {1, 1, 1, 8, 2, 1}},
+    {16, 2112, 7168, {1, 1, 2, 4, 7, 0}},
     {64, 7168, 2048, {1, 1, 2, 4, 1, 1}},
     {256, 3072, 1536, {1, 1, 1, 4, 1, 1}},
 };

@@ -41,6 +41,14 @@ __device__ __forceinline__ int xcd_linear(int i, int G) {
     return x * q + (x < r ? x : r) + i / 8;
 }
 
+// LDS of the WK-reduction buffer and of the staged bf16 output tile.
+__host__ __device__ constexpr size_t gemm_red_bytes(int wn, int wk, int mb, int nb) {
+    return wk > 1 ? (size_t)wn * wk * mb * nb * 16 * 64 * 4 : 0;
+}
+__host__ __device__ constexpr size_t gemm_stage_bytes(int wn, int mb, int nb) {
+    return (size_t)mb * kRowBlock * (nb * wn * kRowBlock + 8) * 2;
+}
+
 // 4 consecutive bf16 outputs (n0..n0+3) of row m, masked at N.
 __device__ __forceinline__ void store_bf16x4(const GemmParams& p, int m, int n0, const float (&v)[4]) {
     uint16_t* dst = p.C + (size_t)m * p.ldc + n0;
@@ -88,9 +96,49 @@ gemm_kernel(GemmParams p) {
     // the same straight-line code for every wave.
     constexpr uint32_t kOutOfRange = 0x80000000u;
 
-    // ---- 1. weight (and pre-quantised activation) fragments, all in flight.
+    // ---- 1. operand loads.  With FUSED, the bf16 activation loads of the
+    // first quantisation pass go out first: loads complete in issue order,
+    // so the quantisation can start while the weight is still in flight.
+    // Activation slot u = (mb * T + tl) * 64 + lane of the workgroup's LDS
+    // operand holds row 32 (mb0 + mb) + lane % 32, group 2 (tb + tl) +
+    // lane / 32 (MFMA lane order).  Rows past M read as zero through the
+    // buffer bound and quantise to zero codes with scale byte 0; a group past
+    // K (K % 64 == 32) is zeroed explicitly.
+    constexpr int QREG = 2;   // activation slots per thread whose loads are issued together
+    const int slots = MBLK * T * 64;
+    const int G = p.K / kGroup;
+    u32x4 x[QREG][4];
+    auto load_slots = [&](int u0) {
+        const Rsrc rx_ = make_rsrc(p.A, p.a_bytes);
+#pragma unroll
+        for (int q = 0; q < QREG; ++q) {
+            const int u = u0 + q * NT + tid;
+            const int lane = u & 63, mtl = u >> 6;
+            const int row = (mb0 + mtl / T) * kRowBlock + (lane & 31);
+            const int g = 2 * (tb + mtl % T) + (lane >> 5);
+            const bool live = u < slots && g < G;
+            const uint32_t off = live ? (uint32_t)row * (uint32_t)p.lda * 2u + (uint32_t)g * 64u : kOutOfRange;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) x[q][c] = bload16(rx_, off + 16u * c, 0u);
+        }
+    };
+    auto quant_slots = [&](int u0) {
+#pragma unroll
+        for (int q = 0; q < QREG; ++q) {
+            const int u = u0 + q * NT + tid;
+            if (u < slots) {
+                u32x4 codes;
+                const uint32_t byte = quant_group32(x[q], codes);
+                *(u32x4*)(lds + 16 * u) = codes;
+                lds[16 * slots + u] = (uint8_t)byte;
+            }
+        }
+    };
+    if constexpr (FUSED) load_slots(0);
+
+    // Weight (and pre-quantised activation) fragments, all in flight.
     // Buffer loads: the wave-uniform part of every offset is a scalar, the
-    // lane part one VGPR; blocks past the operand's end read as zero.
+    // lane part one VGPR; steps past the wave's share read as zero.
     const Rsrc rb_ = make_rsrc(p.bp, p.bp_bytes);
     const Rsrc ra_ = make_rsrc(p.aop, p.aop_bytes);
     u32x4 bfrag[KR][NBLK];
@@ -119,41 +167,12 @@ gemm_kernel(GemmParams p) {
         }
     }
 
-    // ---- 2. (FUSED) quantise the activation slice into LDS, MFMA lane order:
-    // slot u = (mb * T + tl) * 64 + lane holds row 32 (mb0 + mb) + lane % 32,
-    // group 2 (tb + tl) + lane / 32; codes at 16 u, scale byte at
-    // 16 MBLK T 64 + u.  Rows past M read as zero through the buffer bound
-    // and quantise to zero codes with scale byte 0; a group past K (K % 64
-    // == 32) is zeroed explicitly.
+    // ---- 2. (FUSED) quantise the activation slice into LDS.
     if constexpr (FUSED) {
-        const Rsrc rx_ = make_rsrc(p.A, p.a_bytes);
-        const int slots = MBLK * T * 64;
-        const int G = p.K / kGroup;
-        constexpr int QREG = 2;   // slots per thread whose loads are issued together
-        for (int u0 = 0; u0 < slots; u0 += NT * QREG) {
-            u32x4 x[QREG][4];
-            bool live[QREG];
-#pragma unroll
-            for (int q = 0; q < QREG; ++q) {
-                const int u = u0 + q * NT + tid;
-                const int lane = u & 63, mtl = u >> 6;
-                const int row = (mb0 + mtl / T) * kRowBlock + (lane & 31);
-                const int g = 2 * (tb + mtl % T) + (lane >> 5);
-                live[q] = u < slots && g < G;
-                const uint32_t off = live[q] ? (uint32_t)row * (uint32_t)p.lda * 2u + (uint32_t)g * 64u : p.a_bytes;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) x[q][c] = bload16(rx_, off + 16u * c, 0u);
-            }
-#pragma unroll
-            for (int q = 0; q < QREG; ++q) {
-                const int u = u0 + q * NT + tid;
-                if (u < slots) {
-                    u32x4 codes;
-                    const uint32_t byte = quant_group32(x[q], codes);
-                    *(u32x4*)(lds + 16 * u) = codes;
-                    lds[16 * slots + u] = (uint8_t)byte;
-                }
-            }
+        quant_slots(0);
+        for (int u0 = NT * QREG; u0 < slots; u0 += NT * QREG) {
+            load_slots(u0);
+            quant_slots(u0);
         }
         __syncthreads();
     }
@@ -208,9 +227,14 @@ gemm_kernel(GemmParams p) {
     const int m_lane = L & 31;
     const int n_lane = 4 * (L >> 5);
     constexpr int E = MBLK * NBLK * 16;       // accumulator floats per lane
+    constexpr int TR = MBLK * kRowBlock;      // rows of the workgroup tile
+    constexpr int TC = NBLK * WN * kRowBlock; // columns of the workgroup tile
+    constexpr int SROW = TC + 8;              // bf16 per staged row (16-byte pad)
     float* red = (float*)lds;
+    uint16_t* stage = (uint16_t*)(lds + gemm_red_bytes(WN, WK, MBLK, NBLK));
+    const bool partial = p.splits > 1;
+    if constexpr (FUSED || WK > 1) __syncthreads();   // every wave is done with the activation operand
     if constexpr (WK > 1) {
-        if constexpr (FUSED) __syncthreads();   // every wave is done with the activation operand
 #pragma unroll
         for (int i = 0; i < MBLK; ++i)
 #pragma unroll
@@ -219,17 +243,24 @@ gemm_kernel(GemmParams p) {
                 for (int e = 0; e < 16; ++e) red[((wave * E) + (i * NBLK + j) * 16 + e) * 64 + L] = acc[i][j][e];
         __syncthreads();
     }
-    // groups of 4 consecutive n per (i, j, r); the WK waves of column wn share them
+    // groups of 4 consecutive n per (i, j, r); the WK waves of column wn share
+    // them.  Split-K partials go straight to the workspace as fp32; bf16
+    // results are staged in LDS as a row-major tile first.
     auto emit = [&](int i, int j, int r, const float (&v)[4]) {
-        const int m = (mb0 + i) * kRowBlock + m_lane;
-        const int nb = nb0 + j;
-        const int n0 = nb * kRowBlock + 8 * r + n_lane;
-        if (m >= p.M || nb >= p.RBn) return;
-        if (p.splits > 1) {
+        if (partial) {
+            const int m = (mb0 + i) * kRowBlock + m_lane;
+            const int nb = nb0 + j;
+            const int n0 = nb * kRowBlock + 8 * r + n_lane;
+            if (m >= p.M || nb >= p.RBn) return;
             const f32x4 pv = {v[0], v[1], v[2], v[3]};
             *(f32x4*)(p.partial + ((size_t)split * p.M + m) * p.ldp + n0) = pv;
         } else {
-            store_bf16x4(p, m, n0, v);
+            const int row = i * kRowBlock + m_lane;
+            const int col = (wn * NBLK + j) * kRowBlock + 8 * r + n_lane;
+            uint2 w;
+            w.x = pack_bf16x2(v[0], v[1]);
+            w.y = pack_bf16x2(v[2], v[3]);
+            *(uint2*)(stage + row * SROW + col) = w;
         }
     };
     if constexpr (WK == 1) {
@@ -258,6 +289,28 @@ gemm_kernel(GemmParams p) {
                 v[q] = s;
             }
             emit(i, j, r, v);
+        }
+    }
+    if (partial) return;
+    __syncthreads();
+    // the staged tile leaves in 16-byte row chunks: consecutive lanes write
+    // consecutive bytes of a row of C
+    const int m_base = mb0 * kRowBlock;
+    const int n_base = nt * WN * NBLK * kRowBlock;
+    const bool vec16 = ((uintptr_t)p.C % 16 == 0) && (p.ldc % 8 == 0);
+    for (int c = tid; c < TR * TC / 8; c += NT) {
+        const int row = c / (TC / 8), c8 = c % (TC / 8);
+        const int m = m_base + row, n = n_base + 8 * c8;
+        if (m >= p.M || n >= p.N) continue;
+        const u32x4 v = *(const u32x4*)(stage + row * SROW + 8 * c8);
+        uint16_t* dst = p.C + (size_t)m * p.ldc + n;
+        if (vec16 && n + 7 < p.N) {
+            *(u32x4*)dst = v;
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (n + q < p.N) dst[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
         }
     }
 }
@@ -352,8 +405,8 @@ static GemmFn find_kernel(const Plan& plan, int kr) {
 
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
     const size_t a_op = plan.preq ? 0 : (size_t)plan.mb * steps_per_split * 64 * 17;
-    const size_t red = plan.wk > 1 ? (size_t)plan.wn * plan.wk * plan.mb * plan.nb * 16 * 64 * 4 : 0;
-    return a_op > red ? a_op : red;
+    const size_t out = gemm_red_bytes(plan.wn, plan.wk, plan.mb, plan.nb) + gemm_stage_bytes(plan.wn, plan.mb, plan.nb);
+    return a_op > out ? a_op : out;
 }
 
 bool gemm_plan_supported(const Plan& plan) {

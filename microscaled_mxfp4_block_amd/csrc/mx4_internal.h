@@ -12,8 +12,8 @@ namespace mx4 {
 // Largest number of K steps one wave holds in registers (its whole share of
 // a split); the planner splits K further when a shape needs more.
 constexpr int kStepsPerWaveMax = 8;
-// Largest LDS block the planner gives a workgroup.
-constexpr size_t kLdsBudget = 64 * 1024;
+// Largest LDS block the planner gives a workgroup (gfx950: 160 KiB per CU).
+constexpr size_t kLdsBudget = 160 * 1024;
 
 // Arguments of the GEMM and reduction kernels.  The MFMA's first operand is
 // the weight tile (rows = N), the second the activation tile (rows = M), so

@@ -142,7 +142,7 @@ def test_explicit_plan_rejections():
            dict(mb=1, nb=1, wn=1, wk=4, splits=0, preq=1),
            dict(mb=1, nb=1, wn=1, wk=4, splits=1000, preq=1),   # more splits than K steps
            dict(mb=1, nb=1, wn=1, wk=8, splits=1, preq=1),      # 14 K steps per wave > register budget
-           dict(mb=2, nb=1, wn=1, wk=8, splits=2, preq=0)]      # activation slice over the LDS budget
+           dict(mb=2, nb=1, wn=1, wk=16, splits=1, preq=0)]     # activation slice over the 160 KiB LDS
     for p in bad:
         with pytest.raises(B.MxError) as e:
             B.mx_gemm_workspace_bytes(16, 2112, 7168, p)
@@ -154,3 +154,15 @@ def test_binding_without_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(ImportError):
         B.lib()
+
+
+def test_fast_call_extension_validates_without_gpu():
+    ext = B.ext()
+    # same validation path as the C entry points: no HIP call is reached
+    assert ext.gemm(FAKE, 0, 512, 512, FAKE, 64, FAKE, 64, 0, 0, 0) == B.MX_EINVAL
+    assert ext.gemm(FAKE, 4, 512, 512, None, 64, FAKE, 64, 0, 0, 0) == B.MX_EALIGN
+    assert ext.gemm_with_plan(FAKE, 4, 512, 512, FAKE, 64, FAKE, 64, 0, 0, 3, 1, 1, 1, 1, 0, 0) == B.MX_EPLAN
+    with pytest.raises(TypeError):
+        ext.gemm(1, 2, 3)
+    with pytest.raises(OverflowError):
+        ext.gemm(FAKE, 1 << 40, 512, 512, FAKE, 64, FAKE, 64, 0, 0, 0)
