@@ -102,7 +102,8 @@ int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host);
  *              initialisation needed, scratch after the call.  Calls that
  *              overlap in time (other streams) need separate workspaces.
  * Launches per call: 1 (A quantised inside the GEMM), +1 for the quantisation
- * kernel when the plan has preq, +1 for the split-K reduction when splits > 1.
+ * kernel when the plan's amode is MX_AMODE_PREQUANT, +1 for the split-K
+ * reduction when splits > 1.
  * The split-K reduction sums the partials in split order: results do not
  * depend on timing. */
 int mx_gemm(const void* A_dev, int M, int K, int lda,
@@ -117,12 +118,20 @@ int mx_gemm(const void* A_dev, int M, int K, int lda,
 typedef struct mx_plan {
     int mb;          /* 32-row blocks of M per wave (1 or 2) */
     int nb;          /* 32-column blocks of N per wave (1 or 2) */
-    int wn;          /* waves along N per workgroup (1, 2 or 4) */
+    int wn;          /* waves along N per workgroup (1 or 2) */
     int wk;          /* waves along K per workgroup (1, 2, 4, 8 or 16; wn*wk <= 16) */
     int splits;      /* workgroups along K; > 1 adds a reduction kernel */
-    int preq;        /* 1: quantise A in a first kernel into the workspace;
-                        0: each GEMM workgroup quantises its slice of A itself */
+    int amode;       /* where A is quantised: one of MX_AMODE_* */
 } mx_plan;
+
+/* Activation modes of a plan. */
+enum {
+    MX_AMODE_LDS = 0,       /* each GEMM workgroup quantises its slice of A into
+                               LDS, shared by its waves */
+    MX_AMODE_PREQUANT = 1,  /* a first kernel quantises A into the workspace */
+    MX_AMODE_DIRECT = 2     /* each wave quantises the A fragments it consumes
+                               in registers (no LDS, no barrier) */
+};
 
 /* The plan mx_gemm uses for (M, N, K) (host only). */
 int mx_gemm_plan(int M, int N, int K, mx_plan* plan_host);

@@ -21,6 +21,10 @@ MX_EALIGN = -2
 MX_ESPACE = -3
 MX_EHIP = -4
 MX_EPLAN = -5
+# activation modes of a plan (where A is quantised)
+MX_AMODE_LDS = 0
+MX_AMODE_PREQUANT = 1
+MX_AMODE_DIRECT = 2
 
 EXPORTS = [
     "mx_strerror", "mx_packed_weight_bytes", "mx_pack_weight", "mx_unpack_weight",
@@ -31,7 +35,7 @@ EXPORTS = [
 
 class MxPlan(ctypes.Structure):
     _fields_ = [("mb", ctypes.c_int), ("nb", ctypes.c_int), ("wn", ctypes.c_int), ("wk", ctypes.c_int),
-                ("splits", ctypes.c_int), ("preq", ctypes.c_int)]
+                ("splits", ctypes.c_int), ("amode", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -190,6 +194,6 @@ def mx_gemm(A: torch.Tensor, packed: torch.Tensor, N: int, C: Optional[torch.Ten
     else:
         rc = ext().gemm_with_plan(A.data_ptr(), M, K, lda, packed.data_ptr(), N, C.data_ptr(), ldc,
                                   workspace.data_ptr(), workspace.numel(), plan["mb"], plan["nb"], plan["wn"],
-                                  plan["wk"], plan["splits"], plan["preq"], s)
+                                  plan["wk"], plan["splits"], plan["amode"], s)
     _check(rc, "mx_gemm")
     return C

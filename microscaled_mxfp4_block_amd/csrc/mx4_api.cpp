@@ -14,6 +14,11 @@
 using mx4::GemmParams;
 using mx4::OperandGeom;
 using mx4::Plan;
+using mx4::kAmDirect;
+using mx4::kAmLds;
+using mx4::kAmPrequant;
+static_assert(kAmLds == MX_AMODE_LDS && kAmPrequant == MX_AMODE_PREQUANT && kAmDirect == MX_AMODE_DIRECT,
+              "activation modes of the C ABI and the kernels differ");
 
 namespace {
 
@@ -35,7 +40,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_EHIP; }
 // in model_plan().
 struct TableEntry {
     int M, N, K;
-    Plan plan;   // mb, nb, wn, wk, splits, preq
+    Plan plan;   // mb, nb, wn, wk, splits, amode
 };
 const TableEntry kTable[] = {
     {4, 2880, 512, {1, 1, 1, 4, 1, 0}},
@@ -70,12 +75,16 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     l.steps_per_split = (gb.KS + plan.splits - 1) / plan.splits;
     l.splits = (gb.KS + l.steps_per_split - 1) / l.steps_per_split;  // every split non-empty
     if ((l.steps_per_split + plan.wk - 1) / plan.wk > mx4::kStepsPerWaveMax) return MX_EPLAN;
+    // kAmDirect holds the raw bf16 of every fragment of the wave (16 VGPRs per
+    // K step and m block) while the weight loads are in flight: at most 128.
+    if (plan.amode == kAmDirect && plan.mb * mx4::gemm_kr_for((l.steps_per_split + plan.wk - 1) / plan.wk) > 8)
+        return MX_EPLAN;
     if (mx4::gemm_lds_bytes(plan, l.steps_per_split) > mx4::kLdsBudget) return MX_EPLAN;
     l.mtiles = (ga.RB + plan.mb - 1) / plan.mb;
     l.ntiles = (gb.RB + plan.nb * plan.wn - 1) / (plan.nb * plan.wn);
     if ((long long)l.mtiles * l.ntiles * l.splits >= (1LL << 31)) return MX_EINVAL;
     l.aop_offset = 0;
-    l.aop_bytes = plan.preq ? round_up(ga.total_bytes, 256) : 0;
+    l.aop_bytes = plan.amode == kAmPrequant ? round_up(ga.total_bytes, 256) : 0;
     l.partial_offset = l.aop_bytes;
     l.partial_bytes = l.splits > 1 ? round_up((size_t)l.splits * M * gb.RB * mx4::kRowBlock * sizeof(float), 256) : 0;
     l.total = l.aop_bytes + l.partial_bytes;
@@ -94,8 +103,8 @@ Plan model_plan(int M, int N, int K) {
     const OperandGeom ga = mx4::operand_geom(M, K);
     const OperandGeom gb = mx4::operand_geom(N, K);
     Plan p;
-    p.preq = (ga.RB > 1 || gb.KS > 16) ? 1 : 0;
-    p.mb = (p.preq && ga.RB >= 2) ? 2 : 1;
+    p.amode = (ga.RB > 1 || gb.KS > 16) ? kAmPrequant : kAmLds;
+    p.mb = (p.amode == kAmPrequant && ga.RB >= 2) ? 2 : 1;
     p.nb = 1;
     p.wn = 1;
     p.wk = pow2_floor(gb.KS < 8 ? gb.KS : 8);
@@ -142,7 +151,7 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     p.A = (const uint16_t*)A;
     p.lda = lda;
     p.a_bytes = (uint32_t)((size_t)M * lda * 2);
-    p.aop = plan.preq ? wsb + lay.aop_offset : nullptr;
+    p.aop = plan.amode == kAmPrequant ? wsb + lay.aop_offset : nullptr;
     p.aop_bytes = (uint32_t)ga.total_bytes;
     p.a_code_bytes = (uint32_t)ga.code_bytes;
     p.bp = (const uint8_t*)packed;
@@ -165,7 +174,7 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     p.partial = lay.splits > 1 ? (float*)(wsb + lay.partial_offset) : nullptr;
     p.ldp = gb.RB * mx4::kRowBlock;
 
-    if (plan.preq) {
+    if (plan.amode == kAmPrequant) {
         rc = hip_status(mx4::launch_pack((const uint16_t*)A, M, K, lda, wsb + lay.aop_offset, s));
         if (rc) return rc;
     }
@@ -242,7 +251,7 @@ int mx_gemm_plan(int M, int N, int K, mx_plan* plan_host) {
     plan_host->wn = p.wn;
     plan_host->wk = p.wk;
     plan_host->splits = lay.splits;
-    plan_host->preq = p.preq;
+    plan_host->amode = p.amode;
     return MX_OK;
 }
 
@@ -252,7 +261,7 @@ int mx_gemm_plan_workspace_bytes(const mx_plan* plan_host, int M, int N, int K, 
     if (rc) return rc;
     rc = check_operand_shape(N, K);
     if (rc) return rc;
-    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wn, plan_host->wk, plan_host->splits, plan_host->preq};
+    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wn, plan_host->wk, plan_host->splits, plan_host->amode};
     Layout lay;
     rc = plan_layout(p, M, N, K, &lay);
     if (rc) return rc;
@@ -270,7 +279,7 @@ int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host) {
 int mx_gemm_with_plan(const void* A_dev, int M, int K, int lda, const void* packed_dev, int N, void* C_dev, int ldc,
                       void* ws_dev, size_t ws_bytes, const mx_plan* plan_host, void* stream) {
     if (!plan_host) return MX_EALIGN;
-    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wn, plan_host->wk, plan_host->splits, plan_host->preq};
+    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wn, plan_host->wk, plan_host->splits, plan_host->amode};
     return gemm_impl(A_dev, M, K, lda, packed_dev, N, C_dev, ldc, ws_dev, ws_bytes, p, stream);
 }
 

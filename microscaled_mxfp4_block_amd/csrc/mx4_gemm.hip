@@ -14,15 +14,20 @@
 //   1. Every wave issues the 128-bit loads of all its weight fragments (its
 //      whole share of the split) before anything else: the weight costs one
 //      HBM round trip, read exactly once, straight into VGPRs, non-temporal.
-//   2. The activation operand:
-//      FUSED   the workgroup quantises its activation slice (its m rows x its
-//              K split) itself into LDS, in MFMA lane order: one lane per
-//              32-element group, per-lane amax, scale byte by the bit rule,
-//              e2m1 codes by the gfx950 fp4 convert;
-//      !FUSED  a first kernel (pack_kernel) quantised A into the packed
-//              operand layout in the workspace; each wave loads its
-//              fragments from there (L2-resident) together with step 1.
-//   3. K loop: MFMAs on registers (and 16-byte LDS reads when FUSED).
+//   2. The activation operand, by the plan's activation mode AM:
+//      kAmLds     the workgroup quantises its activation slice (its m rows x
+//                 its K split) itself into LDS, in MFMA lane order: one lane
+//                 per 32-element group, per-lane amax, scale byte by the bit
+//                 rule, e2m1 codes by the gfx950 fp4 convert; the WN waves
+//                 of the workgroup share it;
+//      kAmPrequant a first kernel (pack_kernel) quantised A into the packed
+//                 operand layout in the workspace; each wave loads its
+//                 fragments from there (L2-resident) together with step 1;
+//      kAmDirect  every lane loads the 32 bf16 of exactly the fragment it
+//                 feeds to the MFMA (one row, one 32-element group) and
+//                 quantises it in registers: no LDS, no barrier; waves with
+//                 the same m rows and K steps each quantise them.
+//   3. K loop: MFMAs on registers (and 16-byte LDS reads with kAmLds).
 //   4. The WK waves add their accumulators through LDS; the result is
 //      rounded to bf16 and stored, or, when K is split over workgroups,
 //      written as fp32 partials that reduce_kernel sums in split order
@@ -64,10 +69,13 @@ __device__ __forceinline__ void store_bf16x4(const GemmParams& p, int m, int n0,
     }
 }
 
-template <int MBLK, int NBLK, int WN, int WK, bool FUSED, int KR>
+template <int MBLK, int NBLK, int WN, int WK, int AM, int KR>
 __global__ void __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(2)))
 gemm_kernel(GemmParams p) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    constexpr bool FUSED = AM == kAmLds;
+    constexpr bool DIRECT = AM == kAmDirect;
+    constexpr bool PREQ = AM == kAmPrequant;
     constexpr int NT = 64 * WN * WK;
     const int tid = threadIdx.x;
     // wave-uniform values in SGPRs: weight and operand base addresses then
@@ -136,6 +144,27 @@ gemm_kernel(GemmParams p) {
     };
     if constexpr (FUSED) load_slots(0);
 
+    // kAmDirect: lane L's fragment of step s, m block i is row
+    // 32 (mb0 + i) + L % 32, group 2 (wb + s) + L / 32; padding steps and a
+    // group past K read zeros (zero codes, scale byte 0), rows past M read
+    // zeros through the buffer bound.
+    u32x4 xa[DIRECT ? KR : 1][MBLK][4];
+    if constexpr (DIRECT) {
+        const Rsrc rx_ = make_rsrc(p.A, p.a_bytes);
+#pragma unroll
+        for (int s = 0; s < KR; ++s) {
+            const int g = 2 * (wb + s) + (L >> 5);
+            const bool live = s < nsteps && g < G;
+#pragma unroll
+            for (int i = 0; i < MBLK; ++i) {
+                const int row = (mb0 + i) * kRowBlock + (L & 31);
+                const uint32_t off = live ? (uint32_t)row * (uint32_t)p.lda * 2u + (uint32_t)g * 64u : kOutOfRange;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) xa[s][i][c] = bload16(rx_, off + 16u * c, 0u);
+            }
+        }
+    }
+
     // Weight (and pre-quantised activation) fragments, all in flight.
     // Buffer loads: the wave-uniform part of every offset is a scalar, the
     // lane part one VGPR; steps past the wave's share read as zero.
@@ -143,8 +172,8 @@ gemm_kernel(GemmParams p) {
     const Rsrc ra_ = make_rsrc(p.aop, p.aop_bytes);
     u32x4 bfrag[KR][NBLK];
     uint32_t bscale[KR][NBLK];
-    u32x4 afrag[FUSED ? 1 : KR][MBLK];
-    uint32_t ascale[FUSED ? 1 : KR][MBLK];
+    u32x4 afrag[PREQ ? KR : 1][MBLK];
+    uint32_t ascale[PREQ ? KR : 1][MBLK];
 #pragma unroll
     for (int s = 0; s < KR; ++s) {
         const bool on = s < nsteps;
@@ -157,7 +186,7 @@ gemm_kernel(GemmParams p) {
             bfrag[s][j] = bload16<kNonTemporal>(rb_, vcode, (uint32_t)(nb * p.KS + t) * 1024u);
             bscale[s][j] = bload4(rb_, vscale, p.b_code_bytes + (uint32_t)(nb * p.KW + (t >> 2)) * 256u);
         }
-        if constexpr (!FUSED) {
+        if constexpr (PREQ) {
 #pragma unroll
             for (int i = 0; i < MBLK; ++i) {
                 const int mb = min(mb0 + i, p.RBm - 1);   // clamped blocks are never stored
@@ -199,6 +228,8 @@ gemm_kernel(GemmParams p) {
                 const u32x4 a = *(const u32x4*)(lds + 16 * u);
                 af[i] = on ? a : u32x4{0u, 0u, 0u, 0u};
                 as[i] = lds[16 * MBLK * T * 64 + u];
+            } else if constexpr (DIRECT) {
+                as[i] = quant_group32(xa[s][i], af[i]);
             } else {
                 af[i] = afrag[s][i];
                 as[i] = ascale[s][i] >> sh;
@@ -318,7 +349,8 @@ gemm_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------
 // Instantiation table.  This file is compiled once per K-step budget KR
 // (-DMX4_KR=1, 2, 4 or 8); each object instantiates MBLK, NBLK in {1, 2},
-// WN in {1, 2}, WK in {1, 2, 4, 8, 16} (at most 16 waves), FUSED in {0, 1}.
+// WN in {1, 2}, WK in {1, 2, 4, 8, 16} (at most 16 waves) and the three
+// activation modes.
 
 #ifndef MX4_KR
 #error "compile with -DMX4_KR=<K steps per wave>"
@@ -326,41 +358,46 @@ gemm_kernel(GemmParams p) {
 
 typedef void (*GemmFn)(GemmParams);
 
-template <int MBLK, int NBLK, int WN, bool FUSED>
+template <int MBLK, int NBLK, int WN, int AM>
 static GemmFn pick_wk(int wk) {
     constexpr int KR = MX4_KR;
     switch (wk) {
-        case 1: return gemm_kernel<MBLK, NBLK, WN, 1, FUSED, KR>;
-        case 2: return gemm_kernel<MBLK, NBLK, WN, 2, FUSED, KR>;
-        case 4: return gemm_kernel<MBLK, NBLK, WN, 4, FUSED, KR>;
-        case 8: return gemm_kernel<MBLK, NBLK, WN, 8, FUSED, KR>;
-        case 16: return WN == 1 ? gemm_kernel<MBLK, NBLK, WN, (WN == 1 ? 16 : 8), FUSED, KR> : nullptr;
+        case 1: return gemm_kernel<MBLK, NBLK, WN, 1, AM, KR>;
+        case 2: return gemm_kernel<MBLK, NBLK, WN, 2, AM, KR>;
+        case 4: return gemm_kernel<MBLK, NBLK, WN, 4, AM, KR>;
+        case 8: return gemm_kernel<MBLK, NBLK, WN, 8, AM, KR>;
+        case 16: return WN == 1 ? gemm_kernel<MBLK, NBLK, WN, (WN == 1 ? 16 : 8), AM, KR> : nullptr;
         default: return nullptr;
     }
 }
 
-template <int MBLK, int NBLK, bool FUSED>
+template <int MBLK, int NBLK, int AM>
 static GemmFn pick_wn(int wn, int wk) {
     switch (wn) {
-        case 1: return pick_wk<MBLK, NBLK, 1, FUSED>(wk);
-        case 2: return pick_wk<MBLK, NBLK, 2, FUSED>(wk);
+        case 1: return pick_wk<MBLK, NBLK, 1, AM>(wk);
+        case 2: return pick_wk<MBLK, NBLK, 2, AM>(wk);
         default: return nullptr;
     }
 }
 
-template <bool FUSED>
+template <int AM>
 static GemmFn pick_tile(const Plan& plan) {
-    if (plan.mb == 1 && plan.nb == 1) return pick_wn<1, 1, FUSED>(plan.wn, plan.wk);
-    if (plan.mb == 1 && plan.nb == 2) return pick_wn<1, 2, FUSED>(plan.wn, plan.wk);
-    if (plan.mb == 2 && plan.nb == 1) return pick_wn<2, 1, FUSED>(plan.wn, plan.wk);
-    if (plan.mb == 2 && plan.nb == 2) return pick_wn<2, 2, FUSED>(plan.wn, plan.wk);
+    if (plan.mb == 1 && plan.nb == 1) return pick_wn<1, 1, AM>(plan.wn, plan.wk);
+    if (plan.mb == 1 && plan.nb == 2) return pick_wn<1, 2, AM>(plan.wn, plan.wk);
+    if (plan.mb == 2 && plan.nb == 1) return pick_wn<2, 1, AM>(plan.wn, plan.wk);
+    if (plan.mb == 2 && plan.nb == 2) return pick_wn<2, 2, AM>(plan.wn, plan.wk);
     return nullptr;
 }
 
 #define MX4_CAT2(a, b) a##b
 #define MX4_CAT(a, b) MX4_CAT2(a, b)
 GemmFn MX4_CAT(find_gemm_kr, MX4_KR)(const Plan& plan) {
-    return plan.preq ? pick_tile<false>(plan) : pick_tile<true>(plan);
+    switch (plan.amode) {
+        case kAmLds: return pick_tile<kAmLds>(plan);
+        case kAmPrequant: return pick_tile<kAmPrequant>(plan);
+        case kAmDirect: return pick_tile<kAmDirect>(plan);
+        default: return nullptr;
+    }
 }
 
 #if MX4_KR == 1
@@ -404,7 +441,7 @@ static GemmFn find_kernel(const Plan& plan, int kr) {
 }
 
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
-    const size_t a_op = plan.preq ? 0 : (size_t)plan.mb * steps_per_split * 64 * 17;
+    const size_t a_op = plan.amode == kAmLds ? (size_t)plan.mb * steps_per_split * 64 * 17 : 0;
     const size_t out = gemm_red_bytes(plan.wn, plan.wk, plan.mb, plan.nb) + gemm_stage_bytes(plan.wn, plan.mb, plan.nb);
     return a_op > out ? a_op : out;
 }

@@ -42,13 +42,17 @@ struct GemmParams {
 };
 
 // mb: 32-row M blocks per wave; nb: 32-row N blocks per wave; wn x wk waves
-// per workgroup (wn along N, wk along K); splits along K; preq: quantise A
-// in a separate first kernel instead of inside the GEMM.
+// per workgroup (wn along N, wk along K); splits along K; amode: where the
+// activation is quantised (kAm*, the same values as the public MX_AMODE_*).
 struct Plan {
-    int mb, nb, wn, wk, splits, preq;
+    int mb, nb, wn, wk, splits, amode;
 };
+constexpr int kAmLds = 0;        // by the workgroup, into LDS
+constexpr int kAmPrequant = 1;   // by pack_kernel, into the workspace
+constexpr int kAmDirect = 2;     // by each wave, in registers
 
 bool gemm_plan_supported(const Plan& p);
+int gemm_kr_for(int steps_per_wave);   // K-step budget KR of the kernel for that many steps (0: none)
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split);
 hipError_t launch_gemm(const Plan& plan, const GemmParams& p, hipStream_t s);
 hipError_t launch_reduce(const GemmParams& p, hipStream_t s);

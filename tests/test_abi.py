@@ -119,10 +119,11 @@ def test_gemm_validation():
 def test_plans_for_workloads():
     for w in WORKLOADS:
         p = B.mx_gemm_plan(w.M, w.N, w.K)
-        assert p["mb"] in (1, 2) and p["nb"] in (1, 2) and p["wn"] in (1, 2, 4)
+        assert p["mb"] in (1, 2) and p["nb"] in (1, 2) and p["wn"] in (1, 2)
+        assert p["amode"] in (B.MX_AMODE_LDS, B.MX_AMODE_PREQUANT, B.MX_AMODE_DIRECT)
         assert p["wk"] in (1, 2, 4, 8) and p["wn"] * p["wk"] <= 16 and p["splits"] >= 1
         ws = B.mx_gemm_workspace_bytes(w.M, w.N, w.K)
-        if p["splits"] == 1 and not p["preq"]:
+        if p["splits"] == 1 and p["amode"] != B.MX_AMODE_PREQUANT:
             assert ws == 0
         else:
             assert ws > 0
@@ -136,13 +137,15 @@ def test_plan_model_for_other_shapes():
 
 
 def test_explicit_plan_rejections():
-    bad = [dict(mb=3, nb=1, wn=1, wk=1, splits=1, preq=0),      # no such tile
-           dict(mb=1, nb=1, wn=1, wk=3, splits=1, preq=1),      # no such wave count
-           dict(mb=1, nb=1, wn=4, wk=8, splits=4, preq=0),      # more than 16 waves
-           dict(mb=1, nb=1, wn=1, wk=4, splits=0, preq=1),
-           dict(mb=1, nb=1, wn=1, wk=4, splits=1000, preq=1),   # more splits than K steps
-           dict(mb=1, nb=1, wn=1, wk=8, splits=1, preq=1),      # 14 K steps per wave > register budget
-           dict(mb=2, nb=1, wn=1, wk=16, splits=1, preq=0)]     # activation slice over the 160 KiB LDS
+    bad = [dict(mb=3, nb=1, wn=1, wk=1, splits=1, amode=0),      # no such tile
+           dict(mb=1, nb=1, wn=1, wk=3, splits=1, amode=1),      # no such wave count
+           dict(mb=1, nb=1, wn=4, wk=8, splits=4, amode=0),      # no such wave count along N
+           dict(mb=1, nb=1, wn=2, wk=16, splits=4, amode=2),     # more than 16 waves
+           dict(mb=1, nb=1, wn=1, wk=4, splits=4, amode=3),      # no such activation mode
+           dict(mb=1, nb=1, wn=1, wk=4, splits=0, amode=1),
+           dict(mb=1, nb=1, wn=1, wk=4, splits=1000, amode=1),   # more splits than K steps
+           dict(mb=1, nb=1, wn=1, wk=8, splits=1, amode=1),      # 14 K steps per wave > register budget
+           dict(mb=2, nb=1, wn=1, wk=16, splits=1, amode=0)]     # activation slice over the 160 KiB LDS
     for p in bad:
         with pytest.raises(B.MxError) as e:
             B.mx_gemm_workspace_bytes(16, 2112, 7168, p)

@@ -192,23 +192,29 @@ SMALL_SHAPES = [
 ]
 
 PLANS = [
-    dict(mb=1, nb=1, wn=1, wk=1, splits=1, preq=0),
-    dict(mb=1, nb=2, wn=1, wk=4, splits=1, preq=0),
-    dict(mb=1, nb=1, wn=1, wk=8, splits=2, preq=0),
-    dict(mb=2, nb=1, wn=2, wk=2, splits=1, preq=0),
-    dict(mb=1, nb=2, wn=2, wk=4, splits=3, preq=0),
-    dict(mb=2, nb=2, wn=4, wk=4, splits=1, preq=0),
-    dict(mb=1, nb=1, wn=1, wk=16, splits=1, preq=0),
-    dict(mb=1, nb=1, wn=1, wk=1, splits=1, preq=1),
-    dict(mb=2, nb=2, wn=1, wk=1, splits=6, preq=1),
-    dict(mb=1, nb=1, wn=2, wk=8, splits=4, preq=1),
-    dict(mb=2, nb=1, wn=4, wk=2, splits=2, preq=1),
-    dict(mb=2, nb=2, wn=1, wk=16, splits=1, preq=1),
+    dict(mb=1, nb=1, wn=1, wk=1, splits=1, amode=0),
+    dict(mb=1, nb=2, wn=1, wk=4, splits=1, amode=0),
+    dict(mb=1, nb=1, wn=1, wk=8, splits=2, amode=0),
+    dict(mb=2, nb=1, wn=2, wk=2, splits=1, amode=0),
+    dict(mb=1, nb=2, wn=2, wk=4, splits=3, amode=0),
+    dict(mb=2, nb=2, wn=2, wk=4, splits=1, amode=0),
+    dict(mb=1, nb=1, wn=1, wk=16, splits=1, amode=0),
+    dict(mb=1, nb=1, wn=1, wk=1, splits=1, amode=1),
+    dict(mb=2, nb=2, wn=1, wk=1, splits=6, amode=1),
+    dict(mb=1, nb=1, wn=2, wk=8, splits=4, amode=1),
+    dict(mb=2, nb=1, wn=2, wk=2, splits=2, amode=1),
+    dict(mb=2, nb=2, wn=1, wk=16, splits=1, amode=1),
+    dict(mb=1, nb=1, wn=1, wk=1, splits=1, amode=2),
+    dict(mb=1, nb=1, wn=1, wk=4, splits=1, amode=2),
+    dict(mb=2, nb=2, wn=2, wk=2, splits=3, amode=2),
+    dict(mb=1, nb=2, wn=1, wk=16, splits=1, amode=2),
+    dict(mb=2, nb=1, wn=1, wk=8, splits=2, amode=2),
+    dict(mb=1, nb=1, wn=2, wk=4, splits=7, amode=2),
 ]
 
 
 def plan_id(p):
-    return "mb%d_nb%d_wn%d_wk%d_s%d_q%d" % (p["mb"], p["nb"], p["wn"], p["wk"], p["splits"], p["preq"])
+    return "mb%d_nb%d_wn%d_wk%d_s%d_q%d" % (p["mb"], p["nb"], p["wn"], p["wk"], p["splits"], p["amode"])
 
 
 def plan_runs(M, N, K, plan):
@@ -230,7 +236,7 @@ def test_gemm_small_shapes_auto_plan(shape):
 
 
 @pytest.mark.parametrize("plan", PLANS, ids=plan_id)
-@pytest.mark.parametrize("shape", [(5, 200, 320), (70, 300, 1536), (33, 130, 2048)],
+@pytest.mark.parametrize("shape", [(5, 200, 320), (70, 300, 1536), (33, 130, 2048), (9, 70, 352)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_gemm_explicit_plans(shape, plan):
     M, N, K = shape
