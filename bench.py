@@ -194,7 +194,7 @@ def main():
         flops = 2.0 * w.M * w.N * w.K
         rec = {
             "M": w.M, "N": w.N, "K": w.K, "plan": st.plan,
-            "launches_per_call": 1 + (st.plan["amode"] == 1) + (1 if st.plan["splits"] > 1 else 0),
+            "launches_per_call": 1 + (st.plan["amode"] == 1) + (1 if st.plan["splits"] > 1 and not st.plan["finish"] else 0),
             "us_per_call_e2e_cold": round(e2e_cold, 3), "us_per_call_e2e_hot": round(e2e_hot, 3),
             "gpu_us_cold": round(gpu_cold, 3), "gpu_us_hot": round(gpu_hot, 3),
             "algorithmic_bytes": nbytes, "gbps_cold": round(nbytes / gpu_cold / 1e3, 1),

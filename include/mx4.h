@@ -86,9 +86,12 @@ int mx_quant_act(const void* A_dev, int M, int K, int lda,
                  void* codes_dev, void* scales_dev, void* stream);
 
 /* Workspace bytes mx_gemm needs for this shape under the library's plan
- * (0 when A is quantised inside the GEMM and K is not split).  The workspace
- * holds the quantised activation operand and the fp32 partial sums of the K
- * splits. */
+ * (0 when A is quantised inside the GEMM and K is not split).  A non-empty
+ * workspace holds, in this order, 16 KiB of per-tile arrival counters, the
+ * quantised activation operand and the fp32 partial sums of the K splits.
+ * The counters must be zero before a workspace's first use (allocate it
+ * zero-filled, or clear it once); every completed call leaves them zero, so
+ * one workspace can serve any sequence of shapes on one stream. */
 int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host);
 
 /* C = A x B^T with A quantised on the fly (quantisation, block-scaled MFMA
@@ -98,13 +101,14 @@ int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host);
  *   packed_dev weight packed by mx_pack_weight for (N, K)
  *   C_dev      bf16 [M, N] output, ldc >= N
  *   ws_dev     workspace of ws_bytes >= mx_gemm_workspace_bytes(M, N, K),
- *              256-byte aligned (may be NULL when that is 0); no
- *              initialisation needed, scratch after the call.  Calls that
- *              overlap in time (other streams) need separate workspaces.
+ *              256-byte aligned (may be NULL when that is 0), zero-filled
+ *              before its first use (see mx_gemm_workspace_bytes).  Calls
+ *              that overlap in time (other streams) need separate
+ *              workspaces.
  * Launches per call: 1 (A quantised inside the GEMM), +1 for the quantisation
  * kernel when the plan's amode is MX_AMODE_PREQUANT, +1 for the split-K
- * reduction when splits > 1.
- * The split-K reduction sums the partials in split order: results do not
+ * reduction when splits > 1 and the plan's finish is MX_FINISH_KERNEL.
+ * Either split-K finish sums the partials in split order: results do not
  * depend on timing. */
 int mx_gemm(const void* A_dev, int M, int K, int lda,
             const void* packed_dev, int N,
@@ -122,6 +126,7 @@ typedef struct mx_plan {
     int wk;          /* waves along K per workgroup (1, 2, 4, 8 or 16; wn*wk <= 16) */
     int splits;      /* workgroups along K; > 1 adds a reduction kernel */
     int amode;       /* where A is quantised: one of MX_AMODE_* */
+    int finish;      /* who sums the split-K partials: one of MX_FINISH_* */
 } mx_plan;
 
 /* Activation modes of a plan. */
@@ -131,6 +136,13 @@ enum {
     MX_AMODE_PREQUANT = 1,  /* a first kernel quantises A into the workspace */
     MX_AMODE_DIRECT = 2     /* each wave quantises the A fragments it consumes
                                in registers (no LDS, no barrier) */
+};
+
+/* Split-K finishes of a plan (no effect when splits == 1). */
+enum {
+    MX_FINISH_KERNEL = 0,       /* a second kernel sums the partials */
+    MX_FINISH_LAST_ARRIVAL = 1  /* the last GEMM workgroup to finish a tile
+                                   sums them (at most 4096 output tiles) */
 };
 
 /* The plan mx_gemm uses for (M, N, K) (host only). */

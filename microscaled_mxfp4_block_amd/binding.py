@@ -25,6 +25,9 @@ MX_EPLAN = -5
 MX_AMODE_LDS = 0
 MX_AMODE_PREQUANT = 1
 MX_AMODE_DIRECT = 2
+# split-K finishes of a plan
+MX_FINISH_KERNEL = 0
+MX_FINISH_LAST_ARRIVAL = 1
 
 EXPORTS = [
     "mx_strerror", "mx_packed_weight_bytes", "mx_pack_weight", "mx_unpack_weight",
@@ -35,7 +38,8 @@ EXPORTS = [
 
 class MxPlan(ctypes.Structure):
     _fields_ = [("mb", ctypes.c_int), ("nb", ctypes.c_int), ("wn", ctypes.c_int), ("wk", ctypes.c_int),
-                ("splits", ctypes.c_int), ("amode", ctypes.c_int)]
+                ("splits", ctypes.c_int), ("amode", ctypes.c_int),
+                ("finish", ctypes.c_int)]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}
@@ -171,9 +175,9 @@ def mx_gemm_workspace_bytes(M: int, N: int, K: int, plan: Optional[dict] = None)
 
 
 def new_workspace(M: int, N: int, K: int, plan: Optional[dict] = None, device="cuda") -> torch.Tensor:
-    """A workspace for mx_gemm on this shape (and plan)."""
+    """A zero-filled workspace for mx_gemm on this shape (and plan); calls keep its counters zero."""
     nbytes = mx_gemm_workspace_bytes(M, N, K, plan)
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
 def mx_gemm(A: torch.Tensor, packed: torch.Tensor, N: int, C: Optional[torch.Tensor] = None,
@@ -194,6 +198,7 @@ def mx_gemm(A: torch.Tensor, packed: torch.Tensor, N: int, C: Optional[torch.Ten
     else:
         rc = ext().gemm_with_plan(A.data_ptr(), M, K, lda, packed.data_ptr(), N, C.data_ptr(), ldc,
                                   workspace.data_ptr(), workspace.numel(), plan["mb"], plan["nb"], plan["wn"],
-                                  plan["wk"], plan["splits"], plan["amode"], s)
+                                  plan["wk"], plan["splits"], plan["amode"],
+                                  plan.get("finish", MX_FINISH_KERNEL), s)
     _check(rc, "mx_gemm")
     return C

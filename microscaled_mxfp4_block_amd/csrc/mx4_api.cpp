@@ -40,14 +40,14 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MX_OK : MX_EHIP; }
 // in model_plan().
 struct TableEntry {
     int M, N, K;
-    Plan plan;   // mb, nb, wn, wk, splits, amode
+    Plan plan;   // mb, nb, wn, wk, splits, amode, finish
 };
 const TableEntry kTable[] = {
-    {4, 2880, 512, {1, 1, 1, 4, 1, 0}},
-    {32, 4096, 512, {1, 1, 1, 4, 1, 0}},
-    {16, 2112, 7168, {1, 1, 2, 4, 7, 0}},
-    {64, 7168, 2048, {1, 1, 2, 4, 1, 1}},
-    {256, 3072, 1536, {1, 1, 1, 4, 1, 1}},
+    {4, 2880, 512, {1, 1, 1, 4, 1, 0, 0}},
+    {32, 4096, 512, {1, 1, 1, 4, 1, 0, 0}},
+    {16, 2112, 7168, {1, 1, 2, 4, 7, 0, 0}},
+    {64, 7168, 2048, {1, 1, 2, 4, 1, 1, 0}},
+    {256, 3072, 1536, {1, 1, 1, 4, 1, 1, 0}},
 };
 
 int pow2_floor(int x) {
@@ -59,6 +59,7 @@ int pow2_floor(int x) {
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct Layout {
+    size_t counter_bytes;   // at offset 0 of every non-empty workspace
     size_t aop_offset, aop_bytes;
     size_t partial_offset, partial_bytes;
     size_t total;
@@ -83,11 +84,14 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     l.mtiles = (ga.RB + plan.mb - 1) / plan.mb;
     l.ntiles = (gb.RB + plan.nb * plan.wn - 1) / (plan.nb * plan.wn);
     if ((long long)l.mtiles * l.ntiles * l.splits >= (1LL << 31)) return MX_EINVAL;
-    l.aop_offset = 0;
+    if (plan.finish != 0 && plan.finish != 1) return MX_EPLAN;
+    if (plan.finish == 1 && l.splits > 1 && (long long)l.mtiles * l.ntiles > mx4::kMaxCounters) return MX_EPLAN;
     l.aop_bytes = plan.amode == kAmPrequant ? round_up(ga.total_bytes, 256) : 0;
-    l.partial_offset = l.aop_bytes;
     l.partial_bytes = l.splits > 1 ? round_up((size_t)l.splits * M * gb.RB * mx4::kRowBlock * sizeof(float), 256) : 0;
-    l.total = l.aop_bytes + l.partial_bytes;
+    l.counter_bytes = (l.aop_bytes + l.partial_bytes) > 0 ? mx4::kCounterBytes : 0;
+    l.aop_offset = l.counter_bytes;
+    l.partial_offset = l.aop_offset + l.aop_bytes;
+    l.total = l.counter_bytes + l.aop_bytes + l.partial_bytes;
     *out = l;
     return MX_OK;
 }
@@ -109,6 +113,7 @@ Plan model_plan(int M, int N, int K) {
     p.wn = 1;
     p.wk = pow2_floor(gb.KS < 8 ? gb.KS : 8);
     p.splits = 1;
+    p.finish = 0;
     Layout l;
     while (p.splits < gb.KS && plan_layout(p, M, N, K, &l) != MX_OK) ++p.splits;
     const long long tiles = (long long)((ga.RB + p.mb - 1) / p.mb) * gb.RB;
@@ -173,6 +178,8 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     p.c_vec = (ldc % 4 == 0 && aligned(C, 8)) ? 1 : 0;
     p.partial = lay.splits > 1 ? (float*)(wsb + lay.partial_offset) : nullptr;
     p.ldp = gb.RB * mx4::kRowBlock;
+    const bool finish_in_gemm = lay.splits > 1 && plan.finish == 1;
+    p.counters = finish_in_gemm ? (uint32_t*)wsb : nullptr;
 
     if (plan.amode == kAmPrequant) {
         rc = hip_status(mx4::launch_pack((const uint16_t*)A, M, K, lda, wsb + lay.aop_offset, s));
@@ -182,7 +189,7 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     run.splits = lay.splits;
     rc = hip_status(mx4::launch_gemm(run, p, s));
     if (rc) return rc;
-    if (lay.splits > 1) rc = hip_status(mx4::launch_reduce(p, s));
+    if (lay.splits > 1 && !finish_in_gemm) rc = hip_status(mx4::launch_reduce(p, s));
     return rc;
 }
 
@@ -252,6 +259,7 @@ int mx_gemm_plan(int M, int N, int K, mx_plan* plan_host) {
     plan_host->wk = p.wk;
     plan_host->splits = lay.splits;
     plan_host->amode = p.amode;
+    plan_host->finish = p.finish;
     return MX_OK;
 }
 
@@ -261,7 +269,8 @@ int mx_gemm_plan_workspace_bytes(const mx_plan* plan_host, int M, int N, int K, 
     if (rc) return rc;
     rc = check_operand_shape(N, K);
     if (rc) return rc;
-    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wn, plan_host->wk, plan_host->splits, plan_host->amode};
+    const Plan p = {plan_host->mb,     plan_host->nb,    plan_host->wn,    plan_host->wk,
+                    plan_host->splits, plan_host->amode, plan_host->finish};
     Layout lay;
     rc = plan_layout(p, M, N, K, &lay);
     if (rc) return rc;
@@ -279,7 +288,8 @@ int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host) {
 int mx_gemm_with_plan(const void* A_dev, int M, int K, int lda, const void* packed_dev, int N, void* C_dev, int ldc,
                       void* ws_dev, size_t ws_bytes, const mx_plan* plan_host, void* stream) {
     if (!plan_host) return MX_EALIGN;
-    const Plan p = {plan_host->mb, plan_host->nb, plan_host->wn, plan_host->wk, plan_host->splits, plan_host->amode};
+    const Plan p = {plan_host->mb,     plan_host->nb,    plan_host->wn,    plan_host->wk,
+                    plan_host->splits, plan_host->amode, plan_host->finish};
     return gemm_impl(A_dev, M, K, lda, packed_dev, N, C_dev, ldc, ws_dev, ws_bytes, p, stream);
 }
 

@@ -29,9 +29,15 @@
 //                 the same m rows and K steps each quantise them.
 //   3. K loop: MFMAs on registers (and 16-byte LDS reads with kAmLds).
 //   4. The WK waves add their accumulators through LDS; the result is
-//      rounded to bf16 and stored, or, when K is split over workgroups,
-//      written as fp32 partials that reduce_kernel sums in split order
-//      (deterministic, no atomics).
+//      rounded to bf16, staged in LDS and stored in 16-byte row chunks.
+//      When K is split over workgroups, each writes fp32 partials and
+//      either reduce_kernel sums them in split order (a second launch), or
+//      the last workgroup of a tile to arrive does (one launch): its arrival
+//      is counted by an agent-scope atomic on a per-tile counter, the
+//      partials are written and read with agent-scope (L2-coherent across
+//      XCDs) accesses, and that workgroup returns the counter to zero.
+//      Either way the sum runs in split order, so results do not depend on
+//      timing.
 #include "mx4_device.h"
 #include "mx4_internal.h"
 
@@ -52,6 +58,21 @@ __host__ __device__ constexpr size_t gemm_red_bytes(int wn, int wk, int mb, int 
 }
 __host__ __device__ constexpr size_t gemm_stage_bytes(int wn, int mb, int nb) {
     return (size_t)mb * kRowBlock * (nb * wn * kRowBlock + 8) * 2;
+}
+
+// Four fp32 partials as two 64-bit agent-scope atomic accesses: coherent
+// across the XCDs' L2s without a cache-wide write-back or invalidate.
+__device__ __forceinline__ void store_partial_agent(float* dst, const float (&v)[4]) {
+    const uint64_t lo = (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
+    const uint64_t hi = (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32);
+    __hip_atomic_store((uint64_t*)dst, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store((uint64_t*)dst + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ f32x4 load_partial_agent(const float* src) {
+    const uint64_t lo = __hip_atomic_load((const uint64_t*)src, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load((const uint64_t*)src + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return f32x4{__uint_as_float((uint32_t)lo), __uint_as_float((uint32_t)(lo >> 32)),
+                 __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
 }
 
 // 4 consecutive bf16 outputs (n0..n0+3) of row m, masked at N.
@@ -264,6 +285,8 @@ gemm_kernel(GemmParams p) {
     float* red = (float*)lds;
     uint16_t* stage = (uint16_t*)(lds + gemm_red_bytes(WN, WK, MBLK, NBLK));
     const bool partial = p.splits > 1;
+    const bool finish_here = partial && p.counters != nullptr;
+    __shared__ uint32_t last_arrival;
     if constexpr (FUSED || WK > 1) __syncthreads();   // every wave is done with the activation operand
     if constexpr (WK > 1) {
 #pragma unroll
@@ -277,22 +300,53 @@ gemm_kernel(GemmParams p) {
     // groups of 4 consecutive n per (i, j, r); the WK waves of column wn share
     // them.  Split-K partials go straight to the workspace as fp32; bf16
     // results are staged in LDS as a row-major tile first.
+    auto stage4 = [&](int i, int j, int r, const float (&v)[4]) {
+        const int row = i * kRowBlock + m_lane;
+        const int col = (wn * NBLK + j) * kRowBlock + 8 * r + n_lane;
+        uint2 w;
+        w.x = pack_bf16x2(v[0], v[1]);
+        w.y = pack_bf16x2(v[2], v[3]);
+        *(uint2*)(stage + row * SROW + col) = w;
+    };
     auto emit = [&](int i, int j, int r, const float (&v)[4]) {
         if (partial) {
             const int m = (mb0 + i) * kRowBlock + m_lane;
             const int nb = nb0 + j;
             const int n0 = nb * kRowBlock + 8 * r + n_lane;
             if (m >= p.M || nb >= p.RBn) return;
-            const f32x4 pv = {v[0], v[1], v[2], v[3]};
-            *(f32x4*)(p.partial + ((size_t)split * p.M + m) * p.ldp + n0) = pv;
+            float* dst = p.partial + ((size_t)split * p.M + m) * p.ldp + n0;
+            if (finish_here) {
+                store_partial_agent(dst, v);
+            } else {
+                const f32x4 pv = {v[0], v[1], v[2], v[3]};
+                *(f32x4*)dst = pv;
+            }
         } else {
-            const int row = i * kRowBlock + m_lane;
-            const int col = (wn * NBLK + j) * kRowBlock + 8 * r + n_lane;
-            uint2 w;
-            w.x = pack_bf16x2(v[0], v[1]);
-            w.y = pack_bf16x2(v[2], v[3]);
-            *(uint2*)(stage + row * SROW + col) = w;
+            stage4(i, j, r, v);
         }
+    };
+    // The last arrival's sum of one group over the splits, in split order.
+    auto finish = [&](int i, int j, int r) {
+        const int m = (mb0 + i) * kRowBlock + m_lane;
+        const int nb = nb0 + j;
+        const int n0 = nb * kRowBlock + 8 * r + n_lane;
+        float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (m < p.M && nb < p.RBn) {
+            const float* src = p.partial + (size_t)m * p.ldp + n0;
+            f32x4 acc4 = load_partial_agent(src);
+            for (int k = 1; k < p.splits; ++k) {
+                const f32x4 x = load_partial_agent(src + (size_t)k * p.M * p.ldp);
+                acc4.x += x.x;
+                acc4.y += x.y;
+                acc4.z += x.z;
+                acc4.w += x.w;
+            }
+            v[0] = acc4.x;
+            v[1] = acc4.y;
+            v[2] = acc4.z;
+            v[3] = acc4.w;
+        }
+        stage4(i, j, r, v);
     };
     if constexpr (WK == 1) {
 #pragma unroll
@@ -322,7 +376,34 @@ gemm_kernel(GemmParams p) {
             emit(i, j, r, v);
         }
     }
-    if (partial) return;
+    if (partial) {
+        if (!finish_here) return;   // reduce_kernel sums the partials
+        // Every wave's partial stores have completed (the barrier waits for
+        // them); one atomic per workgroup counts the arrival at this tile.
+        __syncthreads();
+        if (tid == 0) {
+            uint32_t* counter = p.counters + (nt * p.mtiles + mt);
+            const uint32_t before = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            last_arrival = before == (uint32_t)(p.splits - 1);
+            if (last_arrival) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (!last_arrival) return;
+        if constexpr (WK == 1) {
+#pragma unroll
+            for (int i = 0; i < MBLK; ++i)
+#pragma unroll
+                for (int j = 0; j < NBLK; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) finish(i, j, r);
+        } else {
+            constexpr int GPW = MBLK * NBLK * 4;
+            for (int gi = wkk; gi < GPW; gi += WK) {
+                const int ij = gi >> 2, r = gi & 3;
+                finish(ij / NBLK, ij % NBLK, r);
+            }
+        }
+    }
     __syncthreads();
     // the staged tile leaves in 16-byte row chunks: consecutive lanes write
     // consecutive bytes of a row of C

@@ -12,8 +12,15 @@ namespace mx4 {
 // Largest number of K steps one wave holds in registers (its whole share of
 // a split); the planner splits K further when a shape needs more.
 constexpr int kStepsPerWaveMax = 8;
-// Largest LDS block the planner gives a workgroup (gfx950: 160 KiB per CU).
-constexpr size_t kLdsBudget = 160 * 1024;
+// Largest dynamic LDS block the planner gives a workgroup (gfx950: 160 KiB
+// per CU, less a little for the kernel's static LDS).
+constexpr size_t kLdsBudget = 160 * 1024 - 256;
+
+// Per-tile arrival counters sit at the start of every non-empty workspace,
+// whatever the shape, so that a workspace reused across shapes never has
+// partials or activation codes written over a counter.
+constexpr size_t kCounterBytes = 16384;
+constexpr int kMaxCounters = (int)(kCounterBytes / 4);
 
 // Arguments of the GEMM and reduction kernels.  The MFMA's first operand is
 // the weight tile (rows = N), the second the activation tile (rows = M), so
@@ -39,13 +46,17 @@ struct GemmParams {
     int c_vec;                // 1 when rows of C are 8-byte aligned (ldc % 4 == 0)
     float* partial;           // fp32 partials [splits, M, ldp] when splits > 1
     int ldp;
+    uint32_t* counters;       // per-tile arrival counters (zero between calls) when the
+                              // last-arriving workgroup sums the partials, else null
 };
 
 // mb: 32-row M blocks per wave; nb: 32-row N blocks per wave; wn x wk waves
 // per workgroup (wn along N, wk along K); splits along K; amode: where the
-// activation is quantised (kAm*, the same values as the public MX_AMODE_*).
+// activation is quantised (kAm*, the same values as the public MX_AMODE_*);
+// finish: with splits > 1, 1 = the last workgroup to arrive at a tile sums
+// the partials, 0 = reduce_kernel does.
 struct Plan {
-    int mb, nb, wn, wk, splits, amode;
+    int mb, nb, wn, wk, splits, amode, finish;
 };
 constexpr int kAmLds = 0;        // by the workgroup, into LDS
 constexpr int kAmPrequant = 1;   // by pack_kernel, into the workspace

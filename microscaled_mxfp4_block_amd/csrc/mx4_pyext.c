@@ -58,11 +58,11 @@ static PyObject* py_gemm(PyObject* self, PyObject* const* a, Py_ssize_t n) {
 }
 
 /* gemm_with_plan(A, M, K, lda, packed, N, C, ldc, ws, ws_bytes,
- *                mb, nb, wn, wk, splits, amode, stream) -> rc */
+ *                mb, nb, wn, wk, splits, amode, finish, stream) -> rc */
 static PyObject* py_gemm_with_plan(PyObject* self, PyObject* const* a, Py_ssize_t n) {
     (void)self;
-    if (n != 17) {
-        PyErr_SetString(PyExc_TypeError, "gemm_with_plan expects 17 arguments");
+    if (n != 18) {
+        PyErr_SetString(PyExc_TypeError, "gemm_with_plan expects 18 arguments");
         return NULL;
     }
     void *A, *P, *C, *W, *S;
@@ -73,7 +73,7 @@ static PyObject* py_gemm_with_plan(PyObject* self, PyObject* const* a, Py_ssize_
         get_ptr(a[4], &P) || get_int(a[5], &N) || get_ptr(a[6], &C) || get_int(a[7], &ldc) ||
         get_ptr(a[8], &W) || get_size(a[9], &wsb) || get_int(a[10], &plan.mb) || get_int(a[11], &plan.nb) ||
         get_int(a[12], &plan.wn) || get_int(a[13], &plan.wk) || get_int(a[14], &plan.splits) ||
-        get_int(a[15], &plan.amode) || get_ptr(a[16], &S))
+        get_int(a[15], &plan.amode) || get_int(a[16], &plan.finish) || get_ptr(a[17], &S))
         return NULL;
     return PyLong_FromLong(mx_gemm_with_plan(A, M, K, lda, P, N, C, ldc, W, wsb, &plan, S));
 }

@@ -121,6 +121,7 @@ def test_plans_for_workloads():
         p = B.mx_gemm_plan(w.M, w.N, w.K)
         assert p["mb"] in (1, 2) and p["nb"] in (1, 2) and p["wn"] in (1, 2)
         assert p["amode"] in (B.MX_AMODE_LDS, B.MX_AMODE_PREQUANT, B.MX_AMODE_DIRECT)
+        assert p["finish"] in (B.MX_FINISH_KERNEL, B.MX_FINISH_LAST_ARRIVAL)
         assert p["wk"] in (1, 2, 4, 8) and p["wn"] * p["wk"] <= 16 and p["splits"] >= 1
         ws = B.mx_gemm_workspace_bytes(w.M, w.N, w.K)
         if p["splits"] == 1 and p["amode"] != B.MX_AMODE_PREQUANT:
@@ -142,6 +143,7 @@ def test_explicit_plan_rejections():
            dict(mb=1, nb=1, wn=4, wk=8, splits=4, amode=0),      # no such wave count along N
            dict(mb=1, nb=1, wn=2, wk=16, splits=4, amode=2),     # more than 16 waves
            dict(mb=1, nb=1, wn=1, wk=4, splits=4, amode=3),      # no such activation mode
+           dict(mb=1, nb=1, wn=1, wk=4, splits=4, amode=0, finish=2),   # no such split-K finish
            dict(mb=1, nb=1, wn=1, wk=4, splits=0, amode=1),
            dict(mb=1, nb=1, wn=1, wk=4, splits=1000, amode=1),   # more splits than K steps
            dict(mb=1, nb=1, wn=1, wk=8, splits=1, amode=1),      # 14 K steps per wave > register budget
@@ -164,8 +166,27 @@ def test_fast_call_extension_validates_without_gpu():
     # same validation path as the C entry points: no HIP call is reached
     assert ext.gemm(FAKE, 0, 512, 512, FAKE, 64, FAKE, 64, 0, 0, 0) == B.MX_EINVAL
     assert ext.gemm(FAKE, 4, 512, 512, None, 64, FAKE, 64, 0, 0, 0) == B.MX_EALIGN
-    assert ext.gemm_with_plan(FAKE, 4, 512, 512, FAKE, 64, FAKE, 64, 0, 0, 3, 1, 1, 1, 1, 0, 0) == B.MX_EPLAN
+    assert ext.gemm_with_plan(FAKE, 4, 512, 512, FAKE, 64, FAKE, 64, 0, 0, 3, 1, 1, 1, 1, 0, 0, 0) == B.MX_EPLAN
+    assert ext.gemm_with_plan(FAKE, 4, 512, 512, FAKE, 64, FAKE, 64, 0, 0, 1, 1, 1, 1, 2, 0, 5, 0) == B.MX_EPLAN
     with pytest.raises(TypeError):
         ext.gemm(1, 2, 3)
     with pytest.raises(OverflowError):
         ext.gemm(FAKE, 1 << 40, 512, 512, FAKE, 64, FAKE, 64, 0, 0, 0)
+
+
+def test_workspace_layout_reserves_counters():
+    """A non-empty workspace always starts with the 16 KiB counter block, so
+    that shapes sharing one workspace never overlap a counter."""
+    p = dict(mb=1, nb=1, wn=1, wk=4, splits=1, amode=B.MX_AMODE_LDS, finish=0)
+    assert B.mx_gemm_workspace_bytes(32, 4096, 512, p) == 0
+    pre = dict(p, amode=B.MX_AMODE_PREQUANT)
+    codes = 32 * 512 // 2 + 32 * 512 // 32
+    assert B.mx_gemm_workspace_bytes(32, 4096, 512, pre) == 16384 + (codes + 255) // 256 * 256
+    split = dict(p, splits=2, finish=1)
+    assert B.mx_gemm_workspace_bytes(32, 4096, 512, split) == 16384 + 2 * 32 * 4096 * 4
+    # more output tiles than counters: only the reduction kernel can finish
+    big = dict(p, splits=2, finish=1)
+    with pytest.raises(B.MxError) as e:
+        B.mx_gemm_workspace_bytes(32 * 65, 32 * 64, 512, big)
+    assert e.value.code == B.MX_EPLAN
+    assert B.mx_gemm_workspace_bytes(32 * 65, 32 * 64, 512, dict(big, finish=0)) > 0

@@ -210,11 +210,16 @@ PLANS = [
     dict(mb=1, nb=2, wn=1, wk=16, splits=1, amode=2),
     dict(mb=2, nb=1, wn=1, wk=8, splits=2, amode=2),
     dict(mb=1, nb=1, wn=2, wk=4, splits=7, amode=2),
+    dict(mb=1, nb=1, wn=2, wk=4, splits=7, amode=0, finish=1),
+    dict(mb=2, nb=2, wn=1, wk=1, splits=6, amode=1, finish=1),
+    dict(mb=1, nb=2, wn=2, wk=4, splits=3, amode=2, finish=1),
+    dict(mb=2, nb=1, wn=1, wk=16, splits=2, amode=0, finish=1),
 ]
 
 
 def plan_id(p):
-    return "mb%d_nb%d_wn%d_wk%d_s%d_q%d" % (p["mb"], p["nb"], p["wn"], p["wk"], p["splits"], p["amode"])
+    return "mb%d_nb%d_wn%d_wk%d_s%d_a%d_f%d" % (p["mb"], p["nb"], p["wn"], p["wk"], p["splits"], p["amode"],
+                                                p.get("finish", 0))
 
 
 def plan_runs(M, N, K, plan):
@@ -293,7 +298,8 @@ def test_gemm_streams_and_reuse_of_workspace():
     s = torch.cuda.Stream()
     shapes = [(16, 2112, 7168), (70, 300, 1536)]
     ws_bytes = max(B.mx_gemm_workspace_bytes(*sh) for sh in shapes)
-    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=DEV)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=DEV)
+    s.wait_stream(torch.cuda.current_stream())
     outs = []
     with torch.cuda.stream(s):
         for (M, N, K) in shapes:
@@ -305,3 +311,55 @@ def test_gemm_streams_and_reuse_of_workspace():
     s.synchronize()
     for C, A, Bm in outs:
         assert_c_close(inputs.bits(C.cpu()), oracle.gemm(inputs.bits(A), inputs.bits(Bm)), "stream")
+
+
+LAST_ARRIVAL_CASES = [
+    ((16, 2112, 7168), dict(mb=1, nb=1, wn=2, wk=4, splits=7, amode=0)),
+    ((16, 2112, 7168), dict(mb=1, nb=2, wn=1, wk=8, splits=14, amode=2)),
+    ((33, 130, 2048), dict(mb=2, nb=1, wn=1, wk=2, splits=8, amode=1)),
+    ((70, 300, 1536), dict(mb=1, nb=1, wn=1, wk=4, splits=3, amode=0)),
+    ((9, 70, 352), dict(mb=1, nb=1, wn=1, wk=1, splits=6, amode=2)),
+]
+
+
+@pytest.mark.parametrize("case", LAST_ARRIVAL_CASES, ids=lambda c: "x".join(map(str, c[0])) + "_s%d" % c[1]["splits"])
+def test_split_k_last_arrival_matches_reduce_kernel(case):
+    """The in-GEMM finish sums the same partials in the same order as the
+    reduction kernel: bit-identical C, within tolerance of the oracle, and
+    the arrival counters are back at zero after every call."""
+    (M, N, K), plan = case
+    if not plan_runs(M, N, K, dict(plan, finish=1)):
+        pytest.skip("plan outside the register / LDS budget for this shape")
+    say("last arrival", (M, N, K), plan)
+    A, Bm = inputs.shape_inputs(M, N, K, seed=5 + M + K)
+    Ad = to_dev(A)
+    packed = B.mx_pack_weight(to_dev(Bm))
+    ref_kernel = gpu_bits(B.mx_gemm(Ad, packed, N, plan=dict(plan, finish=0)))
+    ws = B.new_workspace(M, N, K, dict(plan, finish=1), device=DEV)
+    outs = [B.mx_gemm(Ad, packed, N, plan=dict(plan, finish=1), workspace=ws) for _ in range(5)]
+    torch.cuda.synchronize()
+    assert int(ws[:16384].count_nonzero()) == 0, "arrival counters not returned to zero"
+    for C in outs:
+        np.testing.assert_array_equal(gpu_bits(C), ref_kernel)
+    assert_c_close(ref_kernel, oracle.gemm(inputs.bits(A), inputs.bits(Bm)), "last arrival")
+
+
+def test_split_k_last_arrival_workspace_across_shapes():
+    """One zero-filled workspace serves a sequence of shapes and plans, with
+    partials of one shape landing where another's activation codes were."""
+    seq = [((16, 2112, 7168), dict(mb=1, nb=1, wn=2, wk=4, splits=7, amode=0, finish=1)),
+           ((70, 300, 1536), dict(mb=2, nb=1, wn=1, wk=4, splits=3, amode=1, finish=1)),
+           ((16, 2112, 7168), dict(mb=1, nb=1, wn=2, wk=4, splits=7, amode=0, finish=1)),
+           ((33, 130, 2048), dict(mb=1, nb=1, wn=1, wk=8, splits=4, amode=2, finish=1)),
+           ((70, 300, 1536), dict(mb=2, nb=1, wn=1, wk=4, splits=3, amode=1, finish=1))]
+    ws = torch.zeros(max(B.mx_gemm_workspace_bytes(*sh, p) for sh, p in seq), dtype=torch.uint8, device=DEV)
+    data = {}
+    for (M, N, K), plan in seq:
+        if (M, N, K) not in data:
+            A, Bm = inputs.shape_inputs(M, N, K, seed=M * N)
+            data[(M, N, K)] = (A, Bm, to_dev(A), B.mx_pack_weight(to_dev(Bm)))
+        A, Bm, Ad, packed = data[(M, N, K)]
+        say("workspace sequence", (M, N, K), plan)
+        C = gpu_bits(B.mx_gemm(Ad, packed, N, plan=plan, workspace=ws))
+        assert_c_close(C, oracle.gemm(inputs.bits(A), inputs.bits(Bm)), str((M, N, K)))
+    assert int(ws[:16384].count_nonzero()) == 0
