@@ -79,6 +79,15 @@ int mx_pack_weight(const void* B_dev, int N, int K, int ldb,
 int mx_unpack_weight(const void* packed_dev, int N, int K,
                      void* codes_dev, void* scales_dev, void* stream);
 
+/* Import of a weight quantised elsewhere by the same MXFP4 rule: natural
+ * e2m1 codes [N, K/2] (two per byte, even k in the low nibble; codes_dev
+ * 16-byte aligned) and e8m0 scales [N, K/32] are moved unchanged into the
+ * packed layout, with no re-quantisation; the exact inverse of
+ * mx_unpack_weight on the bytes it covers.
+ *   packed_dev  output, packed_bytes >= mx_packed_weight_bytes(N, K), 16-B aligned */
+int mx_import_weight(const void* codes_dev, const void* scales_dev, int N, int K,
+                     void* packed_dev, size_t packed_bytes, void* stream);
+
 /* Stand-alone activation quantisation to the natural layouts.
  *   A_dev       bf16 [M, K], row stride lda (lda >= K, lda % 8 == 0)
  *   codes_dev   [M, K/2] bytes, scales_dev [M, K/32] bytes (dense) */

@@ -9,6 +9,7 @@ from .binding import (  # noqa: F401
     mx_gemm,
     mx_gemm_plan,
     mx_gemm_workspace_bytes,
+    mx_import_weight,
     mx_pack_weight,
     mx_packed_weight_bytes,
     mx_quant_act,

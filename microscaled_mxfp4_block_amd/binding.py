@@ -31,7 +31,7 @@ MX_FINISH_LAST_ARRIVAL = 1
 
 EXPORTS = [
     "mx_strerror", "mx_packed_weight_bytes", "mx_pack_weight", "mx_unpack_weight",
-    "mx_quant_act", "mx_gemm_workspace_bytes", "mx_gemm", "mx_gemm_plan",
+    "mx_import_weight", "mx_quant_act", "mx_gemm_workspace_bytes", "mx_gemm", "mx_gemm_plan",
     "mx_gemm_plan_workspace_bytes", "mx_gemm_with_plan",
 ]
 
@@ -80,6 +80,7 @@ def lib() -> ctypes.CDLL:
         L.mx_packed_weight_bytes.argtypes = [I, I, PS]
         L.mx_pack_weight.argtypes = [P, I, I, I, P, S, P]
         L.mx_unpack_weight.argtypes = [P, I, I, P, P, P]
+        L.mx_import_weight.argtypes = [P, P, I, I, P, S, P]
         L.mx_quant_act.argtypes = [P, I, I, I, P, P, P]
         L.mx_gemm_workspace_bytes.argtypes = [I, I, I, PS]
         L.mx_gemm.argtypes = [P, I, I, I, P, I, P, I, P, S, P]
@@ -143,6 +144,20 @@ def mx_unpack_weight(packed: torch.Tensor, N: int, K: int, stream=None) -> Tuple
     _check(lib().mx_unpack_weight(_ptr(packed), N, K, _ptr(codes), _ptr(scales), _stream(stream)),
            "mx_unpack_weight")
     return codes, scales
+
+
+def mx_import_weight(codes: torch.Tensor, scales: torch.Tensor, N: int, K: int, packed: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Packed weight from natural-layout codes [N, K/2] and e8m0 bytes [N, K/32] quantised elsewhere."""
+    for t, name, cols in ((codes, "codes", K // 2), (scales, "scales", K // 32)):
+        if t.dtype != torch.uint8 or tuple(t.shape) != (N, cols) or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous uint8 [%d, %d] tensor" % (name, N, cols))
+    nbytes = mx_packed_weight_bytes(N, K)
+    if packed is None:
+        packed = torch.empty(nbytes, dtype=torch.uint8, device=codes.device)
+    _check(lib().mx_import_weight(_ptr(codes), _ptr(scales), N, K, _ptr(packed), packed.numel(), _stream(stream)),
+           "mx_import_weight")
+    return packed
 
 
 def mx_quant_act(A: torch.Tensor, codes: Optional[torch.Tensor] = None, scales: Optional[torch.Tensor] = None,

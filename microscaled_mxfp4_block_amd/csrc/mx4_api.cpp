@@ -43,8 +43,9 @@ struct TableEntry {
     Plan plan;   // mb, nb, wn, wk, splits, amode, finish
 };
 const TableEntry kTable[] = {
-    {4, 2880, 512, {1, 1, 1, 4, 1, 0, 0}},
-    {32, 4096, 512, {1, 1, 1, 4, 1, 0, 0}},
+    {4, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
+    {32, 4096, 512, {1, 1, 1, 4, 1, 2, 0}},
+    {32, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
     {16, 2112, 7168, {1, 1, 2, 4, 7, 0, 0}},
     {64, 7168, 2048, {1, 1, 2, 4, 1, 1, 0}},
     {256, 3072, 1536, {1, 1, 1, 4, 1, 1, 0}},
@@ -96,9 +97,10 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     return MX_OK;
 }
 
-// Model for shapes without a table entry: quantise A inside the GEMM while
-// the activation slice of a workgroup is small next to the weight it meets,
-// else in a first kernel; two 32-row M blocks per wave when M allows, one
+// Model for shapes without a table entry: quantise A inside the GEMM (each
+// wave its own fragments, in registers) while the activation slice of a
+// workgroup is small next to the weight it meets, else in a first kernel;
+// two 32-row M blocks per wave when M allows, one
 // N block per wave, 8 waves along K (fewer for short K); then the fewest K
 // splits that keep every wave within its register budget and the activation
 // slice within LDS, doubled while the tiles leave most of the 256 CUs idle
@@ -107,7 +109,7 @@ Plan model_plan(int M, int N, int K) {
     const OperandGeom ga = mx4::operand_geom(M, K);
     const OperandGeom gb = mx4::operand_geom(N, K);
     Plan p;
-    p.amode = (ga.RB > 1 || gb.KS > 16) ? kAmPrequant : kAmLds;
+    p.amode = (ga.RB > 1 || gb.KS > 16) ? kAmPrequant : kAmDirect;
     p.mb = (p.amode == kAmPrequant && ga.RB >= 2) ? 2 : 1;
     p.nb = 1;
     p.wn = 1;
@@ -232,6 +234,16 @@ int mx_unpack_weight(const void* packed_dev, int N, int K, void* codes_dev, void
     if (!aligned(packed_dev, 16) || !aligned(codes_dev, 16) || !aligned(scales_dev, 1)) return MX_EALIGN;
     return hip_status(mx4::launch_unpack((const uint8_t*)packed_dev, N, K, (uint8_t*)codes_dev, (uint8_t*)scales_dev,
                                          (hipStream_t)stream));
+}
+
+int mx_import_weight(const void* codes_dev, const void* scales_dev, int N, int K, void* packed_dev,
+                     size_t packed_bytes, void* stream) {
+    int rc = check_operand_shape(N, K);
+    if (rc) return rc;
+    if (!aligned(codes_dev, 16) || !aligned(scales_dev, 1) || !aligned(packed_dev, 16)) return MX_EALIGN;
+    if (packed_bytes < mx4::operand_geom(N, K).total_bytes) return MX_ESPACE;
+    return hip_status(mx4::launch_import((const uint8_t*)codes_dev, (const uint8_t*)scales_dev, N, K,
+                                         (uint8_t*)packed_dev, (hipStream_t)stream));
 }
 
 int mx_quant_act(const void* A_dev, int M, int K, int lda, void* codes_dev, void* scales_dev, void* stream) {

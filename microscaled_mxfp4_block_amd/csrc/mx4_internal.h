@@ -71,6 +71,8 @@ hipError_t launch_reduce(const GemmParams& p, hipStream_t s);
 hipError_t launch_quant_natural(const uint16_t* x, int rows, int K, int ld, uint8_t* codes, uint8_t* scales,
                                 hipStream_t s);
 hipError_t launch_pack(const uint16_t* x, int rows, int K, int ld, uint8_t* packed, hipStream_t s);
+hipError_t launch_import(const uint8_t* codes, const uint8_t* scales, int rows, int K, uint8_t* packed,
+                         hipStream_t s);
 hipError_t launch_unpack(const uint8_t* packed, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s);
 
 }  // namespace mx4

@@ -4,6 +4,8 @@
 //   pack_kernel          : bf16 [rows, K] -> packed operand layout (mx4_layout.h);
 //                          used once for the weight B and per call for A
 //   unpack_kernel        : packed operand layout -> natural codes + scales
+//   import_kernel        : natural codes + scales (already quantised elsewhere)
+//                          -> packed operand layout, bytes moved unchanged
 //
 // The rule is the MXFP4 quantisation of the kernelindex.com amd-mxfp4-mm pages
 // (submission 755056, "Software MXFP4 quant"): per 32-element group, amax
@@ -107,6 +109,31 @@ __global__ void __launch_bounds__(256) unpack_kernel(const uint8_t* __restrict__
     scales[(size_t)row * (K / kGroup) + g] = (uint8_t)(word >> (8 * (t % kStepsPerWord)));
 }
 
+// Natural layouts -> packed layout, no re-quantisation.  One lane per
+// (rb, t, L) slot as in pack_kernel; padding slots get zero codes, byte 0.
+__global__ void __launch_bounds__(256) import_kernel(const uint8_t* __restrict__ codes,
+                                                     const uint8_t* __restrict__ scales, int rows, int K,
+                                                     uint8_t* __restrict__ packed, int RB, int KS, int KW,
+                                                     size_t code_bytes) {
+    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long total = (long long)RB * KW * kStepsPerWord * 64;
+    if (gid >= total) return;
+    const int L = (int)(gid & 63);
+    const long long rt = gid >> 6;
+    const int t = (int)(rt % (KW * kStepsPerWord));
+    const int rb = (int)(rt / (KW * kStepsPerWord));
+    const int row = rb * kRowBlock + (L & 31);
+    const int g = 2 * t + (L >> 5);
+    u32x4 c = {0u, 0u, 0u, 0u};
+    uint32_t byte = 0u;
+    if (row < rows && g < K / kGroup) {
+        c = load16(codes + (size_t)row * (K / 2) + (size_t)g * 16);
+        byte = scales[(size_t)row * (K / kGroup) + g];
+    }
+    if (t < KS) *(u32x4*)(packed + ((size_t)(rb * KS + t) * 64 + L) * 16) = c;
+    packed[code_bytes + ((size_t)(rb * KW + t / kStepsPerWord) * 64 + L) * 4 + t % kStepsPerWord] = (uint8_t)byte;
+}
+
 hipError_t launch_quant_natural(const uint16_t* x, int rows, int K, int ld, uint8_t* codes, uint8_t* scales,
                                 hipStream_t s) {
     const long long total = (long long)rows * (K / 8);
@@ -122,6 +149,16 @@ hipError_t launch_pack(const uint16_t* x, int rows, int K, int ld, uint8_t* pack
     const long long blocks = (total + 255) / 256;
     hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, K, ld, packed, g.RB, g.KS,
                        g.KW, g.code_bytes);
+    return hipGetLastError();
+}
+
+hipError_t launch_import(const uint8_t* codes, const uint8_t* scales, int rows, int K, uint8_t* packed,
+                         hipStream_t s) {
+    const OperandGeom g = operand_geom(rows, K);
+    const long long total = (long long)g.RB * g.KW * kStepsPerWord * 64;
+    const long long blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(import_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales, rows, K, packed, g.RB,
+                       g.KS, g.KW, g.code_bytes);
     return hipGetLastError();
 }
 

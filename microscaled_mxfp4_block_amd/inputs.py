@@ -37,6 +37,12 @@ WORKLOADS = [
     Workload("m256_n3072_k1536", 256, 3072, 1536),
 ]
 
+# A sixth decode shape the same workload family lists (K=512, M=32); inputs
+# come from shape_inputs with a per-shape seed.
+EXTRA_WORKLOADS = [
+    Workload("m32_n2880_k512", 32, 2880, 512),
+]
+
 
 def bf16_randn(rows: int, cols: int, gen: torch.Generator, scale: float = 1.0) -> torch.Tensor:
     """N(0, scale^2) drawn in fp32 from ``gen`` and rounded to a CPU bf16 tensor."""

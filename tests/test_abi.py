@@ -8,6 +8,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 from microscaled_mxfp4_block_amd import binding as B
 from microscaled_mxfp4_block_amd.inputs import WORKLOADS
@@ -77,6 +78,20 @@ def test_pack_weight_validation():
     assert L.mx_pack_weight(None, 64, 512, 512, FAKE, nbytes, None) == B.MX_EALIGN
     assert L.mx_pack_weight(FAKE_ODD, 64, 512, 512, FAKE, nbytes, None) == B.MX_EALIGN
     assert L.mx_pack_weight(FAKE, 64, 512, 512, FAKE, nbytes - 1, None) == B.MX_ESPACE
+
+
+def test_import_weight_validation():
+    L = B.lib()
+    nbytes = size_of(64, 512)[1]
+    assert L.mx_import_weight(FAKE, FAKE, 64, 500, FAKE, nbytes, None) == B.MX_EINVAL      # K % 32
+    assert L.mx_import_weight(FAKE, FAKE, 0, 512, FAKE, nbytes, None) == B.MX_EINVAL
+    assert L.mx_import_weight(FAKE_ODD, FAKE, 64, 512, FAKE, nbytes, None) == B.MX_EALIGN  # codes 16-B
+    assert L.mx_import_weight(FAKE, None, 64, 512, FAKE, nbytes, None) == B.MX_EALIGN
+    assert L.mx_import_weight(FAKE, FAKE + 1, 64, 512, FAKE_ODD, nbytes, None) == B.MX_EALIGN
+    assert L.mx_import_weight(FAKE, FAKE + 1, 64, 512, FAKE, nbytes - 1, None) == B.MX_ESPACE
+    with pytest.raises(ValueError):
+        B.mx_import_weight(torch.zeros((64, 256), dtype=torch.uint8), torch.zeros((64, 15), dtype=torch.uint8),
+                           64, 512)
 
 
 def test_quant_act_validation():

@@ -161,6 +161,32 @@ def test_pack_unpack_ragged_bit_exact(N, K):
     np.testing.assert_array_equal(scales.cpu().numpy(), rs)
 
 
+@pytest.mark.parametrize("N,K", [(4, 64), (33, 96), (70, 160), (129, 1088), (2112, 7168)])
+def test_import_weight_matches_pack(N, K):
+    """Codes and scales quantised by the oracle, imported into the packed
+    layout, give the very bytes mx_pack_weight writes (padding included),
+    and unpack back to themselves."""
+    Bm = inputs.binade_spread(N, K, seed=3 * N + K, lo=-20, hi=20)
+    rc, rs = oracle.quant(inputs.bits(Bm))
+    imported = B.mx_import_weight(to_dev(torch.from_numpy(rc)), to_dev(torch.from_numpy(rs)), N, K)
+    packed = B.mx_pack_weight(to_dev(Bm))
+    codes, scales = B.mx_unpack_weight(imported, N, K)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(imported.cpu().numpy(), packed.cpu().numpy())
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+
+
+def test_import_weight_gemm():
+    """A GEMM on an imported weight against the oracle on the same codes."""
+    M, N, K = 16, 300, 1536
+    A, Bm = inputs.shape_inputs(M, N, K, seed=99)
+    rc, rs = oracle.quant(inputs.bits(Bm))
+    packed = B.mx_import_weight(to_dev(torch.from_numpy(rc)), to_dev(torch.from_numpy(rs)), N, K)
+    C = gpu_bits(B.mx_gemm(to_dev(A), packed, N))
+    assert_c_close(C, oracle.gemm(inputs.bits(A), inputs.bits(Bm)), "imported weight")
+
+
 def test_pack_adversarial_bit_exact():
     x = adversarial_rows()
     packed = B.mx_pack_weight(to_dev(inputs.from_bits(x)))
@@ -184,6 +210,15 @@ def test_gemm_workloads_full(idx, seed):
     C = run_gemm(A, Bm)
     ref = oracle.gemm(inputs.bits(A), inputs.bits(Bm))
     assert_c_close(C, ref, w.name)
+
+
+@pytest.mark.parametrize("w", inputs.EXTRA_WORKLOADS, ids=[w.name for w in inputs.EXTRA_WORKLOADS])
+@pytest.mark.parametrize("seed", [1, 2])
+def test_gemm_extra_workloads_full(w, seed):
+    say("gemm", w.name, seed, B.mx_gemm_plan(w.M, w.N, w.K))
+    A, Bm = inputs.shape_inputs(w.M, w.N, w.K, seed=seed)
+    C = run_gemm(A, Bm)
+    assert_c_close(C, oracle.gemm(inputs.bits(A), inputs.bits(Bm)), w.name)
 
 
 SMALL_SHAPES = [
