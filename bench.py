@@ -113,6 +113,32 @@ def time_loop(torch, st, steps, warmup, rotate=True):
     return wall, e0.elapsed_time(e1) * 1e3 / steps
 
 
+def graph_loop(torch, st, ncap=100, reps=20):
+    """GPU time per call with the host out of the loop: `ncap` calls over
+    distinct buffer copies are captured once into a HIP graph on a side
+    stream and replayed `reps` times between two events on that stream."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        handle = torch.cuda.current_stream().cuda_stream
+        for i in range(ncap):
+            rc = st.fn(*st.args[i % st.copies][:-1], handle)
+            if rc:
+                raise RuntimeError("mx_gemm returned %d under capture" % rc)
+    with torch.cuda.stream(s):
+        g.replay()
+        g.replay()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(s)
+        for _ in range(reps):
+            g.replay()
+        e1.record(s)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / (reps * ncap)
+
+
 def cpu_baseline(idx, inputs, seconds=10.0):
     """The oracle (C, fp64 accumulation, OpenMP over N) on the host cores:
     quantise A + dequantise + GEMM per call; B is quantised and dequantised
@@ -155,6 +181,94 @@ def profile_run(torch, B, inputs, calls):
         torch.cuda.empty_cache()
 
 
+def summarize_profiles(trace_dir, fetch_dir, write_dir, calls_trace, calls_pmc):
+    """Write profiles/gemm_kernels_trace.md (per-kernel durations from a
+    rocprofv3 kernel trace of `bench.py --profile`, HBM bytes from the
+    FETCH_SIZE and WRITE_SIZE passes) and profiles/gemm_traffic.json (the
+    bytes per GEMM launch that the bench line reports as roofline traffic).
+    The counters are scaled by their reading on the 256 MiB copy that
+    `--profile` runs first."""
+    import collections
+    import csv
+    import re
+
+    def table(d, suffix):
+        for f in sorted(os.listdir(d)):
+            if f.endswith(suffix):
+                with open(os.path.join(d, f)) as fh:
+                    return list(csv.DictReader(fh))
+        raise SystemExit("no *%s under %s" % (suffix, d))
+
+    def grid_of(r):
+        return r.get("Grid_Size_X", r.get("Grid_Size"))
+
+    durations = collections.OrderedDict()
+    for r in table(trace_dir, "kernel_trace.csv"):
+        key = (r["Kernel_Name"], str(grid_of(r)))
+        durations.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+
+    def counter(d):
+        agg = collections.OrderedDict()
+        for r in table(d, "counter_collection.csv"):
+            agg.setdefault((r["Kernel_Name"], str(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return agg
+
+    fetch, write = counter(fetch_dir), counter(write_dir)
+    copy_bytes = 256 << 20
+    cal_f = max(max(v) for v in fetch.values())
+    cal_w = max(max(v) for v in write.values())
+    f_scale, w_scale = copy_bytes / (cal_f * 1024), copy_bytes / (cal_w * 1024)
+    cmd_t = ("rocprofv3 --kernel-trace --stats -f csv -d %s -o trace -- python3 bench.py --profile %d"
+             % (trace_dir, calls_trace))
+    cmd_f = ("rocprofv3 --pmc FETCH_SIZE -f csv -d %s -o fetch -- python3 bench.py --profile %d"
+             % (fetch_dir, calls_pmc))
+    cmd_w = ("rocprofv3 --pmc WRITE_SIZE -f csv -d %s -o write -- python3 bench.py --profile %d"
+             % (write_dir, calls_pmc))
+    lines = ["# GEMM kernels on MI355X: rocprofv3 kernel trace and HBM counters", "",
+             "Kernel durations (end minus start timestamp of each dispatch): `%s`" % cmd_t, "",
+             "Counters, one per run: `%s` and `%s`" % (cmd_f, cmd_w), "",
+             "Calibration: the 256 MiB device copy that `--profile` runs first reads FETCH_SIZE = %.0f KiB and "
+             "WRITE_SIZE = %.0f KiB per dispatch, so FETCH_SIZE is scaled by %.3f and WRITE_SIZE by %.3f to "
+             "bytes." % (cal_f, cal_w, f_scale, w_scale), "",
+             "`--profile` runs, per workload in order: the weight pack (one dispatch, large grid), then the "
+             "calls of mx_gemm over rotating buffer copies (>= 1 GiB working set).", "",
+             "| kernel | grid (threads) | dispatches | avg us | median us | min us | FETCH bytes | WRITE bytes |",
+             "|---|---|---|---|---|---|---|---|"]
+    per_launch = collections.OrderedDict()
+    for (name, grid), ds in durations.items():
+        if "mx4::" not in name:
+            continue
+        fb = statistics.median(fetch[(name, grid)]) * 1024 * f_scale if (name, grid) in fetch else None
+        wb = statistics.median(write[(name, grid)]) * 1024 * w_scale if (name, grid) in write else None
+        short = re.sub(r"\(.*", "", name).replace("void ", "")
+        lines.append("| `%s` | %s | %d | %.3f | %.3f | %.3f | %s | %s |" % (
+            short, grid, len(ds), statistics.mean(ds), statistics.median(ds), min(ds),
+            "%.0f" % fb if fb is not None else "-", "%.0f" % wb if wb is not None else "-"))
+        if short.startswith("mx4::gemm_kernel") and len(ds) > 1:
+            per_launch[(short, grid)] = (statistics.mean(ds), fb, wb)
+    from microscaled_mxfp4_block_amd import inputs
+    gemms = list(per_launch.items())
+    traffic = {"kernel_source_hash": kernel_source_hash(),
+               "source": "profiles/gemm_kernels_trace.md: FETCH_SIZE and WRITE_SIZE passes over python3 bench.py "
+                         "--profile %d, scaled by their reading on a 256 MiB device copy (x%.3f, x%.3f)"
+                         % (calls_pmc, f_scale, w_scale),
+               "workloads": {}}
+    if len(gemms) == len(inputs.WORKLOADS):
+        for w, ((short, grid), (avg, fb, wb)) in zip(inputs.WORKLOADS, gemms):
+            traffic["workloads"][w.name] = {
+                "kernel": short, "grid": int(grid), "avg_us": round(avg, 3),
+                "fetch_bytes": None if fb is None else round(fb),
+                "write_bytes": None if wb is None else round(wb),
+                "hbm_bytes_per_launch": None if fb is None or wb is None else round(fb + wb)}
+    out = os.path.join(ROOT, "profiles")
+    with open(os.path.join(out, "gemm_kernels_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(out, "gemm_traffic.json"), "w") as f:
+        json.dump(traffic, f, indent=1)
+        f.write("\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,7 +279,14 @@ def main():
     ap.add_argument("--profile", type=int, default=0, metavar="CALLS",
                     help="no timing: a 256 MiB device copy (counter calibration), then CALLS cold mx_gemm "
                          "calls per workload, for running under rocprofv3")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: summarise rocprofv3 output of --profile runs into profiles/")
+    ap.add_argument("--summarize-calls", nargs=2, type=int, default=[200, 20], metavar=("TRACE", "PMC"),
+                    help="the --profile CALLS of the trace and of the counter runs being summarised")
     args = ap.parse_args()
+    if args.summarize:
+        summarize_profiles(*args.summarize, *args.summarize_calls)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode (run with --gpus 1)",
               file=sys.stderr)
@@ -190,6 +311,7 @@ def main():
         steps = args.steps if idx == HEADLINE else max(200, args.steps // 4)
         e2e_cold, gpu_cold = time_loop(torch, st, steps, args.warmup)
         e2e_hot, gpu_hot = time_loop(torch, st, steps, args.warmup, rotate=False)
+        gpu_graph = graph_loop(torch, st)
         nbytes = algorithmic_bytes(w.M, w.N, w.K)
         flops = 2.0 * w.M * w.N * w.K
         rec = {
@@ -197,6 +319,7 @@ def main():
             "launches_per_call": 1 + (st.plan["amode"] == 1) + (1 if st.plan["splits"] > 1 and not st.plan["finish"] else 0),
             "us_per_call_e2e_cold": round(e2e_cold, 3), "us_per_call_e2e_hot": round(e2e_hot, 3),
             "gpu_us_cold": round(gpu_cold, 3), "gpu_us_hot": round(gpu_hot, 3),
+            "gpu_us_graph_replay": round(gpu_graph, 3),
             "algorithmic_bytes": nbytes, "gbps_cold": round(nbytes / gpu_cold / 1e3, 1),
             "hbm_frac_cold": round(nbytes / gpu_cold / 1e3 / HBM_PEAK_GBS, 4),
             "tflops_cold": round(flops / gpu_cold / 1e6, 2),
