@@ -139,6 +139,37 @@ def graph_loop(torch, st, ncap=100, reps=20):
     return e0.elapsed_time(e1) * 1e3 / (reps * ncap)
 
 
+def launch_floor(torch, ncap=100, reps=20):
+    """What any kernel costs on this GPU, replayed from a HIP graph so that the
+    host is out of the loop: a near-empty kernel (torch's one-cycle sleep)
+    and a plain 1 MiB device copy over rotating buffers."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    n = 1 << 20
+    src = [torch.ones(n, dtype=torch.uint8, device="cuda:0") for _ in range(ncap)]
+    dst = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(ncap)]
+    torch.cuda.synchronize()
+    out = {}
+    for name, body in (("empty_kernel_us", lambda i: torch.cuda._sleep(1)),
+                       ("copy_1MiB_us", lambda i: dst[i].copy_(src[i]))):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(ncap):
+                body(i)
+        with torch.cuda.stream(s):
+            g.replay()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(reps):
+                g.replay()
+            e1.record(s)
+        torch.cuda.synchronize()
+        out[name] = round(e0.elapsed_time(e1) * 1e3 / (reps * ncap), 3)
+    out["method"] = "HIP graph of %d launches replayed %d times, HIP events on the replay stream" % (ncap, reps)
+    return out
+
+
 def cpu_baseline(idx, inputs, seconds=10.0):
     """The oracle (C, fp64 accumulation, OpenMP over N) on the host cores:
     quantise A + dequantise + GEMM per call; B is quantised and dequantised
@@ -364,6 +395,7 @@ def main():
             "bytes_per_launch": nbytes,
         },
         "per_workload": per_workload,
+        "launch_floor": launch_floor(torch),
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(HEADLINE, inputs)
