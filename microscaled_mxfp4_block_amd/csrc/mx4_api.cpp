@@ -46,7 +46,7 @@ const TableEntry kTable[] = {
     {4, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
     {32, 4096, 512, {1, 1, 1, 4, 1, 2, 0}},
     {32, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
-    {16, 2112, 7168, {1, 1, 2, 4, 7, 0, 0}},
+    {16, 2112, 7168, {1, 2, 1, 8, 7, 2, 0}},
     {64, 7168, 2048, {1, 1, 2, 4, 1, 1, 0}},
     {256, 3072, 1536, {1, 1, 1, 4, 1, 1, 0}},
 };
@@ -84,7 +84,8 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     if (mx4::gemm_lds_bytes(plan, l.steps_per_split) > mx4::kLdsBudget) return MX_EPLAN;
     l.mtiles = (ga.RB + plan.mb - 1) / plan.mb;
     l.ntiles = (gb.RB + plan.nb * plan.wn - 1) / (plan.nb * plan.wn);
-    if ((long long)l.mtiles * l.ntiles * l.splits >= (1LL << 31)) return MX_EINVAL;
+    // grid (N tiles, M tiles, splits): y and z are 16-bit
+    if (l.mtiles > 65535 || l.splits > 65535 || l.ntiles > (1 << 30)) return MX_EINVAL;
     if (plan.finish != 0 && plan.finish != 1) return MX_EPLAN;
     if (plan.finish == 1 && l.splits > 1 && (long long)l.mtiles * l.ntiles > mx4::kMaxCounters) return MX_EPLAN;
     l.aop_bytes = plan.amode == kAmPrequant ? round_up(ga.total_bytes, 256) : 0;

@@ -43,14 +43,11 @@
 
 namespace mx4 {
 
-// Workgroups are dispatched round-robin over the 8 XCDs (blockIdx i runs on
-// XCD i % 8).  Remap so that consecutive logical tile indices share an XCD:
-// the M tiles that read the same weight tiles, placed next to each other,
-// then share one L2.
-__device__ __forceinline__ int xcd_linear(int i, int G) {
-    const int q = G / 8, r = G % 8, x = i % 8;
-    return x * q + (x < r ? x : r) + i / 8;
-}
+// The grid is (N tiles, M tiles, K splits), so the tile indices come straight
+// from the workgroup-id SGPRs, with no division.  Workgroups are dispatched
+// round-robin over the 8 XCDs by their linear index x + X (y + Y z): when the
+// number of N tiles X is a multiple of 8, every M tile of one N tile runs on
+// the same XCD, and the M tiles that read the same weight tile share one L2.
 
 // LDS of the WK-reduction buffer and of the staged bf16 output tile.
 __host__ __device__ constexpr size_t gemm_red_bytes(int wn, int wk, int mb, int nb) {
@@ -107,11 +104,9 @@ gemm_kernel(GemmParams p) {
     const int wkk = wave / WN;
 
     // ---- tile of this workgroup
-    const int lin = xcd_linear(blockIdx.x, gridDim.x);
-    const int mt = lin % p.mtiles;
-    const int rest = lin / p.mtiles;
-    const int split = rest % p.splits;
-    const int nt = rest / p.splits;
+    const int nt = blockIdx.x;
+    const int mt = blockIdx.y;
+    const int split = blockIdx.z;
     const int mb0 = mt * MBLK;
     const int nb0 = (nt * WN + wn) * NBLK;   // first n block of this wave
     const int tb = split * p.steps_per_split;
@@ -287,7 +282,7 @@ gemm_kernel(GemmParams p) {
     const bool partial = p.splits > 1;
     const bool finish_here = partial && p.counters != nullptr;
     __shared__ uint32_t last_arrival;
-    if constexpr (FUSED || WK > 1) __syncthreads();   // every wave is done with the activation operand
+    if constexpr (FUSED) __syncthreads();   // every wave is done with the activation operand in LDS
     if constexpr (WK > 1) {
 #pragma unroll
         for (int i = 0; i < MBLK; ++i)
@@ -535,9 +530,9 @@ hipError_t launch_gemm(const Plan& plan, const GemmParams& p, hipStream_t s) {
     const int per_wave = (p.steps_per_split + plan.wk - 1) / plan.wk;
     GemmFn fn = find_kernel(plan, gemm_kr_for(per_wave));
     if (!fn) return hipErrorInvalidValue;
-    const long long grid = (long long)p.mtiles * p.ntiles * p.splits;
     const size_t lds = gemm_lds_bytes(plan, p.steps_per_split);
-    hipLaunchKernelGGL(fn, dim3((unsigned)grid), dim3(64 * plan.wn * plan.wk), lds, s, p);
+    hipLaunchKernelGGL(fn, dim3((unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits),
+                       dim3(64 * plan.wn * plan.wk), lds, s, p);
     return hipGetLastError();
 }
 
