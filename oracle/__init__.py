@@ -9,6 +9,8 @@ module only builds it with gcc when needed and marshals numpy arrays.  The
 rule it follows is the MXFP4 quantisation of the kernelindex.com amd-mxfp4-mm
 pages (submission 755056, section "Software MXFP4 quant"), the dequantisation
 (-1)^sign * e2m1 * 2^(byte-127), and C = bf16_RNE(fp64 sum of products).
+``gemm`` quantises both operands; ``gemm_a16w4`` is the pages' a16wfp4
+product, which leaves A in bf16 and quantises only B.
 
 Pins (tests marked ``not gpu``): hand-worked groups under ``tests/golden``,
 an independent exact pure-Python brute force (``oracle.bruteforce``), closed
@@ -57,6 +59,8 @@ def _load():
         lib.mxo_scale_byte.restype = I
         lib.mxo_decode.argtypes = [I, I]
         lib.mxo_decode.restype = ctypes.c_double
+        lib.mxo_bf16_to_double.argtypes = [P, ctypes.c_longlong, P]
+        lib.mxo_bf16_to_double.restype = I
         lib.mxo_bf16_from_double.argtypes = [ctypes.c_double]
         lib.mxo_bf16_from_double.restype = ctypes.c_uint16
         lib.mxo_num_threads.argtypes = []
@@ -112,6 +116,23 @@ def gemm(A_bf16: np.ndarray, B_bf16: np.ndarray) -> np.ndarray:
     ca, sa = quant(A_bf16)
     cb, sb = quant(B_bf16)
     return gemm_dequantised(dequant(ca, sa), dequant(cb, sb))
+
+
+def bf16_values(x_bf16: np.ndarray) -> np.ndarray:
+    """Exact fp64 values of bf16 bits (any shape)."""
+    x = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    out = np.zeros(x.shape, np.float64)
+    _load().mxo_bf16_to_double(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def gemm_a16w4(A_bf16: np.ndarray, B_bf16: np.ndarray) -> np.ndarray:
+    """The a16wfp4 product (routing notes of submission 733989: bf16 A times
+    fp4 B, no activation quantisation): A's bf16 values as they are, B
+    quantised and dequantised by the rule above, the fp64 sum rounded once to
+    bf16; bits [M, N]."""
+    cb, sb = quant(B_bf16)
+    return gemm_dequantised(bf16_values(A_bf16), dequant(cb, sb))
 
 
 def e2m1_code(q: float) -> int:

@@ -124,6 +124,16 @@ def bf16_round(x: Fraction) -> int:
     return sign | (f32 >> 16)
 
 
+def gemm_a16w4(A_bits, B_bits):
+    """C = bf16(exact sum_k A[m,k] deqB[n,k]) with A's bf16 values unquantised."""
+    cb, sb = quant_rows(B_bits)
+    K = len(A_bits[0])
+    Av = [[bf16_bits_to_fraction(a) for a in row] for row in A_bits]
+    Bd = [[decode(cb[n][k], sb[n][k // 32]) for k in range(K)] for n in range(len(B_bits))]
+    return [[bf16_round(sum((a * b for a, b in zip(Av[m], Bd[n])), Fraction(0))) for n in range(len(Bd))]
+            for m in range(len(Av))]
+
+
 def gemm(A_bits, B_bits):
     """C = bf16(exact sum_k deqA[m,k] deqB[n,k]); A_bits [M][K], B_bits [N][K]."""
     ca, sa = quant_rows(A_bits)

@@ -179,6 +179,14 @@ int mxo_gemm_dequantised(const double* Ad, const double* Bd, int M, int N, int K
     return 0;
 }
 
+/* Exact fp64 values of n bf16 bit patterns (a bf16 is the upper half of an
+ * fp32, so the widening is exact). */
+int mxo_bf16_to_double(const uint16_t* x, long long n, double* out) {
+    if (n < 0) return -1;
+    for (long long i = 0; i < n; ++i) out[i] = (double)bf16_to_float(x[i]);
+    return 0;
+}
+
 /* Number of OpenMP threads the GEMM loop uses (1 without OpenMP). */
 int mxo_num_threads(void) {
 #ifdef _OPENMP

@@ -294,3 +294,72 @@ def test_bf16_rounding_random_against_exact():
 
 def test_oracle_is_built_with_threads():
     assert oracle.num_threads() >= 1
+
+
+# ---------------------------------------------------------------------------
+# The a16wfp4 product (A unquantised bf16, B quantised): oracle.gemm_a16w4
+
+
+def test_bf16_values_every_finite_pattern():
+    """The exact widening of every finite bf16 pattern, against the rational
+    decoding of the brute force."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    vals = oracle.bf16_values(bits)
+    for h, v in zip(bits[finite][::97], vals[finite][::97]):
+        assert Fraction(float(v)) == bf.bf16_bits_to_fraction(int(h)), hex(int(h))
+    assert np.array_equal(np.signbit(vals[finite]), (bits[finite] & 0x8000) != 0)
+
+
+@pytest.mark.parametrize("case", ["randn", "binades", "tiny_and_huge"])
+def test_bruteforce_a16w4_4x64x64(case):
+    M, N, K = 4, 64, 64
+    if case == "randn":
+        A, B = inputs.shape_inputs(M, N, K, seed=15)
+    elif case == "binades":
+        A = inputs.binade_spread(M, K, seed=16, lo=-12, hi=12)
+        B = inputs.binade_spread(N, K, seed=17, lo=-12, hi=12)
+    else:
+        A = inputs.binade_spread(M, K, seed=18, lo=-120, hi=-100)
+        B = inputs.binade_spread(N, K, seed=19, lo=90, hi=110)
+    Ab, Bb = inputs.bits(A), inputs.bits(B)
+    C = oracle.gemm_a16w4(Ab, Bb)
+    Cb = bf.gemm_a16w4([list(map(int, r)) for r in Ab], [list(map(int, r)) for r in Bb])
+    assert [list(map(int, r)) for r in C] == Cb
+
+
+def test_a16w4_equals_a4w4_when_A_is_representable():
+    """Quantisation is the identity on MXFP4-representable A, so both products agree."""
+    M, N, K = 8, 40, 256
+    Ab, _, _, _ = representable(M, K, 5)
+    B = inputs.binade_spread(N, K, seed=21, lo=-8, hi=8)
+    Bb = inputs.bits(B)
+    np.testing.assert_array_equal(oracle.gemm_a16w4(Ab, Bb), oracle.gemm(Ab, Bb))
+
+
+def test_a16w4_differs_from_a4w4_on_general_A():
+    """On N(0,1) activations the two products are different functions (the
+    activation's quantisation error is not in a16w4)."""
+    A, B = inputs.shape_inputs(8, 64, 512, seed=22)
+    Ab, Bb = inputs.bits(A), inputs.bits(B)
+    assert np.mean(oracle.gemm_a16w4(Ab, Bb) != oracle.gemm(Ab, Bb)) > 0.5
+
+
+def test_a16w4_closed_form_representable_B_is_textbook_matmul():
+    """With B representable, dequant(quant(B)) = B and the product is the
+    textbook matmul of the two bf16 matrices, rounded once (the fp64 sum is
+    exact at these magnitudes: 11-bit products over ~30 binades)."""
+    M, N, K = 6, 24, 256
+    A, _ = inputs.shape_inputs(M, 8, K, seed=23)
+    Ab = inputs.bits(A)
+    Bb, _, _, Bv = representable(N, K, 24)
+    ref = A.float().double().numpy() @ Bv.T
+    want = np.array([[bf.bf16_round(Fraction(float(v))) for v in row] for row in ref], np.uint16)
+    np.testing.assert_array_equal(oracle.gemm_a16w4(Ab, Bb), want)
+
+
+def test_a16w4_all_ones():
+    for K in (512, 7168):
+        A = np.full((2, K), 0x3F80, np.uint16)
+        B = np.full((3, K), 0x3F80, np.uint16)
+        assert np.all(oracle.gemm_a16w4(A, B) == oracle.bf16_from_double(float(K)))
