@@ -143,8 +143,10 @@ enum {
     MX_AMODE_LDS = 0,       /* each GEMM workgroup quantises its slice of A into
                                LDS, shared by its waves */
     MX_AMODE_PREQUANT = 1,  /* a first kernel quantises A into the workspace */
-    MX_AMODE_DIRECT = 2     /* each wave quantises the A fragments it consumes
+    MX_AMODE_DIRECT = 2,    /* each wave quantises the A fragments it consumes
                                in registers (no LDS, no barrier) */
+    MX_AMODE_BF16 = 3       /* A is NOT quantised: the a16wfp4 product of
+                               mx_gemm_a16w4 (a different result) */
 };
 
 /* Split-K finishes of a plan (no effect when splits == 1). */
@@ -167,6 +169,20 @@ int mx_gemm_with_plan(const void* A_dev, int M, int K, int lda,
                       void* C_dev, int ldc,
                       void* ws_dev, size_t ws_bytes,
                       const mx_plan* plan_host, void* stream);
+
+/* The a16wfp4 product (the pages' route for small M: submission 733989,
+ * routing notes, "bf16 A x fp4 B"): C = A x dequant(B)^T with A's bf16
+ * values used as they are, B packed by mx_pack_weight (or imported), fp32
+ * accumulation of exact bf16 x bf16 products on bf16 MFMAs, bf16
+ * round-to-nearest-even.  This is a different function from mx_gemm, which
+ * also quantises A.  Arguments, alignment, workspace rules and return codes
+ * are those of mx_gemm; the plan has amode MX_AMODE_BF16. */
+int mx_gemm_a16w4_plan(int M, int N, int K, mx_plan* plan_host);
+int mx_gemm_a16w4_workspace_bytes(int M, int N, int K, size_t* bytes_host);
+int mx_gemm_a16w4(const void* A_dev, int M, int K, int lda,
+                  const void* packed_dev, int N,
+                  void* C_dev, int ldc,
+                  void* ws_dev, size_t ws_bytes, void* stream);
 
 #ifdef __cplusplus
 }

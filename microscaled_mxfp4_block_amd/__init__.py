@@ -7,6 +7,7 @@ The Python names mirror the C entry points (see ``binding``); the HIP library
 from .binding import (  # noqa: F401
     MxError,
     mx_gemm,
+    mx_gemm_a16w4,
     mx_gemm_plan,
     mx_gemm_workspace_bytes,
     mx_import_weight,

@@ -25,6 +25,7 @@ MX_EPLAN = -5
 MX_AMODE_LDS = 0
 MX_AMODE_PREQUANT = 1
 MX_AMODE_DIRECT = 2
+MX_AMODE_BF16 = 3          # A not quantised: the a16wfp4 product
 # split-K finishes of a plan
 MX_FINISH_KERNEL = 0
 MX_FINISH_LAST_ARRIVAL = 1
@@ -33,6 +34,7 @@ EXPORTS = [
     "mx_strerror", "mx_packed_weight_bytes", "mx_pack_weight", "mx_unpack_weight",
     "mx_import_weight", "mx_quant_act", "mx_gemm_workspace_bytes", "mx_gemm", "mx_gemm_plan",
     "mx_gemm_plan_workspace_bytes", "mx_gemm_with_plan",
+    "mx_gemm_a16w4_plan", "mx_gemm_a16w4_workspace_bytes", "mx_gemm_a16w4",
 ]
 
 
@@ -87,6 +89,9 @@ def lib() -> ctypes.CDLL:
         L.mx_gemm_plan.argtypes = [I, I, I, PP]
         L.mx_gemm_plan_workspace_bytes.argtypes = [PP, I, I, I, PS]
         L.mx_gemm_with_plan.argtypes = [P, I, I, I, P, I, P, I, P, S, PP, P]
+        L.mx_gemm_a16w4_plan.argtypes = [I, I, I, PP]
+        L.mx_gemm_a16w4_workspace_bytes.argtypes = [I, I, I, PS]
+        L.mx_gemm_a16w4.argtypes = [P, I, I, I, P, I, P, I, P, S, P]
         for name in EXPORTS[1:]:
             getattr(L, name).restype = I
         _lib = L
@@ -216,4 +221,34 @@ def mx_gemm(A: torch.Tensor, packed: torch.Tensor, N: int, C: Optional[torch.Ten
                                   plan["wk"], plan["splits"], plan["amode"],
                                   plan.get("finish", MX_FINISH_KERNEL), s)
     _check(rc, "mx_gemm")
+    return C
+
+
+def mx_gemm_a16w4_plan(M: int, N: int, K: int) -> dict:
+    p = MxPlan()
+    _check(lib().mx_gemm_a16w4_plan(M, N, K, ctypes.byref(p)), "mx_gemm_a16w4_plan")
+    return p.as_dict()
+
+
+def mx_gemm_a16w4_workspace_bytes(M: int, N: int, K: int) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().mx_gemm_a16w4_workspace_bytes(M, N, K, ctypes.byref(out)), "mx_gemm_a16w4_workspace_bytes")
+    return out.value
+
+
+def mx_gemm_a16w4(A: torch.Tensor, packed: torch.Tensor, N: int, C: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """C[M, N] (bf16) = A x dequant(B)^T with A left in bf16 (the a16wfp4 product)."""
+    M, K, lda = _bf16_matrix(A, "A")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    Mc, Nc, ldc = _bf16_matrix(C, "C")
+    if (Mc, Nc) != (M, N):
+        raise ValueError("C must be [%d, %d]" % (M, N))
+    if workspace is None:
+        workspace = torch.zeros(max(mx_gemm_a16w4_workspace_bytes(M, N, K), 256), dtype=torch.uint8,
+                                device=A.device)
+    rc = ext().gemm_a16w4(A.data_ptr(), M, K, lda, packed.data_ptr(), N, C.data_ptr(), ldc, workspace.data_ptr(),
+                          workspace.numel(), _stream(stream))
+    _check(rc, "mx_gemm_a16w4")
     return C

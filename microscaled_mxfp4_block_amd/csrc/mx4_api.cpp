@@ -14,10 +14,12 @@
 using mx4::GemmParams;
 using mx4::OperandGeom;
 using mx4::Plan;
+using mx4::kAmBf16;
 using mx4::kAmDirect;
 using mx4::kAmLds;
 using mx4::kAmPrequant;
-static_assert(kAmLds == MX_AMODE_LDS && kAmPrequant == MX_AMODE_PREQUANT && kAmDirect == MX_AMODE_DIRECT,
+static_assert(kAmLds == MX_AMODE_LDS && kAmPrequant == MX_AMODE_PREQUANT && kAmDirect == MX_AMODE_DIRECT &&
+                  kAmBf16 == MX_AMODE_BF16,
               "activation modes of the C ABI and the kernels differ");
 
 namespace {
@@ -77,10 +79,17 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     l.steps_per_split = (gb.KS + plan.splits - 1) / plan.splits;
     l.splits = (gb.KS + l.steps_per_split - 1) / l.steps_per_split;  // every split non-empty
     if ((l.steps_per_split + plan.wk - 1) / plan.wk > mx4::kStepsPerWaveMax) return MX_EPLAN;
-    // kAmDirect holds the raw bf16 of every fragment of the wave (16 VGPRs per
-    // K step and m block) while the weight loads are in flight: at most 128.
-    if (plan.amode == kAmDirect && plan.mb * mx4::gemm_kr_for((l.steps_per_split + plan.wk - 1) / plan.wk) > 8)
-        return MX_EPLAN;
+    // Register budget (no plan may run a kernel that spills).  kAmDirect and
+    // kAmBf16 hold the raw bf16 of every fragment of the wave (16 VGPRs per K
+    // step and m block) while the weight loads are in flight: at most 128.
+    // A 16-wave workgroup leaves each wave 128 VGPRs in all: half that again.
+    {
+        const int kr = mx4::gemm_kr_for((l.steps_per_split + plan.wk - 1) / plan.wk);
+        const bool rega = plan.amode == kAmDirect || plan.amode == kAmBf16;
+        const bool waves16 = plan.wn * plan.wk == 16;
+        if (rega && plan.mb * kr > (waves16 ? 4 : 8)) return MX_EPLAN;
+        if (!rega && waves16 && plan.mb * plan.nb * kr > 8) return MX_EPLAN;
+    }
     if (mx4::gemm_lds_bytes(plan, l.steps_per_split) > mx4::kLdsBudget) return MX_EPLAN;
     l.mtiles = (ga.RB + plan.mb - 1) / plan.mb;
     l.ntiles = (gb.RB + plan.nb * plan.wn - 1) / (plan.nb * plan.wn);
@@ -131,6 +140,19 @@ Plan choose_plan(int M, int N, int K) {
     for (const TableEntry& e : kTable)
         if (e.M == M && e.N == N && e.K == K) return e.plan;
     return model_plan(M, N, K);
+}
+
+// The a16wfp4 product reuses the tiling of the MXFP4 plan with A left in
+// bf16: one 32-row M block per wave (the raw A registers), then the fewest
+// splits that fit the register budget.
+Plan choose_plan_a16w4(int M, int N, int K) {
+    Plan p = choose_plan(M, N, K);
+    p.amode = kAmBf16;
+    p.mb = 1;
+    const OperandGeom gb = mx4::operand_geom(N, K);
+    Layout l;
+    while (p.splits < gb.KS && plan_layout(p, M, N, K, &l) != MX_OK) ++p.splits;
+    return p;
 }
 
 int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, void* C, int ldc, void* ws,
@@ -309,6 +331,33 @@ int mx_gemm_with_plan(const void* A_dev, int M, int K, int lda, const void* pack
 int mx_gemm(const void* A_dev, int M, int K, int lda, const void* packed_dev, int N, void* C_dev, int ldc,
             void* ws_dev, size_t ws_bytes, void* stream) {
     return gemm_impl(A_dev, M, K, lda, packed_dev, N, C_dev, ldc, ws_dev, ws_bytes, choose_plan(M, N, K), stream);
+}
+
+int mx_gemm_a16w4_plan(int M, int N, int K, mx_plan* plan_host) {
+    if (!plan_host) return MX_EALIGN;
+    int rc = check_operand_shape(M, K);
+    if (rc) return rc;
+    rc = check_operand_shape(N, K);
+    if (rc) return rc;
+    const Plan p = choose_plan_a16w4(M, N, K);
+    Layout lay;
+    rc = plan_layout(p, M, N, K, &lay);
+    if (rc) return rc;
+    *plan_host = mx_plan{p.mb, p.nb, p.wn, p.wk, lay.splits, p.amode, p.finish};
+    return MX_OK;
+}
+
+int mx_gemm_a16w4_workspace_bytes(int M, int N, int K, size_t* bytes_host) {
+    mx_plan p;
+    int rc = mx_gemm_a16w4_plan(M, N, K, &p);
+    if (rc) return rc;
+    return mx_gemm_plan_workspace_bytes(&p, M, N, K, bytes_host);
+}
+
+int mx_gemm_a16w4(const void* A_dev, int M, int K, int lda, const void* packed_dev, int N, void* C_dev, int ldc,
+                  void* ws_dev, size_t ws_bytes, void* stream) {
+    return gemm_impl(A_dev, M, K, lda, packed_dev, N, C_dev, ldc, ws_dev, ws_bytes, choose_plan_a16w4(M, N, K),
+                     stream);
 }
 
 }  // extern "C"

@@ -14,6 +14,7 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 // ---------------------------------------------------------------------------
 // MXFP4 group scale (rule of the kernelindex.com amd-mxfp4-mm pages,
@@ -98,6 +99,23 @@ __device__ __forceinline__ f32x16 mfma_fp4_32x32x64(const u32x4& a, const u32x4&
     i32x8 vb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, 4, 4, 0, (int)scale_a, 0,
                                                            (int)scale_b);
+}
+
+// Eight e2m1 codes (one dword, element 0 in the low nibble) widened to bf16
+// times the scale operand 2^s by the gfx950 fp4 convert.  The product is
+// exact in bf16 (a subnormal below 2^-126) for every scale byte the rule
+// makes (s <= 126), except 4 * 2^126 and 6 * 2^126, past bf16's range.
+__device__ __forceinline__ bf16x8 widen8_fp4(uint32_t codes, float sc) {
+    const bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 0);
+    const bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 1);
+    const bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 2);
+    const bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, sc, 3);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+// One bf16 MFMA over 16 K: acc += a x b^T, each operand one lane's 8 bf16.
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(const bf16x8& a, const bf16x8& b, f32x16 acc) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
 }
 
 // 32 wait states after an MFMA whose result is read next: more than the

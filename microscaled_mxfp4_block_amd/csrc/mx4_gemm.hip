@@ -26,7 +26,12 @@
 //      kAmDirect  every lane loads the 32 bf16 of exactly the fragment it
 //                 feeds to the MFMA (one row, one 32-element group) and
 //                 quantises it in registers: no LDS, no barrier; waves with
-//                 the same m rows and K steps each quantise them.
+//                 the same m rows and K steps each quantise them;
+//      kAmBf16    the a16wfp4 product of the pages (submission 733989,
+//                 routing notes): A is not quantised.  Lanes load A as in
+//                 kAmDirect; the weight codes are widened to bf16 times
+//                 their e8m0 scale by the gfx950 fp4 convert (exact) and
+//                 the step runs as four bf16 MFMAs (32x32x16).
 //   3. K loop: MFMAs on registers (and 16-byte LDS reads with kAmLds).
 //   4. The WK waves add their accumulators through LDS; the result is
 //      rounded to bf16, staged in LDS and stored in 16-byte row chunks.
@@ -94,6 +99,8 @@ gemm_kernel(GemmParams p) {
     constexpr bool FUSED = AM == kAmLds;
     constexpr bool DIRECT = AM == kAmDirect;
     constexpr bool PREQ = AM == kAmPrequant;
+    constexpr bool BF16A = AM == kAmBf16;
+    constexpr bool REGA = DIRECT || BF16A;   // activation loaded straight into registers
     constexpr int NT = 64 * WN * WK;
     const int tid = threadIdx.x;
     // wave-uniform values in SGPRs: weight and operand base addresses then
@@ -164,8 +171,8 @@ gemm_kernel(GemmParams p) {
     // 32 (mb0 + i) + L % 32, group 2 (wb + s) + L / 32; padding steps and a
     // group past K read zeros (zero codes, scale byte 0), rows past M read
     // zeros through the buffer bound.
-    u32x4 xa[DIRECT ? KR : 1][MBLK][4];
-    if constexpr (DIRECT) {
+    u32x4 xa[REGA ? KR : 1][MBLK][4];
+    if constexpr (REGA) {
         const Rsrc rx_ = make_rsrc(p.A, p.a_bytes);
 #pragma unroll
         for (int s = 0; s < KR; ++s) {
@@ -246,17 +253,36 @@ gemm_kernel(GemmParams p) {
                 as[i] = lds[16 * MBLK * T * 64 + u];
             } else if constexpr (DIRECT) {
                 as[i] = quant_group32(xa[s][i], af[i]);
+            } else if constexpr (BF16A) {
+                af[i] = u32x4{0u, 0u, 0u, 0u};   // unused: the bf16 MFMAs read xa
+                as[i] = 0u;
             } else {
                 af[i] = afrag[s][i];
                 as[i] = ascale[s][i] >> sh;
             }
         }
+        if constexpr (BF16A) {
+            // 16-K chunk c of the step: lane L's codes 8c..8c+7 (dword c of
+            // its fragment) against A elements 8c..8c+7 of the same group.
 #pragma unroll
-        for (int j = 0; j < NBLK; ++j) {
-            const uint32_t bs = bscale[s][j] >> sh;
+            for (int j = 0; j < NBLK; ++j) {
+                const float bsc = scale_operand((bscale[s][j] >> sh) & 0xFFu);
 #pragma unroll
-            for (int i = 0; i < MBLK; ++i)
-                acc[i][j] = mfma_fp4_32x32x64(bfrag[s][j], af[i], acc[i][j], bs, as[i]);
+                for (int c = 0; c < 4; ++c) {
+                    const bf16x8 bv = widen8_fp4(bfrag[s][j][c], bsc);
+#pragma unroll
+                    for (int i = 0; i < MBLK; ++i)
+                        acc[i][j] = mfma_bf16_32x32x16(bv, __builtin_bit_cast(bf16x8, xa[s][i][c]), acc[i][j]);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < NBLK; ++j) {
+                const uint32_t bs = bscale[s][j] >> sh;
+#pragma unroll
+                for (int i = 0; i < MBLK; ++i)
+                    acc[i][j] = mfma_fp4_32x32x64(bfrag[s][j], af[i], acc[i][j], bs, as[i]);
+            }
         }
     }
 
@@ -472,6 +498,7 @@ GemmFn MX4_CAT(find_gemm_kr, MX4_KR)(const Plan& plan) {
         case kAmLds: return pick_tile<kAmLds>(plan);
         case kAmPrequant: return pick_tile<kAmPrequant>(plan);
         case kAmDirect: return pick_tile<kAmDirect>(plan);
+        case kAmBf16: return pick_tile<kAmBf16>(plan);
         default: return nullptr;
     }
 }

@@ -61,6 +61,7 @@ struct Plan {
 constexpr int kAmLds = 0;        // by the workgroup, into LDS
 constexpr int kAmPrequant = 1;   // by pack_kernel, into the workspace
 constexpr int kAmDirect = 2;     // by each wave, in registers
+constexpr int kAmBf16 = 3;       // not at all: bf16 A x dequantised B (the a16wfp4 product)
 
 bool gemm_plan_supported(const Plan& p);
 int gemm_kr_for(int steps_per_wave);   // K-step budget KR of the kernel for that many steps (0: none)

@@ -78,10 +78,29 @@ static PyObject* py_gemm_with_plan(PyObject* self, PyObject* const* a, Py_ssize_
     return PyLong_FromLong(mx_gemm_with_plan(A, M, K, lda, P, N, C, ldc, W, wsb, &plan, S));
 }
 
+/* gemm_a16w4(A, M, K, lda, packed, N, C, ldc, ws, ws_bytes, stream) -> rc */
+static PyObject* py_gemm_a16w4(PyObject* self, PyObject* const* a, Py_ssize_t n) {
+    (void)self;
+    if (n != 11) {
+        PyErr_SetString(PyExc_TypeError, "gemm_a16w4 expects 11 arguments");
+        return NULL;
+    }
+    void *A, *P, *C, *W, *S;
+    int M, K, lda, N, ldc;
+    size_t wsb;
+    if (get_ptr(a[0], &A) || get_int(a[1], &M) || get_int(a[2], &K) || get_int(a[3], &lda) ||
+        get_ptr(a[4], &P) || get_int(a[5], &N) || get_ptr(a[6], &C) || get_int(a[7], &ldc) ||
+        get_ptr(a[8], &W) || get_size(a[9], &wsb) || get_ptr(a[10], &S))
+        return NULL;
+    return PyLong_FromLong(mx_gemm_a16w4(A, M, K, lda, P, N, C, ldc, W, wsb, S));
+}
+
 static PyMethodDef methods[] = {
     {"gemm", (PyCFunction)(void (*)(void))py_gemm, METH_FASTCALL, "mx_gemm; returns the MX_* code"},
     {"gemm_with_plan", (PyCFunction)(void (*)(void))py_gemm_with_plan, METH_FASTCALL,
      "mx_gemm_with_plan; returns the MX_* code"},
+    {"gemm_a16w4", (PyCFunction)(void (*)(void))py_gemm_a16w4, METH_FASTCALL,
+     "mx_gemm_a16w4; returns the MX_* code"},
     {NULL, NULL, 0, NULL},
 };
 

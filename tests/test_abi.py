@@ -157,7 +157,7 @@ def test_explicit_plan_rejections():
            dict(mb=1, nb=1, wn=1, wk=3, splits=1, amode=1),      # no such wave count
            dict(mb=1, nb=1, wn=4, wk=8, splits=4, amode=0),      # no such wave count along N
            dict(mb=1, nb=1, wn=2, wk=16, splits=4, amode=2),     # more than 16 waves
-           dict(mb=1, nb=1, wn=1, wk=4, splits=4, amode=3),      # no such activation mode
+           dict(mb=1, nb=1, wn=1, wk=4, splits=4, amode=4),      # no such activation mode
            dict(mb=1, nb=1, wn=1, wk=4, splits=4, amode=0, finish=2),   # no such split-K finish
            dict(mb=1, nb=1, wn=1, wk=4, splits=0, amode=1),
            dict(mb=1, nb=1, wn=1, wk=4, splits=1000, amode=1),   # more splits than K steps
@@ -205,3 +205,39 @@ def test_workspace_layout_reserves_counters():
         B.mx_gemm_workspace_bytes(32 * 65, 32 * 64, 512, big)
     assert e.value.code == B.MX_EPLAN
     assert B.mx_gemm_workspace_bytes(32 * 65, 32 * 64, 512, dict(big, finish=0)) > 0
+
+
+def test_planner_rejects_every_spilling_kernel():
+    """Every kernel instantiation whose gfx950 code spills VGPRs (read from the
+    build's device assembly) is refused by the planner, so no accepted plan
+    runs one."""
+    import glob
+    build = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "_build")
+    asms = glob.glob(os.path.join(build, "mx4_gemm_kr*.s"))
+    if not asms:
+        pytest.skip("no device assembly under _build (run the package build first)")
+    checked = 0
+    for path in asms:
+        kr = int(re.search(r"kr(\d+)\.s$", path).group(1))
+        text = open(path).read()
+        for block in text.split("  - .agpr_count:")[1:]:
+            name = re.search(r"\.name:\s+(\S+)", block).group(1)
+            spills = int(re.search(r"\.vgpr_spill_count:\s+(\d+)", block).group(1))
+            m = re.match(r"_ZN3mx411gemm_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E", name)
+            if not m:
+                continue
+            mb, nb, wn, wk, am, kr_t = map(int, m.groups())
+            assert kr_t == kr
+            plan = dict(mb=mb, nb=nb, wn=wn, wk=wk, splits=1, amode=am, finish=0)
+            # a shape whose single split gives each wave exactly KR steps
+            M, N, K = 32 * mb, 32 * nb * wn, 64 * kr * wk
+            try:
+                B.mx_gemm_workspace_bytes(M, N, K, plan)
+                accepted = True
+            except B.MxError as e:
+                assert e.code == B.MX_EPLAN
+                accepted = False
+            if spills:
+                assert not accepted, "planner accepts spilling kernel %s" % (plan,)
+            checked += 1
+    assert checked > 100

@@ -251,6 +251,15 @@ PLANS = [
     dict(mb=2, nb=1, wn=1, wk=16, splits=2, amode=0, finish=1),
 ]
 
+# The a16wfp4 product (amode 3) against its own oracle.
+PLANS_A16W4 = [
+    dict(mb=1, nb=1, wn=1, wk=1, splits=1, amode=3),
+    dict(mb=1, nb=1, wn=1, wk=4, splits=1, amode=3),
+    dict(mb=1, nb=2, wn=2, wk=2, splits=3, amode=3),
+    dict(mb=2, nb=1, wn=1, wk=8, splits=2, amode=3),
+    dict(mb=1, nb=1, wn=2, wk=8, splits=7, amode=3, finish=1),
+]
+
 
 def plan_id(p):
     return "mb%d_nb%d_wn%d_wk%d_s%d_a%d_f%d" % (p["mb"], p["nb"], p["wn"], p["wk"], p["splits"], p["amode"],
@@ -434,3 +443,84 @@ def test_gemm_graph_capture_replays_match_eager():
         for (M, N, K, Ad, packed, C, ws) in cases:
             eager = gpu_bits(B.mx_gemm(Ad, packed, N))
             np.testing.assert_array_equal(gpu_bits(C), eager, err_msg="replay %d shape %s" % (replay, (M, N, K)))
+
+
+
+# ---------------------------------------------------------------------------
+# a16wfp4: C = A (bf16, not quantised) x dequant(B)^T
+
+def run_a16w4(A, Bm, plan=None):
+    Ad = to_dev(A)
+    packed = B.mx_pack_weight(to_dev(Bm))
+    if plan is None:
+        C = B.mx_gemm_a16w4(Ad, packed, Bm.shape[0])
+    else:
+        C = B.mx_gemm(Ad, packed, Bm.shape[0], plan=plan)
+    return gpu_bits(C)
+
+
+@pytest.mark.parametrize("idx", range(len(inputs.WORKLOADS)), ids=[w.name for w in inputs.WORKLOADS])
+def test_a16w4_workloads_full(idx):
+    w = inputs.WORKLOADS[idx]
+    say("a16w4", w.name, B.mx_gemm_a16w4_plan(w.M, w.N, w.K))
+    A, Bm = inputs.workload_inputs(idx, 2000)
+    C = run_a16w4(A, Bm)
+    assert_c_close(C, oracle.gemm_a16w4(inputs.bits(A), inputs.bits(Bm)), "a16w4 " + w.name)
+
+
+@pytest.mark.parametrize("shape", SMALL_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_a16w4_small_shapes(shape):
+    M, N, K = shape
+    A, Bm = inputs.shape_inputs(M, N, K, seed=M + 2 * N + K)
+    C = run_a16w4(A, Bm)
+    assert_c_close(C, oracle.gemm_a16w4(inputs.bits(A), inputs.bits(Bm)), "a16w4 " + str(shape))
+
+
+@pytest.mark.parametrize("plan", PLANS_A16W4, ids=plan_id)
+@pytest.mark.parametrize("shape", [(5, 200, 320), (70, 300, 1536), (9, 70, 352)], ids=lambda s: "x".join(map(str, s)))
+def test_a16w4_explicit_plans(shape, plan):
+    M, N, K = shape
+    if not plan_runs(M, N, K, plan):
+        pytest.skip("plan outside the register / LDS budget for this shape")
+    say("a16w4 plan", shape, plan_id(plan))
+    A, Bm = inputs.shape_inputs(M, N, K, seed=31 + M + N)
+    C = run_a16w4(A, Bm, plan)
+    assert_c_close(C, oracle.gemm_a16w4(inputs.bits(A), inputs.bits(Bm)), "a16w4 " + plan_id(plan))
+
+
+@pytest.mark.parametrize("lo_a,hi_a,lo_b,hi_b", [(-20, 20, -20, 20), (-10, 10, -133, -120), (-110, -90, 80, 100)],
+                         ids=["spread", "tiny_weight", "tiny_act_huge_weight"])
+def test_a16w4_binades(lo_a, hi_a, lo_b, hi_b):
+    """Weight groups down to scale byte 0 widen to bf16 subnormals (the
+    convert must keep them); wide exponent ranges on both sides."""
+    M, N, K = 12, 96, 512
+    A = inputs.binade_spread(M, K, seed=41, lo=lo_a, hi=hi_a)
+    Bm = inputs.binade_spread(N, K, seed=42, lo=lo_b, hi=hi_b)
+    C = run_a16w4(A, Bm)
+    ref = oracle.gemm_a16w4(inputs.bits(A), inputs.bits(Bm))
+    assert np.any(ref != 0)
+    assert_c_close(C, ref, "a16w4 binades")
+
+
+def test_a16w4_representable_weight_is_exact_matmul():
+    """Integer activations in [-16, 16] against an MXFP4-representable weight
+    with scales 2^-1..2^1: every product and partial sum is a multiple of
+    1/4 below 2^13, exact in fp32, so C is bit-identical to the oracle."""
+    M, N, K = 32, 64, 64
+    rng = np.random.default_rng(45)
+    A = torch.from_numpy(rng.integers(-16, 17, (M, K)).astype(np.float32)).to(torch.bfloat16)
+    Bm = inputs.from_bits(oracle_representable(N, K))
+    C = run_a16w4(A, Bm)
+    np.testing.assert_array_equal(C, oracle.gemm_a16w4(inputs.bits(A), inputs.bits(Bm)))
+
+
+def oracle_representable(rows, K):
+    """bf16 bits of an MXFP4-representable matrix (codes and bytes chosen at
+    random, values decoded with the oracle)."""
+    rng = np.random.default_rng(44)
+    codes = rng.integers(0, 16, (rows, K)).astype(np.uint8)
+    codes[:, ::32] = 7                      # every group reaches 6 * 2^s: the rule keeps s
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    scales = rng.integers(126, 129, (rows, K // 32)).astype(np.uint8)
+    vals = oracle.dequant(packed, scales)
+    return inputs.bits(torch.from_numpy(vals).to(torch.bfloat16))
