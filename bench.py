@@ -86,6 +86,13 @@ class Setup:
         self.args = [(a.data_ptr(), w.M, w.K, w.K, p.data_ptr(), w.N, c.data_ptr(), w.N, s.data_ptr(), s.numel(),
                       stream) for a, p, c, s in zip(self.As, self.Ps, self.Cs, self.ws)]
         self.fn = B.ext().gemm   # CPython fast-call wrapper of mx_gemm
+        # the a16wfp4 product on the same buffers (context figures)
+        self.plan16 = B.mx_gemm_a16w4_plan(w.M, w.N, w.K)
+        ws16 = B.mx_gemm_a16w4_workspace_bytes(w.M, w.N, w.K)
+        self.ws16 = [torch.zeros(max(ws16, 256), dtype=torch.uint8, device=dev) for _ in range(min(self.copies, 8))]
+        self.args16 = [a[:8] + (self.ws16[i % len(self.ws16)].data_ptr(), self.ws16[0].numel(), stream)
+                       for i, a in enumerate(self.args)]
+        self.fn16 = B.ext().gemm_a16w4
         torch.cuda.synchronize()
 
     def call(self, i):
@@ -93,20 +100,26 @@ class Setup:
         if rc:
             raise RuntimeError("mx_gemm returned %d" % rc)
 
+    def call16(self, i):
+        rc = self.fn16(*self.args16[i % self.copies])
+        if rc:
+            raise RuntimeError("mx_gemm_a16w4 returned %d" % rc)
 
-def time_loop(torch, st, steps, warmup, rotate=True):
+
+def time_loop(torch, st, steps, warmup, rotate=True, call=None):
     """`steps` back-to-back mx_gemm calls between two synchronisations.
     Returns (wall-clock µs per call, event-timed µs per launch): HIP events
     recorded on the launch stream bracket the whole timed region."""
+    call = call or st.call
     for i in range(warmup):
-        st.call(i if rotate else 0)
+        call(i if rotate else 0)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
     for i in range(steps):
-        st.call(i if rotate else 0)
+        call(i if rotate else 0)
     e1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps * 1e6
@@ -231,7 +244,9 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calls_trace, calls_pmc):
         raise SystemExit("no *%s under %s" % (suffix, d))
 
     def grid_of(r):
-        return r.get("Grid_Size_X", r.get("Grid_Size"))
+        if "Grid_Size_X" in r:   # kernel trace: per dimension; counters: the product
+            return int(r["Grid_Size_X"]) * int(r.get("Grid_Size_Y", 1)) * int(r.get("Grid_Size_Z", 1))
+        return int(r["Grid_Size"])
 
     durations = collections.OrderedDict()
     for r in table(trace_dir, "kernel_trace.csv"):
@@ -241,7 +256,7 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calls_trace, calls_pmc):
     def counter(d):
         agg = collections.OrderedDict()
         for r in table(d, "counter_collection.csv"):
-            agg.setdefault((r["Kernel_Name"], str(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+            agg.setdefault((r["Kernel_Name"], str(grid_of(r))), []).append(float(r["Counter_Value"]))
         return agg
 
     fetch, write = counter(fetch_dir), counter(write_dir)
@@ -343,6 +358,7 @@ def main():
         e2e_cold, gpu_cold = time_loop(torch, st, steps, args.warmup)
         e2e_hot, gpu_hot = time_loop(torch, st, steps, args.warmup, rotate=False)
         gpu_graph = graph_loop(torch, st)
+        e2e16, gpu16 = time_loop(torch, st, max(200, steps // 4), args.warmup, call=st.call16)
         nbytes = algorithmic_bytes(w.M, w.N, w.K)
         flops = 2.0 * w.M * w.N * w.K
         rec = {
@@ -355,6 +371,8 @@ def main():
             "hbm_frac_cold": round(nbytes / gpu_cold / 1e3 / HBM_PEAK_GBS, 4),
             "tflops_cold": round(flops / gpu_cold / 1e6, 2),
             "mfma_frac_cold": round(flops / gpu_cold / 1e6 / FP4_PEAK_TFLOPS, 5),
+            "a16w4": {"note": "the a16wfp4 product (A not quantised; a different function), same buffers",
+                      "plan": st.plan16, "us_per_call_e2e_cold": round(e2e16, 3), "gpu_us_cold": round(gpu16, 3)},
         }
         per_workload[w.name] = rec
         print(json.dumps({w.name: rec}), file=sys.stderr, flush=True)

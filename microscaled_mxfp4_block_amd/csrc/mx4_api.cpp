@@ -142,10 +142,22 @@ Plan choose_plan(int M, int N, int K) {
     return model_plan(M, N, K);
 }
 
-// The a16wfp4 product reuses the tiling of the MXFP4 plan with A left in
-// bf16: one 32-row M block per wave (the raw A registers), then the fewest
-// splits that fit the register budget.
+// Plans measured for the a16wfp4 product on the same shapes.
+const TableEntry kTableA16w4[] = {
+    {4, 2880, 512, {1, 1, 1, 8, 1, 3, 0}},
+    {32, 4096, 512, {1, 1, 1, 8, 1, 3, 0}},
+    {32, 2880, 512, {1, 1, 1, 4, 1, 3, 0}},
+    {16, 2112, 7168, {1, 1, 2, 4, 7, 3, 0}},
+    {64, 7168, 2048, {1, 2, 1, 16, 1, 3, 0}},
+    {256, 3072, 1536, {2, 2, 1, 8, 1, 3, 0}},
+};
+
+// The a16wfp4 product: a measured plan, else the tiling of the MXFP4 plan
+// with A left in bf16: one 32-row M block per wave (the raw A registers),
+// then the fewest splits that fit the register budget.
 Plan choose_plan_a16w4(int M, int N, int K) {
+    for (const TableEntry& e : kTableA16w4)
+        if (e.M == M && e.N == N && e.K == K) return e.plan;
     Plan p = choose_plan(M, N, K);
     p.amode = kAmBf16;
     p.mb = 1;
