@@ -99,6 +99,7 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     if (plan.finish == 1 && l.splits > 1 && (long long)l.mtiles * l.ntiles > mx4::kMaxCounters) return MX_EPLAN;
     l.aop_bytes = plan.amode == kAmPrequant ? round_up(ga.total_bytes, 256) : 0;
     l.partial_bytes = l.splits > 1 ? round_up((size_t)l.splits * M * gb.RB * mx4::kRowBlock * sizeof(float), 256) : 0;
+    if (l.partial_bytes >= (1ull << 31)) return MX_EPLAN;   // 32-bit buffer offsets
     l.counter_bytes = (l.aop_bytes + l.partial_bytes) > 0 ? mx4::kCounterBytes : 0;
     l.aop_offset = l.counter_bytes;
     l.partial_offset = l.aop_offset + l.aop_bytes;
@@ -214,6 +215,7 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     p.ldc = ldc;
     p.c_vec = (ldc % 4 == 0 && aligned(C, 8)) ? 1 : 0;
     p.partial = lay.splits > 1 ? (float*)(wsb + lay.partial_offset) : nullptr;
+    p.partial_bytes = (uint32_t)lay.partial_bytes;
     p.ldp = gb.RB * mx4::kRowBlock;
     const bool finish_in_gemm = lay.splits > 1 && plan.finish == 1;
     p.counters = finish_in_gemm ? (uint32_t*)wsb : nullptr;

@@ -355,12 +355,14 @@ gemm_kernel(GemmParams p) {
         if (m < p.M && nb < p.RBn) {
             const float* src = p.partial + (size_t)m * p.ldp + n0;
             f32x4 acc4 = load_partial_agent(src);
-            for (int k = 1; k < p.splits; ++k) {
-                const f32x4 x = load_partial_agent(src + (size_t)k * p.M * p.ldp);
-                acc4.x += x.x;
-                acc4.y += x.y;
-                acc4.z += x.z;
-                acc4.w += x.w;
+            for (int k0 = 1; k0 < p.splits; k0 += 4) {   // 4 splits' loads in flight, then add in order
+                f32x4 x[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (k0 + q < p.splits) x[q] = load_partial_agent(src + (size_t)(k0 + q) * p.M * p.ldp);
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (k0 + q < p.splits) acc4 += x[q];
             }
             v[0] = acc4.x;
             v[1] = acc4.y;
@@ -505,22 +507,31 @@ GemmFn MX4_CAT(find_gemm_kr, MX4_KR)(const Plan& plan) {
 
 #if MX4_KR == 1
 // The split-K reduction and the launch helpers live in one object only.
+// Grid (ceil(N / 4 / 256), rows): one thread per 4 consecutive n of row m
+// (rows past 65535 are walked by the y workgroups).  The partials of each
+// batch of 8 splits are all loaded before the first add (padding splits read
+// zeros through the buffer bound), then added in split order.
+constexpr int kReduceBatch = 8;
 __global__ void __launch_bounds__(256) reduce_kernel(GemmParams p) {
-    const int n4 = (p.N + 3) / 4;
-    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    if (gid >= (long long)p.M * n4) return;
-    const int m = (int)(gid / n4);
-    const int n0 = (int)(gid % n4) * 4;
-    f32x4 s = *(const f32x4*)(p.partial + (size_t)m * p.ldp + n0);
-    for (int k = 1; k < p.splits; ++k) {
-        const f32x4 x = *(const f32x4*)(p.partial + ((size_t)k * p.M + m) * p.ldp + n0);
-        s.x += x.x;
-        s.y += x.y;
-        s.z += x.z;
-        s.w += x.w;
+    const int n0 = 4 * (int)(blockIdx.x * 256u + threadIdx.x);
+    if (n0 >= p.N) return;
+    const Rsrc rp_ = make_rsrc(p.partial, p.partial_bytes);
+    const uint32_t split_stride = (uint32_t)p.M * (uint32_t)p.ldp * 4u;
+    for (int m = blockIdx.y; m < p.M; m += gridDim.y) {
+        const uint32_t base = ((uint32_t)m * (uint32_t)p.ldp + (uint32_t)n0) * 4u;
+        f32x4 s = __builtin_bit_cast(f32x4, bload16(rp_, base, 0u));
+        for (int k0 = 1; k0 < p.splits; k0 += kReduceBatch) {
+            u32x4 x[kReduceBatch];
+#pragma unroll
+            for (int q = 0; q < kReduceBatch; ++q)
+                x[q] = bload16(rp_, k0 + q < p.splits ? base + (uint32_t)(k0 + q) * split_stride : 0x80000000u, 0u);
+#pragma unroll
+            for (int q = 0; q < kReduceBatch; ++q)
+                if (k0 + q < p.splits) s += __builtin_bit_cast(f32x4, x[q]);
+        }
+        const float v[4] = {s.x, s.y, s.z, s.w};
+        store_bf16x4(p, m, n0, v);
     }
-    const float v[4] = {s.x, s.y, s.z, s.w};
-    store_bf16x4(p, m, n0, v);
 }
 
 GemmFn find_gemm_kr2(const Plan& plan);
@@ -564,9 +575,9 @@ hipError_t launch_gemm(const Plan& plan, const GemmParams& p, hipStream_t s) {
 }
 
 hipError_t launch_reduce(const GemmParams& p, hipStream_t s) {
-    const long long total = (long long)p.M * ((p.N + 3) / 4);
-    const long long blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+    const unsigned gx = (unsigned)(((p.N + 3) / 4 + 255) / 256);
+    const unsigned gy = (unsigned)(p.M < 65535 ? p.M : 65535);
+    hipLaunchKernelGGL(reduce_kernel, dim3(gx, gy), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 #endif

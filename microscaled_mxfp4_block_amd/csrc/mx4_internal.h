@@ -45,6 +45,7 @@ struct GemmParams {
     int ldc;
     int c_vec;                // 1 when rows of C are 8-byte aligned (ldc % 4 == 0)
     float* partial;           // fp32 partials [splits, M, ldp] when splits > 1
+    uint32_t partial_bytes;   // bytes of that region (< 2^31)
     int ldp;
     uint32_t* counters;       // per-tile arrival counters (zero between calls) when the
                               // last-arriving workgroup sums the partials, else null
