@@ -65,27 +65,28 @@ __global__ void __launch_bounds__(256) quant_natural_kernel(const uint16_t* __re
 __global__ void __launch_bounds__(256) pack_kernel(const uint16_t* __restrict__ x, int rows, int K, int ld,
                                                    uint8_t* __restrict__ packed, int RB, int KS, int KW,
                                                    size_t code_bytes) {
-    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    const long long total = (long long)RB * KW * kStepsPerWord * 64;
-    if (gid >= total) return;
-    const int L = (int)(gid & 63);
-    const long long rt = gid >> 6;
-    const int t = (int)(rt % (KW * kStepsPerWord));
-    const int rb = (int)(rt / (KW * kStepsPerWord));
-    const int row = rb * kRowBlock + (L & 31);
+    // grid (ceil(KW * 4 * 64 / 256), min(RB, 65535)): slot (t, L) from x with
+    // 32-bit math, row blocks rb from y (walked when there are more than 65535)
+    const int slot = (int)(blockIdx.x * 256u + threadIdx.x);
+    if (slot >= KW * kStepsPerWord * 64) return;
+    const int L = slot & 63;
+    const int t = slot >> 6;
     const int g = 2 * t + (L >> 5);
-    u32x4 codes = {0u, 0u, 0u, 0u};
-    uint32_t byte = 0u;
-    if (row < rows && g < K / kGroup) {
-        const uint16_t* src = x + (size_t)row * ld + (size_t)g * kGroup;
-        u32x4 v[4];
+    for (int rb = (int)blockIdx.y; rb < RB; rb += (int)gridDim.y) {
+        const int row = rb * kRowBlock + (L & 31);
+        u32x4 codes = {0u, 0u, 0u, 0u};
+        uint32_t byte = 0u;
+        if (row < rows && g < K / kGroup) {
+            const uint16_t* src = x + (size_t)row * ld + (size_t)g * kGroup;
+            u32x4 v[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = load16(src + 8 * i);
-        byte = quant_group32(v, codes);
+            for (int i = 0; i < 4; ++i) v[i] = load16(src + 8 * i);
+            byte = quant_group32(v, codes);
+        }
+        // steps past KS exist only as padding bytes of the last scale word
+        if (t < KS) *(u32x4*)(packed + ((size_t)(rb * KS + t) * 64 + L) * 16) = codes;
+        packed[code_bytes + ((size_t)(rb * KW + t / kStepsPerWord) * 64 + L) * 4 + t % kStepsPerWord] = (uint8_t)byte;
     }
-    // steps past KS exist only as padding bytes of the last scale word
-    if (t < KS) *(u32x4*)(packed + ((size_t)(rb * KS + t) * 64 + L) * 16) = codes;
-    packed[code_bytes + ((size_t)(rb * KW + t / kStepsPerWord) * 64 + L) * 4 + t % kStepsPerWord] = (uint8_t)byte;
 }
 
 // Packed layout -> natural layouts.  One lane per (rb, t, L) tile slot.
@@ -145,10 +146,10 @@ hipError_t launch_quant_natural(const uint16_t* x, int rows, int K, int ld, uint
 
 hipError_t launch_pack(const uint16_t* x, int rows, int K, int ld, uint8_t* packed, hipStream_t s) {
     const OperandGeom g = operand_geom(rows, K);
-    const long long total = (long long)g.RB * g.KW * kStepsPerWord * 64;
-    const long long blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, K, ld, packed, g.RB, g.KS,
-                       g.KW, g.code_bytes);
+    const unsigned gx = (unsigned)((g.KW * kStepsPerWord * 64 + 255) / 256);
+    const unsigned gy = (unsigned)(g.RB < 65535 ? g.RB : 65535);
+    hipLaunchKernelGGL(pack_kernel, dim3(gx, gy), dim3(256), 0, s, x, rows, K, ld, packed, g.RB, g.KS, g.KW,
+                       g.code_bytes);
     return hipGetLastError();
 }
 

@@ -241,3 +241,12 @@ def test_planner_rejects_every_spilling_kernel():
                 assert not accepted, "planner accepts spilling kernel %s" % (plan,)
             checked += 1
     assert checked > 100
+
+
+def test_shapes_past_the_addressing_limit_are_refused():
+    """rows * K * 2 >= 2^31 for an operand (32-bit buffer offsets) is refused
+    before any launch; just below it is accepted."""
+    with pytest.raises(B.MxError) as e:
+        B.mx_gemm_workspace_bytes(1, 32768, 32768)
+    assert e.value.code == B.MX_EINVAL
+    assert B.mx_gemm_workspace_bytes(64, 32768, 32736) > 0

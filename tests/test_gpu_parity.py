@@ -524,3 +524,42 @@ def oracle_representable(rows, K):
     scales = rng.integers(126, 129, (rows, K // 32)).astype(np.uint8)
     vals = oracle.dequant(packed, scales)
     return inputs.bits(torch.from_numpy(vals).to(torch.bfloat16))
+
+
+# ---------------------------------------------------------------------------
+# Sizes at the 32-bit addressing limits (rows * K * 2 < 2^31 per operand),
+# checked on sampled outputs the oracle computes one row / column at a time.
+
+def gpu_randn_bf16(rows, cols, seed, scale=1.0):
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    return (torch.randn(rows, cols, generator=g, device=DEV, dtype=torch.float32) * scale).to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("M,N,K,sample", [
+    (64, 32768, 32736, "n"),     # a 1 GiB bf16 weight (rows * K just under 2^30), K % 64 == 32
+    (32768, 512, 1024, "m"),     # a 64 MiB activation, many M tiles
+    (32, 32, 1 << 22, "all"),    # K = 4M: 65536 K steps, 1024 splits
+    (1, 16384, 65504, "n"),      # one row against a 2 GiB-limit weight
+], ids=["bigN", "bigM", "bigK", "m1_bigNK"])
+def test_gemm_limit_sizes_sampled(M, N, K, sample):
+    say("limit size", (M, N, K), B.mx_gemm_plan(M, N, K))
+    Ad = gpu_randn_bf16(M, K, seed=M + K)
+    Bd = gpu_randn_bf16(N, K, seed=N + 7 * K)
+    packed = B.mx_pack_weight(Bd)
+    C = B.mx_gemm(Ad, packed, N)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(M + N + K)
+    if sample == "n":
+        cols = np.sort(rng.choice(N, size=min(N, 48), replace=False))
+        ref = oracle.gemm(inputs.bits(Ad.cpu()), inputs.bits(Bd[torch.from_numpy(cols).to(DEV)].cpu()))
+        got = inputs.bits(C[:, torch.from_numpy(cols).to(DEV)].cpu())
+    elif sample == "m":
+        rows = np.sort(rng.choice(M, size=min(M, 48), replace=False))
+        ref = oracle.gemm(inputs.bits(Ad[torch.from_numpy(rows).to(DEV)].cpu()), inputs.bits(Bd.cpu()))
+        got = inputs.bits(C[torch.from_numpy(rows).to(DEV)].cpu())
+    else:
+        ref = oracle.gemm(inputs.bits(Ad.cpu()), inputs.bits(Bd.cpu()))
+        got = inputs.bits(C.cpu())
+    assert_c_close(got, ref, "limit size %s" % ((M, N, K),))
+    del Ad, Bd, packed, C
+    torch.cuda.empty_cache()
