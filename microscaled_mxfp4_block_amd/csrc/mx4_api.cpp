@@ -45,11 +45,11 @@ struct TableEntry {
     Plan plan;   // mb, nb, wn, wk, splits, amode, finish
 };
 const TableEntry kTable[] = {
-    {4, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
-    {32, 4096, 512, {1, 1, 1, 4, 1, 2, 0}},
-    {32, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
-    {16, 2112, 7168, {1, 2, 1, 8, 7, 2, 0}},
-    {64, 7168, 2048, {1, 1, 2, 4, 1, 1, 0}},
+    {4, 2880, 512, {1, 1, 1, 8, 1, 2, 0}},
+    {32, 4096, 512, {1, 1, 1, 8, 1, 2, 0}},
+    {32, 2880, 512, {1, 1, 1, 8, 1, 2, 0}},
+    {16, 2112, 7168, {1, 1, 1, 4, 7, 2, 0}},
+    {64, 7168, 2048, {1, 2, 1, 16, 1, 2, 0}},
     {256, 3072, 1536, {1, 1, 1, 4, 1, 1, 0}},
 };
 
@@ -109,10 +109,10 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 }
 
 // Model for shapes without a table entry: quantise A inside the GEMM (each
-// wave its own fragments, in registers) while the activation slice of a
-// workgroup is small next to the weight it meets, else in a first kernel;
-// two 32-row M blocks per wave when M allows, one
-// N block per wave, 8 waves along K (fewer for short K); then the fewest K
+// wave its own fragments) up to 128 rows of A, where re-quantising it per
+// workgroup still costs less than a second launch; beyond that in a first
+// kernel, with two 32-row M blocks per wave when M allows; one N block per
+// wave, 8 waves along K (fewer for short K); then the fewest K
 // splits that keep every wave within its register budget and the activation
 // slice within LDS, doubled while the tiles leave most of the 256 CUs idle
 // and the fp32 partials stay small next to the weight.
@@ -120,7 +120,7 @@ Plan model_plan(int M, int N, int K) {
     const OperandGeom ga = mx4::operand_geom(M, K);
     const OperandGeom gb = mx4::operand_geom(N, K);
     Plan p;
-    p.amode = (ga.RB > 1 || gb.KS > 16) ? kAmPrequant : kAmDirect;
+    p.amode = ga.RB > 4 ? kAmPrequant : kAmDirect;
     p.mb = (p.amode == kAmPrequant && ga.RB >= 2) ? 2 : 1;
     p.nb = 1;
     p.wn = 1;
@@ -145,12 +145,12 @@ Plan choose_plan(int M, int N, int K) {
 
 // Plans measured for the a16wfp4 product on the same shapes.
 const TableEntry kTableA16w4[] = {
-    {4, 2880, 512, {1, 1, 1, 8, 1, 3, 0}},
+    {4, 2880, 512, {1, 1, 1, 4, 1, 3, 0}},
     {32, 4096, 512, {1, 1, 1, 8, 1, 3, 0}},
-    {32, 2880, 512, {1, 1, 1, 4, 1, 3, 0}},
-    {16, 2112, 7168, {1, 1, 2, 4, 7, 3, 0}},
-    {64, 7168, 2048, {1, 2, 1, 16, 1, 3, 0}},
-    {256, 3072, 1536, {2, 2, 1, 8, 1, 3, 0}},
+    {32, 2880, 512, {1, 1, 1, 8, 1, 3, 0}},
+    {16, 2112, 7168, {1, 1, 1, 8, 7, 3, 0}},
+    {64, 7168, 2048, {1, 1, 2, 4, 1, 3, 0}},
+    {256, 3072, 1536, {1, 2, 2, 8, 1, 3, 0}},
 };
 
 // The a16wfp4 product: a measured plan, else the tiling of the MXFP4 plan

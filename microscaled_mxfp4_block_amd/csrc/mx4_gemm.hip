@@ -54,6 +54,19 @@ namespace mx4 {
 // number of N tiles X is a multiple of 8, every M tile of one N tile runs on
 // the same XCD, and the M tiles that read the same weight tile share one L2.
 
+// The activation of kAmDirect / kAmBf16 arrives coalesced: each wave loads its
+// 32-row x 64-K bf16 tiles a whole 128-byte row segment per 8 lanes into a
+// per-wave LDS slab (rows padded to 144 bytes), then every lane reads back
+// the 64 bytes of the fragment it quantises.  One wave writes and reads its
+// own slab, so LDS ordering within the wave is all the synchronisation; the
+// slab holds two K steps at a time and is reused for the next two.  The slabs
+// share LDS with the epilogue's buffers, behind a barrier.
+constexpr int kSlabRow = 144;
+__host__ __device__ constexpr int slab_steps(int kr) { return kr < 2 ? kr : 2; }
+__host__ __device__ constexpr size_t gemm_slab_bytes(int waves, int mb, int kr) {
+    return (size_t)waves * mb * slab_steps(kr) * kRowBlock * kSlabRow;
+}
+
 // LDS of the WK-reduction buffer and of the staged bf16 output tile.
 __host__ __device__ constexpr size_t gemm_red_bytes(int wn, int wk, int mb, int nb) {
     return wk > 1 ? (size_t)wn * wk * mb * nb * 16 * 64 * 4 : 0;
@@ -173,17 +186,25 @@ gemm_kernel(GemmParams p) {
     // zeros through the buffer bound.
     u32x4 xa[REGA ? KR : 1][MBLK][4];
     if constexpr (REGA) {
+        // coalesced: chunk q of lane L is row (64 q + L) / 8 of the tile,
+        // 16-byte column (64 q + L) % 8 of its 128-byte K segment
         const Rsrc rx_ = make_rsrc(p.A, p.a_bytes);
 #pragma unroll
         for (int s = 0; s < KR; ++s) {
-            const int g = 2 * (wb + s) + (L >> 5);
-            const bool live = s < nsteps && g < G;
 #pragma unroll
             for (int i = 0; i < MBLK; ++i) {
-                const int row = (mb0 + i) * kRowBlock + (L & 31);
-                const uint32_t off = live ? (uint32_t)row * (uint32_t)p.lda * 2u + (uint32_t)g * 64u : kOutOfRange;
 #pragma unroll
-                for (int c = 0; c < 4; ++c) xa[s][i][c] = bload16(rx_, off + 16u * c, 0u);
+                for (int q = 0; q < 4; ++q) {
+                    const int c = q * 64 + L;
+                    const int r = c >> 3, col = c & 7;
+                    const int g = 2 * (wb + s) + (col >> 2);
+                    const bool live = s < nsteps && g < G;
+                    const int row = (mb0 + i) * kRowBlock + r;
+                    const uint32_t off = live ? (uint32_t)row * (uint32_t)p.lda * 2u + (uint32_t)(wb + s) * 128u +
+                                                    (uint32_t)col * 16u
+                                              : kOutOfRange;
+                    xa[s][i][q] = bload16(rx_, off, 0u);
+                }
             }
         }
     }
@@ -229,6 +250,35 @@ gemm_kernel(GemmParams p) {
         __syncthreads();
     }
 
+    // ---- 2b. (kAmDirect / kAmBf16) the coalesced activation chunks go through
+    // this wave's LDS slab into fragment order: lane L then holds the 64 bytes
+    // of row 32 (mb0 + i) + L % 32, group 2 (wb + s) + L / 32.
+    if constexpr (REGA) {
+        constexpr int SR = slab_steps(KR);
+        uint8_t* slab = lds + (size_t)wave * (MBLK * SR * kRowBlock * kSlabRow);
+#pragma unroll
+        for (int s0 = 0; s0 < KR; s0 += SR) {
+#pragma unroll
+            for (int ds = 0; ds < SR; ++ds)
+#pragma unroll
+                for (int i = 0; i < MBLK; ++i)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int c = q * 64 + L;
+                        *(u32x4*)(slab + ((i * SR + ds) * kRowBlock + (c >> 3)) * kSlabRow + (c & 7) * 16) =
+                            xa[s0 + ds][i][q];
+                    }
+#pragma unroll
+            for (int ds = 0; ds < SR; ++ds)
+#pragma unroll
+                for (int i = 0; i < MBLK; ++i)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        xa[s0 + ds][i][c] = *(const u32x4*)(slab + ((i * SR + ds) * kRowBlock + (L & 31)) * kSlabRow +
+                                                            (L >> 5) * 64 + c * 16);
+        }
+    }
+
     // ---- 3. K loop over the wave's steps
     f32x16 acc[MBLK][NBLK];
 #pragma unroll
@@ -252,7 +302,7 @@ gemm_kernel(GemmParams p) {
                 af[i] = on ? a : u32x4{0u, 0u, 0u, 0u};
                 as[i] = lds[16 * MBLK * T * 64 + u];
             } else if constexpr (DIRECT) {
-                as[i] = quant_group32(xa[s][i], af[i]);
+                as[i] = quant_group32(xa[s][i], af[i]);   // xa already in fragment order (see the slab pass)
             } else if constexpr (BF16A) {
                 af[i] = u32x4{0u, 0u, 0u, 0u};   // unused: the bf16 MFMAs read xa
                 as[i] = 0u;
@@ -308,7 +358,7 @@ gemm_kernel(GemmParams p) {
     const bool partial = p.splits > 1;
     const bool finish_here = partial && p.counters != nullptr;
     __shared__ uint32_t last_arrival;
-    if constexpr (FUSED) __syncthreads();   // every wave is done with the activation operand in LDS
+    if constexpr (FUSED || REGA) __syncthreads();   // every wave is done with the activation in LDS
     if constexpr (WK > 1) {
 #pragma unroll
         for (int i = 0; i < MBLK; ++i)
@@ -556,7 +606,12 @@ static GemmFn find_kernel(const Plan& plan, int kr) {
 
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
     const size_t a_op = plan.amode == kAmLds ? (size_t)plan.mb * steps_per_split * 64 * 17 : 0;
-    const size_t out = gemm_red_bytes(plan.wn, plan.wk, plan.mb, plan.nb) + gemm_stage_bytes(plan.wn, plan.mb, plan.nb);
+    size_t out = gemm_red_bytes(plan.wn, plan.wk, plan.mb, plan.nb) + gemm_stage_bytes(plan.wn, plan.mb, plan.nb);
+    if (plan.amode == kAmDirect || plan.amode == kAmBf16) {   // the slabs alias the epilogue's buffers
+        const size_t slab =
+            gemm_slab_bytes(plan.wn * plan.wk, plan.mb, gemm_kr_for((steps_per_split + plan.wk - 1) / plan.wk));
+        out = slab > out ? slab : out;
+    }
     return a_op > out ? a_op : out;
 }
 

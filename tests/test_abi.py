@@ -137,12 +137,21 @@ def test_plans_for_workloads():
         assert p["mb"] in (1, 2) and p["nb"] in (1, 2) and p["wn"] in (1, 2)
         assert p["amode"] in (B.MX_AMODE_LDS, B.MX_AMODE_PREQUANT, B.MX_AMODE_DIRECT)
         assert p["finish"] in (B.MX_FINISH_KERNEL, B.MX_FINISH_LAST_ARRIVAL)
-        assert p["wk"] in (1, 2, 4, 8) and p["wn"] * p["wk"] <= 16 and p["splits"] >= 1
+        assert p["wk"] in (1, 2, 4, 8, 16) and p["wn"] * p["wk"] <= 16 and p["splits"] >= 1
         ws = B.mx_gemm_workspace_bytes(w.M, w.N, w.K)
         if p["splits"] == 1 and p["amode"] != B.MX_AMODE_PREQUANT:
             assert ws == 0
         else:
             assert ws > 0
+
+
+def test_measured_plans_are_accepted():
+    """Every plan of the measured tables (both products, all shapes) passes
+    the planner's register, LDS and grid checks."""
+    from microscaled_mxfp4_block_amd.inputs import EXTRA_WORKLOADS
+    for w in list(WORKLOADS) + list(EXTRA_WORKLOADS):
+        for plan in (B.mx_gemm_plan(w.M, w.N, w.K), B.mx_gemm_a16w4_plan(w.M, w.N, w.K)):
+            assert B.mx_gemm_workspace_bytes(w.M, w.N, w.K, plan) >= 0
 
 
 def test_plan_model_for_other_shapes():
