@@ -106,20 +106,27 @@ class Setup:
             raise RuntimeError("mx_gemm_a16w4 returned %d" % rc)
 
 
-def time_loop(torch, st, steps, warmup, rotate=True, call=None):
+def time_loop(torch, st, steps, warmup, rotate=True, a16w4=False):
     """`steps` back-to-back mx_gemm calls between two synchronisations.
     Returns (wall-clock µs per call, event-timed µs per launch): HIP events
-    recorded on the launch stream bracket the whole timed region."""
-    call = call or st.call
-    for i in range(warmup):
-        call(i if rotate else 0)
+    recorded on the launch stream bracket the whole timed region.  The
+    argument tuples of the calls (rotating buffer copies) are listed before
+    the region; each call goes through the fast-call wrapper and its return
+    code is checked."""
+    fn, args = (st.fn16, st.args16) if a16w4 else (st.fn, st.args)
+    seq = [args[i % st.copies if rotate else 0] for i in range(max(steps, warmup))]
+    for a in seq[:warmup]:
+        if fn(*a):
+            raise RuntimeError("mx_gemm failed")
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    seq = seq[:steps]
     t0 = time.perf_counter()
     e0.record()
-    for i in range(steps):
-        call(i if rotate else 0)
+    for a in seq:
+        if fn(*a):
+            raise RuntimeError("mx_gemm failed")
     e1.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / steps * 1e6
@@ -358,7 +365,7 @@ def main():
         e2e_cold, gpu_cold = time_loop(torch, st, steps, args.warmup)
         e2e_hot, gpu_hot = time_loop(torch, st, steps, args.warmup, rotate=False)
         gpu_graph = graph_loop(torch, st)
-        e2e16, gpu16 = time_loop(torch, st, max(200, steps // 4), args.warmup, call=st.call16)
+        e2e16, gpu16 = time_loop(torch, st, max(200, steps // 4), args.warmup, a16w4=True)
         nbytes = algorithmic_bytes(w.M, w.N, w.K)
         flops = 2.0 * w.M * w.N * w.K
         rec = {

@@ -168,36 +168,50 @@ Plan choose_plan_a16w4(int M, int N, int K) {
     return p;
 }
 
-int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, void* C, int ldc, void* ws,
-              size_t ws_bytes, const Plan& plan, void* stream) {
+// Everything of a call that depends on the shape and plan only: checked
+// once, then kept in a small per-thread cache, so that a repeated call only
+// checks its pointers, patches them into the parameter block and launches.
+struct Prepared {
+    int M, N, K, lda, ldc;
+    Plan plan;
+    Layout lay;
+    GemmParams p;            // pointer fields left null
+    mx4::GemmLaunch gl;
+    bool finish_in_gemm;
+};
+
+bool same_key(const Prepared& e, int M, int N, int K, int lda, int ldc, const Plan& pl) {
+    return e.M == M && e.N == N && e.K == K && e.lda == lda && e.ldc == ldc && e.plan.mb == pl.mb &&
+           e.plan.nb == pl.nb && e.plan.wn == pl.wn && e.plan.wk == pl.wk && e.plan.splits == pl.splits &&
+           e.plan.amode == pl.amode && e.plan.finish == pl.finish;
+}
+
+int prepare(int M, int N, int K, int lda, int ldc, const Plan& plan, Prepared* out) {
     int rc = check_operand_shape(M, K);
     if (rc) return rc;
     rc = check_operand_shape(N, K);
     if (rc) return rc;
     if (lda < K || lda % 8 != 0 || ldc < N) return MX_EINVAL;
     if ((unsigned long long)M * lda * 2 >= (1ULL << 31)) return MX_EINVAL;
-    if (!aligned(A, 16) || !aligned(packed, 16) || !aligned(C, 2)) return MX_EALIGN;
     Layout lay;
     rc = plan_layout(plan, M, N, K, &lay);
     if (rc) return rc;
-    if (lay.total > 0) {
-        if (!aligned(ws, 256)) return MX_EALIGN;
-        if (ws_bytes < lay.total) return MX_ESPACE;
-    }
     const OperandGeom ga = mx4::operand_geom(M, K);
     const OperandGeom gb = mx4::operand_geom(N, K);
-    uint8_t* wsb = (uint8_t*)ws;
-    hipStream_t s = (hipStream_t)stream;
-
-    GemmParams p;
-    memset(&p, 0, sizeof p);
-    p.A = (const uint16_t*)A;
+    Prepared e;
+    memset(&e, 0, sizeof e);
+    e.M = M;
+    e.N = N;
+    e.K = K;
+    e.lda = lda;
+    e.ldc = ldc;
+    e.plan = plan;
+    e.lay = lay;
+    GemmParams& p = e.p;
     p.lda = lda;
     p.a_bytes = (uint32_t)((size_t)M * lda * 2);
-    p.aop = plan.amode == kAmPrequant ? wsb + lay.aop_offset : nullptr;
     p.aop_bytes = (uint32_t)ga.total_bytes;
     p.a_code_bytes = (uint32_t)ga.code_bytes;
-    p.bp = (const uint8_t*)packed;
     p.bp_bytes = (uint32_t)gb.total_bytes;
     p.b_code_bytes = (uint32_t)gb.code_bytes;
     p.KS = gb.KS;
@@ -211,24 +225,64 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     p.ntiles = lay.ntiles;
     p.splits = lay.splits;
     p.steps_per_split = lay.steps_per_split;
-    p.C = (uint16_t*)C;
     p.ldc = ldc;
-    p.c_vec = (ldc % 4 == 0 && aligned(C, 8)) ? 1 : 0;
-    p.partial = lay.splits > 1 ? (float*)(wsb + lay.partial_offset) : nullptr;
     p.partial_bytes = (uint32_t)lay.partial_bytes;
     p.ldp = gb.RB * mx4::kRowBlock;
-    const bool finish_in_gemm = lay.splits > 1 && plan.finish == 1;
-    p.counters = finish_in_gemm ? (uint32_t*)wsb : nullptr;
+    e.finish_in_gemm = lay.splits > 1 && plan.finish == 1;
+    Plan run = plan;
+    run.splits = lay.splits;
+    if (!mx4::resolve_gemm(run, p, &e.gl)) return MX_EPLAN;
+    *out = e;
+    return MX_OK;
+}
 
+constexpr int kPreparedCache = 4;
+thread_local Prepared tl_prepared[kPreparedCache];
+thread_local int tl_prepared_count = 0, tl_prepared_next = 0;
+
+int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, void* C, int ldc, void* ws,
+              size_t ws_bytes, const Plan& plan, void* stream) {
+    const Prepared* e = nullptr;
+    for (int i = 0; i < tl_prepared_count; ++i)
+        if (same_key(tl_prepared[i], M, N, K, lda, ldc, plan)) {
+            e = &tl_prepared[i];
+            break;
+        }
+    if (!e) {
+        Prepared fresh;
+        const int rc = prepare(M, N, K, lda, ldc, plan, &fresh);
+        if (rc) return rc;
+        Prepared& slot = tl_prepared[tl_prepared_next];
+        slot = fresh;
+        tl_prepared_next = (tl_prepared_next + 1) % kPreparedCache;
+        if (tl_prepared_count < kPreparedCache) ++tl_prepared_count;
+        e = &slot;
+    }
+    if (!aligned(A, 16) || !aligned(packed, 16) || !aligned(C, 2)) return MX_EALIGN;
+    const Layout& lay = e->lay;
+    if (lay.total > 0) {
+        if (!aligned(ws, 256)) return MX_EALIGN;
+        if (ws_bytes < lay.total) return MX_ESPACE;
+    }
+    uint8_t* wsb = (uint8_t*)ws;
+    hipStream_t s = (hipStream_t)stream;
+    GemmParams p = e->p;
+    p.A = (const uint16_t*)A;
+    p.aop = plan.amode == kAmPrequant ? wsb + lay.aop_offset : nullptr;
+    p.bp = (const uint8_t*)packed;
+    p.C = (uint16_t*)C;
+    p.c_vec = (ldc % 4 == 0 && aligned(C, 8)) ? 1 : 0;
+    p.partial = lay.splits > 1 ? (float*)(wsb + lay.partial_offset) : nullptr;
+    p.counters = e->finish_in_gemm ? (uint32_t*)wsb : nullptr;
+
+    int rc;
     if (plan.amode == kAmPrequant) {
         rc = hip_status(mx4::launch_pack((const uint16_t*)A, M, K, lda, wsb + lay.aop_offset, s));
         if (rc) return rc;
     }
-    Plan run = plan;
-    run.splits = lay.splits;
-    rc = hip_status(mx4::launch_gemm(run, p, s));
+    rc = hip_status(mx4::launch_gemm(e->gl, p, s));
     if (rc) return rc;
-    if (lay.splits > 1 && !finish_in_gemm) rc = hip_status(mx4::launch_reduce(p, s));
+    if (lay.splits > 1 && !e->finish_in_gemm) rc = hip_status(mx4::launch_reduce(p, s));
     return rc;
 }
 

@@ -619,13 +619,17 @@ bool gemm_plan_supported(const Plan& plan) {
     return plan.splits >= 1 && find_kernel(plan, 1) != nullptr;
 }
 
-hipError_t launch_gemm(const Plan& plan, const GemmParams& p, hipStream_t s) {
+bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
     const int per_wave = (p.steps_per_split + plan.wk - 1) / plan.wk;
     GemmFn fn = find_kernel(plan, gemm_kr_for(per_wave));
-    if (!fn) return hipErrorInvalidValue;
-    const size_t lds = gemm_lds_bytes(plan, p.steps_per_split);
-    hipLaunchKernelGGL(fn, dim3((unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits),
-                       dim3(64 * plan.wn * plan.wk), lds, s, p);
+    if (!fn) return false;
+    *out = GemmLaunch{fn, (unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits, (unsigned)(64 * plan.wn * plan.wk),
+                      gemm_lds_bytes(plan, p.steps_per_split)};
+    return true;
+}
+
+hipError_t launch_gemm(const GemmLaunch& gl, const GemmParams& p, hipStream_t s) {
+    hipLaunchKernelGGL(gl.fn, dim3(gl.gx, gl.gy, gl.gz), dim3(gl.block), gl.lds, s, p);
     return hipGetLastError();
 }
 

@@ -67,7 +67,14 @@ constexpr int kAmBf16 = 3;       // not at all: bf16 A x dequantised B (the a16w
 bool gemm_plan_supported(const Plan& p);
 int gemm_kr_for(int steps_per_wave);   // K-step budget KR of the kernel for that many steps (0: none)
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split);
-hipError_t launch_gemm(const Plan& plan, const GemmParams& p, hipStream_t s);
+// A resolved GEMM launch: kernel, grid, block and dynamic LDS for a plan.
+struct GemmLaunch {
+    void (*fn)(GemmParams);
+    unsigned gx, gy, gz, block;
+    size_t lds;
+};
+bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out);
+hipError_t launch_gemm(const GemmLaunch& gl, const GemmParams& p, hipStream_t s);
 hipError_t launch_reduce(const GemmParams& p, hipStream_t s);
 
 hipError_t launch_quant_natural(const uint16_t* x, int rows, int K, int ld, uint8_t* codes, uint8_t* scales,

@@ -1,7 +1,8 @@
 // mx4_quant.hip -- MXFP4 quantisation kernels for gfx950.
 //
 //   quant_natural_kernel : bf16 [rows, K] -> codes [rows, K/2] + scales [rows, K/32]
-//   pack_kernel          : bf16 [rows, K] -> packed operand layout (mx4_layout.h);
+//   pack_kernel          : bf16 [rows, K] -> packed operand layout (mx4_layout.h),
+//                          coalesced row loads, one DPP quad per group;
 //                          used once for the weight B and per call for A
 //   unpack_kernel        : packed operand layout -> natural codes + scales
 //   import_kernel        : natural codes + scales (already quantised elsewhere)
@@ -19,73 +20,68 @@
 
 namespace mx4 {
 
-// Natural-layout quantiser.  One lane per 8 consecutive bf16 (one 16-byte
-// load); the four lanes of a DPP quad hold one 32-element group and reduce
-// its amax across the quad with two lane swaps.  Each lane writes its 8 codes
-// as one dword; the first lane of the quad writes the scale byte.
-__global__ void __launch_bounds__(256) quant_natural_kernel(const uint16_t* __restrict__ x, int rows,
-                                                            int K, int ld, uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales) {
-    const int chunks_per_row = K / 8;
-    const long long total = (long long)rows * chunks_per_row;
-    const long long c = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-    // Every lane of a quad exists: total is a multiple of 4 (K % 32 == 0) and
-    // the grid is rounded to whole blocks of 256, so quads never straddle the end.
-    const bool live = c < total;
-    const int r = live ? (int)(c / chunks_per_row) : 0;
-    const int kc = live ? (int)(c % chunks_per_row) : 0;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (live) v = load16(x + (size_t)r * ld + (size_t)kc * 8);
-    uint32_t m = 0;
-    {
-        u16x2 a = __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu);
-        a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu));
-        a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu));
-        a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu));
-        m = a.x > a.y ? a.x : a.y;
-    }
+// One lane per 8 consecutive bf16 (one 16-byte vector); the four lanes of a
+// DPP quad hold one 32-element group and reduce its amax across the quad with
+// two lane swaps.  Returns the lane's 8 codes as one dword and the group's
+// scale byte.  Every lane of the quad must be active.
+__device__ __forceinline__ uint32_t quad_quant8(const u32x4& v, uint32_t& byte) {
+    u16x2 a = __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu);
+    a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu));
+    a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu));
+    a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu));
+    uint32_t m = a.x > a.y ? a.x : a.y;
     // quad_perm [1,0,3,2] then [2,3,0,1]: max over the four lanes of the quad
     uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false);
     m = m > o ? m : o;
     o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false);
     m = m > o ? m : o;
-    const uint32_t byte = scale_byte_from_amax16(m);
-    if (!live) return;
-    const float sc = scale_operand(byte);
-    const uint32_t q = cvt8(v.x, v.y, v.z, v.w, sc);
-    *(uint32_t*)(codes + (size_t)r * (K / 2) + (size_t)kc * 4) = q;
-    if ((kc & 3) == 0) scales[(size_t)r * (K / 32) + kc / 4] = (uint8_t)byte;
+    byte = scale_byte_from_amax16(m);
+    return cvt8(v.x, v.y, v.z, v.w, scale_operand(byte));
 }
 
-// Packed-layout quantiser.  One lane per operand slot (rb, t, L): it loads
-// the 64 bytes of row 32 rb + L % 32, group 2t + L / 32 with four 16-byte
-// loads, quantises them, writes the 16-byte code fragment to its slot (the
-// 64 lanes of a wave write one contiguous 1 KiB tile) and its scale byte into
-// byte t % 4 of the lane's scale word.  Every lane does one load round trip.
+// Natural-layout quantiser.  Grid (ceil(K / 8 / 256), min(rows, 65535)): one
+// lane per 16-byte column of a row (rows past 65535 walked by y); each lane
+// writes its 8 codes as one dword, the first lane of a quad the scale byte.
+__global__ void __launch_bounds__(256) quant_natural_kernel(const uint16_t* __restrict__ x, int rows,
+                                                            int K, int ld, uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+    const int c = (int)(blockIdx.x * 256u + threadIdx.x);
+    // whole quads leave together: K / 8 is a multiple of 4 and blocks are 256 wide
+    if (c >= K / 8) return;
+    for (int r = (int)blockIdx.y; r < rows; r += (int)gridDim.y) {
+        const u32x4 v = load16(x + (size_t)r * ld + (size_t)c * 8);
+        uint32_t byte;
+        const uint32_t q = quad_quant8(v, byte);
+        *(uint32_t*)(codes + (size_t)r * (K / 2) + (size_t)c * 4) = q;
+        if ((c & 3) == 0) scales[(size_t)r * (K / 32) + c / 4] = (uint8_t)byte;
+    }
+}
+
+// Packed-layout quantiser, coalesced.  Grid (ceil(KW * 32 / 256),
+// min(RB * 32, 65535)): one lane per 16-byte column c of row r of the operand
+// padded to RB * 32 rows and KW * 4 K steps (rows past 65535 walked by y).
+// The quad of group g = c / 4 quantises it; lane q of the quad writes dword q
+// of the 16-byte code fragment of slot (rb, t, L) = (r / 32, g / 2,
+// r % 32 + 32 (g % 2)) (mx4_layout.h), the quad's first lane the scale byte
+// into byte t % 4 of that lane's scale word.  Padding rows and groups get
+// zero codes and byte 0; steps past KS exist only as scale-word bytes.
 __global__ void __launch_bounds__(256) pack_kernel(const uint16_t* __restrict__ x, int rows, int K, int ld,
                                                    uint8_t* __restrict__ packed, int RB, int KS, int KW,
                                                    size_t code_bytes) {
-    // grid (ceil(KW * 4 * 64 / 256), min(RB, 65535)): slot (t, L) from x with
-    // 32-bit math, row blocks rb from y (walked when there are more than 65535)
-    const int slot = (int)(blockIdx.x * 256u + threadIdx.x);
-    if (slot >= KW * kStepsPerWord * 64) return;
-    const int L = slot & 63;
-    const int t = slot >> 6;
-    const int g = 2 * t + (L >> 5);
-    for (int rb = (int)blockIdx.y; rb < RB; rb += (int)gridDim.y) {
-        const int row = rb * kRowBlock + (L & 31);
-        u32x4 codes = {0u, 0u, 0u, 0u};
-        uint32_t byte = 0u;
-        if (row < rows && g < K / kGroup) {
-            const uint16_t* src = x + (size_t)row * ld + (size_t)g * kGroup;
-            u32x4 v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = load16(src + 8 * i);
-            byte = quant_group32(v, codes);
-        }
-        // steps past KS exist only as padding bytes of the last scale word
-        if (t < KS) *(u32x4*)(packed + ((size_t)(rb * KS + t) * 64 + L) * 16) = codes;
-        packed[code_bytes + ((size_t)(rb * KW + t / kStepsPerWord) * 64 + L) * 4 + t % kStepsPerWord] = (uint8_t)byte;
+    const int c = (int)(blockIdx.x * 256u + threadIdx.x);
+    if (c >= KW * 32) return;   // whole quads leave together
+    const int g = c >> 2, q = c & 3, t = g >> 1, h = g & 1;
+    const bool group_live = g < K / kGroup;
+    for (int r = (int)blockIdx.y; r < RB * kRowBlock; r += (int)gridDim.y) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (r < rows && group_live) v = load16(x + (size_t)r * ld + (size_t)c * 8);
+        uint32_t byte;
+        const uint32_t codes = quad_quant8(v, byte);
+        const int rb = r >> 5, L = (r & 31) + 32 * h;
+        if (t < KS) *(uint32_t*)(packed + ((size_t)(rb * KS + t) * 64 + L) * 16 + 4 * q) = codes;
+        if (q == 0)
+            packed[code_bytes + ((size_t)(rb * KW + t / kStepsPerWord) * 64 + L) * 4 + t % kStepsPerWord] =
+                (uint8_t)byte;
     }
 }
 
@@ -137,17 +133,16 @@ __global__ void __launch_bounds__(256) import_kernel(const uint8_t* __restrict__
 
 hipError_t launch_quant_natural(const uint16_t* x, int rows, int K, int ld, uint8_t* codes, uint8_t* scales,
                                 hipStream_t s) {
-    const long long total = (long long)rows * (K / 8);
-    const long long blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(quant_natural_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, rows, K, ld, codes,
-                       scales);
+    const unsigned gx = (unsigned)((K / 8 + 255) / 256);
+    const unsigned gy = (unsigned)(rows < 65535 ? rows : 65535);
+    hipLaunchKernelGGL(quant_natural_kernel, dim3(gx, gy), dim3(256), 0, s, x, rows, K, ld, codes, scales);
     return hipGetLastError();
 }
 
 hipError_t launch_pack(const uint16_t* x, int rows, int K, int ld, uint8_t* packed, hipStream_t s) {
     const OperandGeom g = operand_geom(rows, K);
-    const unsigned gx = (unsigned)((g.KW * kStepsPerWord * 64 + 255) / 256);
-    const unsigned gy = (unsigned)(g.RB < 65535 ? g.RB : 65535);
+    const unsigned gx = (unsigned)((g.KW * 32 + 255) / 256);
+    const unsigned gy = (unsigned)(g.RB * kRowBlock < 65535 ? g.RB * kRowBlock : 65535);
     hipLaunchKernelGGL(pack_kernel, dim3(gx, gy), dim3(256), 0, s, x, rows, K, ld, packed, g.RB, g.KS, g.KW,
                        g.code_bytes);
     return hipGetLastError();
