@@ -43,8 +43,13 @@ def build(force: bool = False) -> str:
 def _load():
     global _lib
     if _lib is None:
-        build()
-        lib = ctypes.CDLL(_LIB)
+        # MX_ORACLE_LIB names another build of mxoracle.c (the mutation tests
+        # load deliberately broken copies this way to show the pins catch them)
+        path = os.environ.get("MX_ORACLE_LIB")
+        if not path:
+            build()
+            path = _LIB
+        lib = ctypes.CDLL(path)
         P = ctypes.c_void_p
         I = ctypes.c_int
         lib.mxo_quant.argtypes = [P, I, I, I, P, P]
