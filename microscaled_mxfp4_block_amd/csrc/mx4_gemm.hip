@@ -68,8 +68,12 @@ __host__ __device__ constexpr size_t gemm_slab_bytes(int waves, int mb, int kr) 
 }
 
 // LDS of the WK-reduction buffer and of the staged bf16 output tile.
+// The reduction buffer is lane-major: each lane's mb * nb * 16 accumulators
+// contiguous, padded by 16 bytes (16-byte writes and reads without bank
+// conflicts).
+__host__ __device__ constexpr int red_lane_bytes(int mb, int nb) { return mb * nb * 16 * 4 + 16; }
 __host__ __device__ constexpr size_t gemm_red_bytes(int wn, int wk, int mb, int nb) {
-    return wk > 1 ? (size_t)wn * wk * mb * nb * 16 * 64 * 4 : 0;
+    return wk > 1 ? (size_t)wn * wk * 64 * red_lane_bytes(mb, nb) : 0;
 }
 __host__ __device__ constexpr size_t gemm_stage_bytes(int wn, int mb, int nb) {
     return (size_t)mb * kRowBlock * (nb * wn * kRowBlock + 8) * 2;
@@ -349,23 +353,31 @@ gemm_kernel(GemmParams p) {
     // n = 32 nb + 8 (e / 4) + 4 (L / 32) + e % 4.
     const int m_lane = L & 31;
     const int n_lane = 4 * (L >> 5);
-    constexpr int E = MBLK * NBLK * 16;       // accumulator floats per lane
     constexpr int TR = MBLK * kRowBlock;      // rows of the workgroup tile
     constexpr int TC = NBLK * WN * kRowBlock; // columns of the workgroup tile
     constexpr int SROW = TC + 8;              // bf16 per staged row (16-byte pad)
-    float* red = (float*)lds;
     uint16_t* stage = (uint16_t*)(lds + gemm_red_bytes(WN, WK, MBLK, NBLK));
     const bool partial = p.splits > 1;
     const bool finish_here = partial && p.counters != nullptr;
     __shared__ uint32_t last_arrival;
     if constexpr (FUSED || REGA) __syncthreads();   // every wave is done with the activation in LDS
+    constexpr int RL = red_lane_bytes(MBLK, NBLK);
+    // four consecutive accumulators (from float index idx) of lane `lane` of wave w2
+    auto red4 = [&](int w2, int lane, int idx) -> f32x4 {
+        return *(const f32x4*)(lds + (size_t)(w2 * 64 + lane) * RL + idx * 4);
+    };
     if constexpr (WK > 1) {
+        uint8_t* mine = lds + (size_t)(wave * 64 + L) * RL;
 #pragma unroll
         for (int i = 0; i < MBLK; ++i)
 #pragma unroll
             for (int j = 0; j < NBLK; ++j)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) red[((wave * E) + (i * NBLK + j) * 16 + e) * 64 + L] = acc[i][j][e];
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const f32x4 v4 = {acc[i][j][4 * e4], acc[i][j][4 * e4 + 1], acc[i][j][4 * e4 + 2],
+                                      acc[i][j][4 * e4 + 3]};
+                    *(f32x4*)(mine + ((i * NBLK + j) * 16 + 4 * e4) * 4) = v4;
+                }
         __syncthreads();
     }
     // groups of 4 consecutive n per (i, j, r); the WK waves of column wn share
@@ -437,15 +449,10 @@ gemm_kernel(GemmParams p) {
         for (int gi = wkk; gi < GPW; gi += WK) {
             const int ij = gi >> 2, r = gi & 3;
             const int i = ij / NBLK, j = ij % NBLK;
-            float v[4];
+            f32x4 s4 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                float s = 0.0f;
-#pragma unroll
-                for (int w2 = 0; w2 < WK; ++w2)
-                    s += red[(((w2 * WN + wn) * E) + (i * NBLK + j) * 16 + 4 * r + q) * 64 + L];
-                v[q] = s;
-            }
+            for (int w2 = 0; w2 < WK; ++w2) s4 += red4(w2 * WN + wn, L, (i * NBLK + j) * 16 + 4 * r);
+            const float v[4] = {s4.x, s4.y, s4.z, s4.w};
             emit(i, j, r, v);
         }
     }
