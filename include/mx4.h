@@ -29,11 +29,15 @@
  *     call returns a negative MX_E* code, enqueues nothing and writes nothing.
  *   - Device pointers read with 128-bit loads must be 16-byte aligned (bf16
  *     inputs A and B, with lda / ldb multiples of 8), the packed weight
- *     16-byte aligned, the workspace 256-byte aligned, C 2-byte aligned (rows
- *     of C that are 8-byte aligned, ldc % 4 == 0, get 8-byte stores).
+ *     16-byte aligned, the workspace 256-byte aligned, C 2-byte aligned (C is
+ *     written with 16-byte stores when it is 16-byte aligned and ldc % 8 == 0,
+ *     with narrower stores otherwise).
  *   - Inputs must be finite; NaN or Inf inputs give unspecified codes.
- *   - Calls on different streams with disjoint output buffers may run
- *     concurrently; the library holds no mutable state.
+ *   - Calls on different streams with disjoint output and workspace buffers
+ *     may run concurrently, from any threads.  The library's only state is a
+ *     small per-thread cache of prepared calls (shape, plan, kernel and grid;
+ *     no buffers), so a repeated mx_gemm call only checks its pointers and
+ *     launches.
  */
 #ifndef MX4_H
 #define MX4_H
@@ -67,8 +71,9 @@ const char* mx_strerror(int code);
  * multiple of 32 and K to a multiple of 64 with zero codes. */
 int mx_packed_weight_bytes(int N, int K, size_t* bytes_host);
 
-/* One-time weight packing (the weight side of the spec path; the rule
- * above applied to B along K, written into the GEMM's tile layout).
+/* One-time weight packing: the MXFP4 rule above applied to B along K (the
+ * weight is quantised the same way as the activation), written into the
+ * GEMM's tile layout.
  *   B_dev       bf16 [N, K], row stride ldb elements (ldb >= K, ldb % 8 == 0)
  *   packed_dev  output, packed_bytes >= mx_packed_weight_bytes(N, K), 16-B aligned */
 int mx_pack_weight(const void* B_dev, int N, int K, int ldb,
