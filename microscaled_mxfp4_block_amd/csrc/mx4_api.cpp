@@ -88,7 +88,8 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
         const bool rega = plan.amode == kAmDirect || plan.amode == kAmBf16;
         const bool waves16 = plan.wn * plan.wk == 16;
         if (rega && plan.mb * kr > (waves16 ? 4 : 8)) return MX_EPLAN;
-        if (!rega && waves16 && plan.mb * plan.nb * kr > 8) return MX_EPLAN;
+        // kAmLds also keeps a row of activation loads in flight per lane
+        if (!rega && waves16 && plan.mb * plan.nb * kr > (plan.amode == kAmLds ? 4 : 8)) return MX_EPLAN;
     }
     if (mx4::gemm_lds_bytes(plan, l.steps_per_split) > mx4::kLdsBudget) return MX_EPLAN;
     l.mtiles = (ga.RB + plan.mb - 1) / plan.mb;

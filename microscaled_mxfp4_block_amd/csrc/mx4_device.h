@@ -80,6 +80,25 @@ __device__ __forceinline__ uint32_t quant_group32(const u32x4 (&x)[4], u32x4& co
     return byte;
 }
 
+// One lane per 8 consecutive bf16 (one 16-byte vector); the four lanes of a
+// DPP quad hold one 32-element group and reduce its amax across the quad with
+// two lane swaps.  Returns the lane's 8 codes as one dword and the group's
+// scale byte.  Every lane of the quad must be active.
+__device__ __forceinline__ uint32_t quad_quant8(const u32x4& v, uint32_t& byte) {
+    u16x2 a = __builtin_bit_cast(u16x2, v.x & 0x7FFF7FFFu);
+    a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.y & 0x7FFF7FFFu));
+    a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.z & 0x7FFF7FFFu));
+    a = __builtin_elementwise_max(a, __builtin_bit_cast(u16x2, v.w & 0x7FFF7FFFu));
+    uint32_t m = a.x > a.y ? a.x : a.y;
+    // quad_perm [1,0,3,2] then [2,3,0,1]: max over the four lanes of the quad
+    uint32_t o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0xB1, 0xF, 0xF, false);
+    m = m > o ? m : o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)m, 0x4E, 0xF, 0xF, false);
+    m = m > o ? m : o;
+    byte = scale_byte_from_amax16(m);
+    return cvt8(v.x, v.y, v.z, v.w, scale_operand(byte));
+}
+
 // fp32 -> bf16 bits, round to nearest even (finite inputs).
 __device__ __forceinline__ uint32_t bf16_rne(float f) {
     uint32_t u = __float_as_uint(f);

@@ -144,45 +144,63 @@ gemm_kernel(GemmParams p) {
     // the same straight-line code for every wave.
     constexpr uint32_t kOutOfRange = 0x80000000u;
 
-    // ---- 1. operand loads.  With FUSED, the bf16 activation loads of the
-    // first quantisation pass go out first: loads complete in issue order,
-    // so the quantisation can start while the weight is still in flight.
-    // Activation slot u = (mb * T + tl) * 64 + lane of the workgroup's LDS
-    // operand holds row 32 (mb0 + mb) + lane % 32, group 2 (tb + tl) +
-    // lane / 32 (MFMA lane order).  Rows past M read as zero through the
-    // buffer bound and quantise to zero codes with scale byte 0; a group past
-    // K (K % 64 == 32) is zeroed explicitly.
-    constexpr int QREG = 2;   // activation slots per thread whose loads are issued together
+    // ---- 1. operand loads.  kAmLds: the workgroup streams its activation
+    // slice (rows 32 mb0 .. 32 (mb0 + MBLK) - 1, K steps tb .. te - 1) a row
+    // at a time: wave w takes slice rows w, w + NW, ..., lane l the 16-byte
+    // chunks l, l + 64, ... of the row (8 chunks per K step), so each load
+    // instruction reads 1 KB of a row.  A DPP quad holds one 32-element group;
+    // each lane writes its 8 codes as dword q of the group's slot
+    // (i T + t) 64 + row % 32 + 32 (group % 2) of the LDS operand (MFMA lane
+    // order), the quad's first lane the scale byte.  The first batch of rows
+    // is loaded before the weight: loads complete in issue order, so the
+    // quantisation starts while the weight is still in flight.  Rows past M
+    // read as zero through the buffer bound (zero codes, scale byte 0); a
+    // group past K (K % 64 == 32) is zeroed explicitly.
     const int slots = MBLK * T * 64;
     const int G = p.K / kGroup;
-    u32x4 x[QREG][4];
-    auto load_slots = [&](int u0) {
+    constexpr int NW = NT / 64;                       // waves of the workgroup
+    constexpr int RPW = MBLK * kRowBlock / NW;        // slice rows per wave
+    constexpr int CPLM = (WK * KR + 7) / 8;           // most 16-byte chunks per lane per row
+    constexpr int BR = (16 / CPLM) < 1 ? 1 : ((16 / CPLM) < RPW ? 16 / CPLM : RPW);   // rows per batch
+    const int cpr = 8 * T;                            // 16-byte chunks per slice row
+    u32x4 xs[FUSED ? BR : 1][FUSED ? CPLM : 1];
+    auto slice_load = [&](int j0) {                   // rows j0 .. j0 + BR - 1 of this wave
         const Rsrc rx_ = make_rsrc(p.A, p.a_bytes);
 #pragma unroll
-        for (int q = 0; q < QREG; ++q) {
-            const int u = u0 + q * NT + tid;
-            const int lane = u & 63, mtl = u >> 6;
-            const int row = (mb0 + mtl / T) * kRowBlock + (lane & 31);
-            const int g = 2 * (tb + mtl % T) + (lane >> 5);
-            const bool live = u < slots && g < G;
-            const uint32_t off = live ? (uint32_t)row * (uint32_t)p.lda * 2u + (uint32_t)g * 64u : kOutOfRange;
+        for (int b = 0; b < BR; ++b) {
+            const int sr = wave + NW * (j0 + b);
+            const int row = (mb0 + sr / kRowBlock) * kRowBlock + sr % kRowBlock;
+            const uint32_t rowoff = (uint32_t)row * (uint32_t)p.lda * 2u + (uint32_t)tb * 128u;
 #pragma unroll
-            for (int c = 0; c < 4; ++c) x[q][c] = bload16(rx_, off + 16u * c, 0u);
-        }
-    };
-    auto quant_slots = [&](int u0) {
-#pragma unroll
-        for (int q = 0; q < QREG; ++q) {
-            const int u = u0 + q * NT + tid;
-            if (u < slots) {
-                u32x4 codes;
-                const uint32_t byte = quant_group32(x[q], codes);
-                *(u32x4*)(lds + 16 * u) = codes;
-                lds[16 * slots + u] = (uint8_t)byte;
+            for (int k = 0; k < CPLM; ++k) {
+                const int kc = 64 * k + L;
+                const bool live = j0 + b < RPW && kc < cpr && 2 * tb + (kc >> 2) < G;
+                xs[b][k] = bload16(rx_, live ? rowoff + (uint32_t)kc * 16u : kOutOfRange, 0u);
             }
         }
     };
-    if constexpr (FUSED) load_slots(0);
+    auto slice_quant = [&](int j0) {
+#pragma unroll
+        for (int b = 0; b < BR; ++b) {
+            if (j0 + b >= RPW) break;
+            const int sr = wave + NW * (j0 + b);
+            const int i = sr / kRowBlock, r = sr % kRowBlock;
+#pragma unroll
+            for (int k = 0; k < CPLM; ++k) {
+                const int kc = 64 * k + L;
+                if (64 * k >= cpr) break;             // no chunk of this lane group left
+                if (kc < cpr) {                       // whole quads (cpr % 8 == 0)
+                    uint32_t byte;
+                    const uint32_t codes = quad_quant8(xs[b][k], byte);
+                    const int t = kc >> 3, h = (kc >> 2) & 1, q = kc & 3;
+                    const int u = (i * T + t) * 64 + r + 32 * h;
+                    *(uint32_t*)(lds + 16 * u + 4 * q) = codes;
+                    if (q == 0) lds[16 * slots + u] = (uint8_t)byte;
+                }
+            }
+        }
+    };
+    if constexpr (FUSED) slice_load(0);
 
     // kAmDirect: lane L's fragment of step s, m block i is row
     // 32 (mb0 + i) + L % 32, group 2 (wb + s) + L / 32; padding steps and a
@@ -246,10 +264,10 @@ gemm_kernel(GemmParams p) {
 
     // ---- 2. (FUSED) quantise the activation slice into LDS.
     if constexpr (FUSED) {
-        quant_slots(0);
-        for (int u0 = NT * QREG; u0 < slots; u0 += NT * QREG) {
-            load_slots(u0);
-            quant_slots(u0);
+        slice_quant(0);
+        for (int j0 = BR; j0 < RPW; j0 += BR) {
+            slice_load(j0);
+            slice_quant(j0);
         }
         __syncthreads();
     }
