@@ -16,17 +16,20 @@
 //      HBM round trip, read exactly once, straight into VGPRs, non-temporal.
 //   2. The activation operand, by the plan's activation mode AM:
 //      kAmLds     the workgroup quantises its activation slice (its m rows x
-//                 its K split) itself into LDS, in MFMA lane order: one lane
-//                 per 32-element group, per-lane amax, scale byte by the bit
-//                 rule, e2m1 codes by the gfx950 fp4 convert; the WN waves
-//                 of the workgroup share it;
+//                 its K split) itself into LDS, in MFMA lane order: rows
+//                 streamed 1 KB per load instruction, one DPP quad of lanes
+//                 per 32-element group (amax across the quad, scale byte by
+//                 the bit rule, e2m1 codes by the gfx950 fp4 convert); the
+//                 WN waves of the workgroup share it after a barrier;
 //      kAmPrequant a first kernel (pack_kernel) quantised A into the packed
 //                 operand layout in the workspace; each wave loads its
 //                 fragments from there (L2-resident) together with step 1;
-//      kAmDirect  every lane loads the 32 bf16 of exactly the fragment it
-//                 feeds to the MFMA (one row, one 32-element group) and
-//                 quantises it in registers: no LDS, no barrier; waves with
-//                 the same m rows and K steps each quantise them;
+//      kAmDirect  every wave loads the rows of exactly the fragments it
+//                 feeds to its MFMAs, 128 bytes per 8 lanes, regroups them
+//                 through its own LDS slab so that each lane holds one row's
+//                 32-element group, and quantises that group in registers:
+//                 no workgroup barrier before the MFMAs; waves with the same
+//                 m rows and K steps each quantise them;
 //      kAmBf16    the a16wfp4 product of the pages (submission 733989,
 //                 routing notes): A is not quantised.  Lanes load A as in
 //                 kAmDirect; the weight codes are widened to bf16 times
