@@ -563,3 +563,39 @@ def test_gemm_limit_sizes_sampled(M, N, K, sample):
     assert_c_close(got, ref, "limit size %s" % ((M, N, K),))
     del Ad, Bd, packed, C
     torch.cuda.empty_cache()
+
+
+def test_gemm_from_several_host_threads():
+    """Four host threads, each with its own stream, shapes and workspace,
+    call mx_gemm repeatedly (each thread keeps its own cache of prepared
+    calls); every result matches the oracle."""
+    import threading
+    shapes = [(32, 4096, 512), (16, 2112, 7168), (64, 640, 2048), (5, 200, 320)]
+    data = []
+    for (M, N, K) in shapes:
+        A, Bm = inputs.shape_inputs(M, N, K, seed=900 + M + N)
+        data.append((M, N, K, to_dev(A), B.mx_pack_weight(to_dev(Bm)),
+                     oracle.gemm(inputs.bits(A), inputs.bits(Bm))))
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(idx):
+        try:
+            M, N, K, Ad, packed, ref = data[idx]
+            s = torch.cuda.Stream()
+            ws = B.new_workspace(M, N, K, device=DEV)
+            s.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(s):
+                outs = [B.mx_gemm(Ad, packed, N, workspace=ws, stream=s) for _ in range(20)]
+            s.synchronize()
+            for C in outs:
+                assert_c_close(inputs.bits(C.cpu()), ref, "thread %d" % idx)
+        except Exception as e:   # reported from the main thread
+            errors.append((idx, repr(e)))
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(len(shapes))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not errors, errors
