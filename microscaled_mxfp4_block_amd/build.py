@@ -26,6 +26,11 @@ ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-Wall", "-I" + os.path.join(ROOT, "include")]
+# Kernel sources: the first 14 SGPRs of kernel arguments are preloaded at wave
+# launch (the GEMM kernels' leading scalar arguments, the quantisers' pointers
+# and sizes), so a kernel's first loads do not wait on a scalar-memory round
+# trip to the argument segment.
+KERNEL_FLAGS = ["-mllvm", "-amdgpu-kernarg-preload-count=14"]
 PACKED_FP32 = re.compile(r"\bv_pk_(add|mul|fma|mov)_f32\b")
 
 
@@ -37,17 +42,21 @@ def _run(cmd):
     return out
 
 
+def _flags(src, extra):
+    return FLAGS + (KERNEL_FLAGS if src.endswith(".hip") else []) + extra
+
+
 def _compile(item):
     src, extra, name = item
     obj = os.path.join(BUILD_DIR, name + ".o")
-    _run([HIPCC] + FLAGS + extra + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
+    _run([HIPCC] + _flags(src, extra) + ["-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj])
     return obj
 
 
 def _device_asm(item):
     src, extra, name = item
     asm = os.path.join(BUILD_DIR, name + ".s")
-    _run([HIPCC] + FLAGS + extra + ["-x", "hip", "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm])
+    _run([HIPCC] + _flags(src, extra) + ["-x", "hip", "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm])
     with open(asm) as f:
         text = f.read()
     bad = sorted(set(m.group(0) for m in PACKED_FP32.finditer(text)))

@@ -112,9 +112,41 @@ __device__ __forceinline__ void store_bf16x4(const GemmParams& p, int m, int n0,
     }
 }
 
+// The leading scalar arguments arrive preloaded in SGPRs (GemmKernelFn); the
+// kernel derives both operands' layouts from them with the host's own
+// operand_geom, so of the parameter block it reads only what the
+// last-arrival split-K finish needs (counters, splits, mtiles).
 template <int MBLK, int NBLK, int WN, int WK, int AM, int KR>
 __global__ void __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(2)))
-gemm_kernel(GemmParams p) {
+gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_buf, int lda, int ldc, int M, int N, int K,
+            int steps_per_split, GemmParams p) {
+    {
+        const OperandGeom ga = operand_geom(M, K), gb = operand_geom(N, K);
+        if constexpr (AM == kAmPrequant) {
+            p.aop = (const uint8_t*)a_src;
+            p.aop_bytes = (uint32_t)ga.total_bytes;
+            p.a_code_bytes = (uint32_t)ga.code_bytes;
+        } else {
+            p.A = (const uint16_t*)a_src;
+            p.a_bytes = (uint32_t)M * (uint32_t)lda * 2u;
+        }
+        p.bp = bp;
+        p.bp_bytes = (uint32_t)gb.total_bytes;
+        p.b_code_bytes = (uint32_t)gb.code_bytes;
+        p.C = C;
+        p.partial = partial_buf;
+        p.lda = lda;
+        p.ldc = ldc;
+        p.M = M;
+        p.N = N;
+        p.K = K;
+        p.KS = gb.KS;
+        p.KW = gb.KW;
+        p.RBm = ga.RB;
+        p.RBn = gb.RB;
+        p.ldp = gb.RB * kRowBlock;
+        p.steps_per_split = steps_per_split;
+    }
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr bool FUSED = AM == kAmLds;
     constexpr bool DIRECT = AM == kAmDirect;
@@ -378,7 +410,7 @@ gemm_kernel(GemmParams p) {
     constexpr int TC = NBLK * WN * kRowBlock; // columns of the workgroup tile
     constexpr int SROW = TC + 8;              // bf16 per staged row (16-byte pad)
     uint16_t* stage = (uint16_t*)(lds + gemm_red_bytes(WN, WK, MBLK, NBLK));
-    const bool partial = p.splits > 1;
+    const bool partial = p.partial != nullptr;   // K is split over workgroups
     const bool finish_here = partial && p.counters != nullptr;
     __shared__ uint32_t last_arrival;
     if constexpr (FUSED || REGA) __syncthreads();   // every wave is done with the activation in LDS
@@ -538,7 +570,7 @@ gemm_kernel(GemmParams p) {
 #error "compile with -DMX4_KR=<K steps per wave>"
 #endif
 
-typedef void (*GemmFn)(GemmParams);
+typedef GemmKernelFn GemmFn;
 
 template <int MBLK, int NBLK, int WN, int AM>
 static GemmFn pick_wk(int wk) {
@@ -652,20 +684,20 @@ bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
     GemmFn fn = find_kernel(plan, gemm_kr_for(per_wave));
     if (!fn) return false;
     *out = GemmLaunch{fn, (unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits, (unsigned)(64 * plan.wn * plan.wk),
-                      gemm_lds_bytes(plan, p.steps_per_split)};
+                      gemm_lds_bytes(plan, p.steps_per_split), plan.amode == kAmPrequant};
     return true;
 }
 
 hipError_t launch_gemm(const GemmLaunch& gl, const GemmParams& p, hipStream_t s) {
-    hipLaunchKernelGGL(gl.fn, dim3(gl.gx, gl.gy, gl.gz), dim3(gl.block), gl.lds, s, p);
-    return hipGetLastError();
+    const void* a_src = gl.prequant ? (const void*)p.aop : (const void*)p.A;
+    return launch_kernel(gl.fn, dim3(gl.gx, gl.gy, gl.gz), dim3(gl.block), gl.lds, s, a_src, p.bp, p.C, p.partial,
+                         p.lda, p.ldc, p.M, p.N, p.K, p.steps_per_split, p);
 }
 
 hipError_t launch_reduce(const GemmParams& p, hipStream_t s) {
     const unsigned gx = (unsigned)(((p.N + 3) / 4 + 255) / 256);
     const unsigned gy = (unsigned)(p.M < 65535 ? p.M : 65535);
-    hipLaunchKernelGGL(reduce_kernel, dim3(gx, gy), dim3(256), 0, s, p);
-    return hipGetLastError();
+    return launch_kernel(reduce_kernel, dim3(gx, gy), dim3(256), 0, s, p);
 }
 #endif
 

@@ -116,17 +116,15 @@ hipError_t launch_quant_natural(const uint16_t* x, int rows, int K, int ld, uint
                                 hipStream_t s) {
     const unsigned gx = (unsigned)((K / 8 + 255) / 256);
     const unsigned gy = (unsigned)(rows < 65535 ? rows : 65535);
-    hipLaunchKernelGGL(quant_natural_kernel, dim3(gx, gy), dim3(256), 0, s, x, rows, K, ld, codes, scales);
-    return hipGetLastError();
+    return launch_kernel(quant_natural_kernel, dim3(gx, gy), dim3(256), 0, s, x, rows, K, ld, codes, scales);
 }
 
 hipError_t launch_pack(const uint16_t* x, int rows, int K, int ld, uint8_t* packed, hipStream_t s) {
     const OperandGeom g = operand_geom(rows, K);
     const unsigned gx = (unsigned)((g.KW * 32 + 255) / 256);
     const unsigned gy = (unsigned)(g.RB * kRowBlock < 65535 ? g.RB * kRowBlock : 65535);
-    hipLaunchKernelGGL(pack_kernel, dim3(gx, gy), dim3(256), 0, s, x, rows, K, ld, packed, g.RB, g.KS, g.KW,
-                       g.code_bytes);
-    return hipGetLastError();
+    return launch_kernel(pack_kernel, dim3(gx, gy), dim3(256), 0, s, x, rows, K, ld, packed, g.RB, g.KS, g.KW,
+                         g.code_bytes);
 }
 
 hipError_t launch_import(const uint8_t* codes, const uint8_t* scales, int rows, int K, uint8_t* packed,
@@ -134,18 +132,16 @@ hipError_t launch_import(const uint8_t* codes, const uint8_t* scales, int rows, 
     const OperandGeom g = operand_geom(rows, K);
     const long long total = (long long)g.RB * g.KW * kStepsPerWord * 64;
     const long long blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(import_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales, rows, K, packed, g.RB,
-                       g.KS, g.KW, g.code_bytes);
-    return hipGetLastError();
+    return launch_kernel(import_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes, scales, rows, K, packed, g.RB,
+                         g.KS, g.KW, g.code_bytes);
 }
 
 hipError_t launch_unpack(const uint8_t* packed, int rows, int K, uint8_t* codes, uint8_t* scales, hipStream_t s) {
     const OperandGeom g = operand_geom(rows, K);
     const long long total = (long long)g.RB * g.KS * 64;
     const long long blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, packed, rows, K, g.RB, g.KS, g.KW,
-                       g.code_bytes, codes, scales);
-    return hipGetLastError();
+    return launch_kernel(unpack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, packed, rows, K, g.RB, g.KS, g.KW,
+                         g.code_bytes, codes, scales);
 }
 
 }  // namespace mx4

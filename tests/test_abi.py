@@ -252,6 +252,29 @@ def test_planner_rejects_every_spilling_kernel():
     assert checked > 100
 
 
+def test_gemm_kernels_take_preloaded_arguments():
+    """Every GEMM kernel's descriptor asks for its 14 leading argument SGPRs
+    (the scalar fields ahead of the parameter block) to be preloaded at wave
+    launch; the reduction kernel takes the block alone and preloads nothing."""
+    import glob
+    build = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "_build")
+    asms = glob.glob(os.path.join(build, "mx4_gemm_kr*.s"))
+    if not asms:
+        pytest.skip("no device assembly under _build (run the package build first)")
+    seen = 0
+    for path in asms:
+        text = open(path).read()
+        for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S):
+            name, body = m.group(1), m.group(2)
+            n = int(re.search(r"\.amdhsa_user_sgpr_kernarg_preload_length (\d+)", body).group(1))
+            if "gemm_kernel" in name:
+                assert n == 14, (name, n)
+                seen += 1
+            elif "reduce_kernel" in name:
+                assert n == 0, (name, n)
+    assert seen > 100
+
+
 def test_shapes_past_the_addressing_limit_are_refused():
     """rows * K * 2 >= 2^31 for an operand (32-bit buffer offsets) is refused
     before any launch; just below it is accepted."""

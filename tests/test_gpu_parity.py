@@ -60,6 +60,26 @@ def gpu_bits(t: torch.Tensor) -> np.ndarray:
     return inputs.bits(t.cpu())
 
 
+SENTINEL = -7.0
+
+
+def guarded_c(M, N, ldc_pad=0):
+    """C as the top-left M x N of a buffer filled with a sentinel: rows up to
+    M rounded up to 64 plus 32 (past every row an M tile of the kernels can
+    cover) and ldc_pad columns past N, so that a store outside C lands in
+    this buffer and shows, instead of corrupting other memory."""
+    rows = (M + 63) // 64 * 64 + 32
+    Cbuf = torch.full((rows, N + ldc_pad), SENTINEL, dtype=torch.bfloat16, device=DEV)
+    return Cbuf, Cbuf[:M, :N]
+
+
+def assert_guard_intact(Cbuf, M, N):
+    sent = inputs.bits(torch.tensor([SENTINEL], dtype=torch.bfloat16))[0]
+    assert np.all(gpu_bits(Cbuf[M:]) == sent), "wrote past row M"
+    if Cbuf.shape[1] > N:
+        assert np.all(gpu_bits(Cbuf[:M, N:]) == sent), "wrote past column N"
+
+
 def run_gemm(A_cpu, B_cpu, plan=None, ldc_pad=0, lda_pad=0):
     M, K = A_cpu.shape
     N = B_cpu.shape[0]
@@ -70,17 +90,10 @@ def run_gemm(A_cpu, B_cpu, plan=None, ldc_pad=0, lda_pad=0):
     else:
         A = to_dev(A_cpu)
     packed = B.mx_pack_weight(to_dev(B_cpu))
-    if ldc_pad:
-        Cbuf = torch.full((M, N + ldc_pad), -7.0, dtype=torch.bfloat16, device=DEV)
-        C = Cbuf[:, :N]
-    else:
-        C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
-        Cbuf = None
+    Cbuf, C = guarded_c(M, N, ldc_pad)
     B.mx_gemm(A, packed, N, C=C, plan=plan)
     out = gpu_bits(C)
-    if Cbuf is not None:
-        pad = gpu_bits(Cbuf[:, N:])
-        assert np.all(pad == inputs.bits(torch.tensor([-7.0], dtype=torch.bfloat16))[0]), "wrote past N"
+    assert_guard_intact(Cbuf, M, N)
     return out
 
 
@@ -295,6 +308,27 @@ def test_gemm_explicit_plans(shape, plan):
     A, Bm = inputs.shape_inputs(M, N, K, seed=11 + M + N)
     C = run_gemm(A, Bm, plan=plan)
     assert_c_close(C, oracle.gemm(inputs.bits(A), inputs.bits(Bm)), "%s %s" % (shape, plan_id(plan)))
+
+
+@pytest.mark.parametrize("plan", PLANS + PLANS_A16W4, ids=plan_id)
+@pytest.mark.parametrize("shape", [(5, 200, 320), (33, 130, 2048), (9, 70, 352), (40, 100, 2048)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_gemm_writes_nothing_outside_c(shape, plan):
+    """Every plan leaves the memory around C alone: the rows past M of its
+    last M tile and the columns past N of its last N tile are masked (C sits
+    in a sentinel-filled buffer 128 columns wider, ldc = N + 128)."""
+    M, N, K = shape
+    if not plan_runs(M, N, K, plan):
+        pytest.skip("plan outside the register / LDS budget for this shape")
+    say("gemm guard", shape, plan_id(plan))
+    A, Bm = inputs.shape_inputs(M, N, K, seed=3 + M + N)
+    Ad = to_dev(A)
+    packed = B.mx_pack_weight(to_dev(Bm))
+    Cbuf, C = guarded_c(M, N, 128)
+    B.mx_gemm(Ad, packed, N, C=C, plan=plan)
+    assert_guard_intact(Cbuf, M, N)
+    ref = oracle.gemm_a16w4 if plan["amode"] == 3 else oracle.gemm
+    assert_c_close(gpu_bits(C), ref(inputs.bits(A), inputs.bits(Bm)), "%s %s" % (shape, plan_id(plan)))
 
 
 def test_gemm_binade_spread_and_strides():
