@@ -45,10 +45,10 @@ struct TableEntry {
     Plan plan;   // mb, nb, wn, wk, splits, amode, finish
 };
 const TableEntry kTable[] = {
-    {4, 2880, 512, {1, 1, 1, 8, 1, 2, 0}},
-    {32, 4096, 512, {1, 1, 1, 8, 1, 2, 0}},
-    {32, 2880, 512, {1, 1, 1, 8, 1, 2, 0}},
-    {16, 2112, 7168, {1, 1, 1, 4, 7, 2, 0}},
+    {4, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
+    {32, 4096, 512, {1, 1, 1, 4, 1, 2, 0}},
+    {32, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
+    {16, 2112, 7168, {1, 2, 1, 8, 7, 2, 0}},
     {64, 7168, 2048, {1, 2, 1, 16, 1, 2, 0}},
     {256, 3072, 1536, {1, 1, 1, 8, 1, 1, 0}},
 };
@@ -125,7 +125,8 @@ Plan model_plan(int M, int N, int K) {
     p.mb = (p.amode == kAmPrequant && ga.RB >= 2) ? 2 : 1;
     p.nb = 1;
     p.wn = 1;
-    p.wk = pow2_floor(gb.KS < 8 ? gb.KS : 8);
+    // about two K steps per wave: the measured optimum for every tabled shape
+    p.wk = pow2_floor(gb.KS < 16 ? (gb.KS + 1) / 2 : 8);
     p.splits = 1;
     p.finish = 0;
     Layout l;
@@ -147,8 +148,8 @@ Plan choose_plan(int M, int N, int K) {
 // Plans measured for the a16wfp4 product on the same shapes.
 const TableEntry kTableA16w4[] = {
     {4, 2880, 512, {1, 1, 1, 4, 1, 3, 0}},
-    {32, 4096, 512, {1, 1, 1, 8, 1, 3, 0}},
-    {32, 2880, 512, {1, 1, 1, 8, 1, 3, 0}},
+    {32, 4096, 512, {1, 1, 1, 4, 1, 3, 0}},
+    {32, 2880, 512, {1, 1, 1, 4, 1, 3, 0}},
     {16, 2112, 7168, {1, 1, 1, 8, 7, 3, 0}},
     {64, 7168, 2048, {1, 1, 2, 4, 1, 3, 0}},
     {256, 3072, 1536, {1, 2, 2, 8, 1, 3, 0}},
