@@ -48,8 +48,8 @@ const TableEntry kTable[] = {
     {4, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
     {32, 4096, 512, {1, 1, 1, 4, 1, 2, 0}},
     {32, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
-    {16, 2112, 7168, {1, 2, 1, 8, 7, 2, 0}},
-    {64, 7168, 2048, {1, 2, 1, 16, 1, 2, 0}},
+    {16, 2112, 7168, {1, 2, 1, 4, 7, 2, 0}},
+    {64, 7168, 2048, {1, 2, 1, 8, 1, 2, 0}},
     {256, 3072, 1536, {1, 1, 1, 8, 1, 1, 0}},
 };
 
@@ -150,8 +150,8 @@ const TableEntry kTableA16w4[] = {
     {4, 2880, 512, {1, 1, 1, 4, 1, 3, 0}},
     {32, 4096, 512, {1, 1, 1, 4, 1, 3, 0}},
     {32, 2880, 512, {1, 1, 1, 4, 1, 3, 0}},
-    {16, 2112, 7168, {1, 1, 1, 8, 7, 3, 0}},
-    {64, 7168, 2048, {1, 1, 2, 4, 1, 3, 0}},
+    {16, 2112, 7168, {1, 1, 1, 4, 7, 3, 0}},
+    {64, 7168, 2048, {1, 2, 1, 8, 1, 3, 0}},
     {256, 3072, 1536, {1, 2, 2, 8, 1, 3, 0}},
 };
 

@@ -163,6 +163,24 @@ __device__ __forceinline__ u32x4 bload16(Rsrc r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, AUX);
 }
 
+// 16 bytes per lane straight into LDS (gfx950 buffer_load_dwordx4 ... lds):
+// lane l's bytes land at lds_base + 16 l, whatever its global offset; a lane
+// whose offset is past the buffer writes zeros.  lds_base is wave-uniform.
+// Completion is counted by vmcnt, in order with the wave's other loads.
+__device__ __forceinline__ void bload16_lds(Rsrc r, uint8_t* lds_base, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16, (int)voff, 0, 0,
+                                             0);
+}
+
+// s_waitcnt for at most n outstanding vector-memory operations (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their
+// maxima, i.e. not waited for).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ uint32_t bload4(Rsrc r, uint32_t voff, uint32_t soff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
 }

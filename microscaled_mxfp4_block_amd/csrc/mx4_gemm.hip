@@ -25,9 +25,11 @@
 //                 operand layout in the workspace; each wave loads its
 //                 fragments from there (L2-resident) together with step 1;
 //      kAmDirect  every wave loads the rows of exactly the fragments it
-//                 feeds to its MFMAs, 128 bytes per 8 lanes, regroups them
-//                 through its own LDS slab so that each lane holds one row's
-//                 32-element group, and quantises that group in registers:
+//                 feeds to its MFMAs, 128 bytes per 8 lanes, straight into
+//                 its own LDS tiles (or through VGPRs into a padded slab when
+//                 the tiles of all its K steps do not fit), reads them back
+//                 so that each lane holds one row's 32-element group, and
+//                 quantises that group in registers:
 //                 no workgroup barrier before the MFMAs; waves with the same
 //                 m rows and K steps each quantise them;
 //      kAmBf16    the a16wfp4 product of the pages (submission 733989,
@@ -69,6 +71,22 @@ __host__ __device__ constexpr int slab_steps(int kr) { return kr < 2 ? kr : 2; }
 __host__ __device__ constexpr size_t gemm_slab_bytes(int waves, int mb, int kr) {
     return (size_t)waves * mb * slab_steps(kr) * kRowBlock * kSlabRow;
 }
+
+// When all of a workgroup's K steps fit in LDS at once (waves x MBLK x KR
+// tiles of 4 KiB), the coalesced loads skip the VGPRs: each goes straight
+// into the wave's LDS tile of its (K step, m block) (gfx950 buffer loads to
+// LDS, 16 bytes per lane).  A tile is 32 rows x 128 bytes with 16-byte column
+// j of row r at slot j ^ ((r >> 1) & 7): the 16 lanes of each fragment read
+// then hit 16 distinct 16-byte bank groups, and each lane still chooses its
+// global chunk, so 8 lanes still read one 128-byte row segment.
+constexpr int kDmaTile = kRowBlock * 128;
+__host__ __device__ constexpr bool gemm_uses_dma(int waves, int mb, int kr) {
+    return (size_t)waves * mb * kr * kDmaTile <= kLdsBudget;
+}
+__host__ __device__ constexpr size_t gemm_dma_bytes(int waves, int mb, int kr) {
+    return (size_t)waves * mb * kr * kDmaTile;
+}
+__host__ __device__ constexpr int dma_slot(int r, int j) { return r * 128 + ((j ^ ((r >> 1) & 7)) << 4); }
 
 // LDS of the WK-reduction buffer and of the staged bf16 output tile.
 // The reduction buffer is lane-major: each lane's mb * nb * 16 accumulators
@@ -242,9 +260,12 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
     // group past K read zeros (zero codes, scale byte 0), rows past M read
     // zeros through the buffer bound.
     u32x4 xa[REGA ? KR : 1][MBLK][4];
+    constexpr bool DMA = REGA && gemm_uses_dma(NT / 64, MBLK, KR);
+    uint8_t* dtile = lds + (size_t)wave * (MBLK * KR * kDmaTile);   // this wave's tiles (DMA)
     if constexpr (REGA) {
         // coalesced: chunk q of lane L is row (64 q + L) / 8 of the tile,
-        // 16-byte column (64 q + L) % 8 of its 128-byte K segment
+        // 16-byte column (64 q + L) % 8 of its 128-byte K segment -- with
+        // DMA, the column whose swizzled slot is (64 q + L) % 8
         const Rsrc rx_ = make_rsrc(p.A, p.a_bytes);
 #pragma unroll
         for (int s = 0; s < KR; ++s) {
@@ -253,17 +274,24 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     const int c = q * 64 + L;
-                    const int r = c >> 3, col = c & 7;
+                    const int r = c >> 3;
+                    const int col = DMA ? (c & 7) ^ ((r >> 1) & 7) : (c & 7);
                     const int g = 2 * (wb + s) + (col >> 2);
                     const bool live = s < nsteps && g < G;
                     const int row = (mb0 + i) * kRowBlock + r;
                     const uint32_t off = live ? (uint32_t)row * (uint32_t)p.lda * 2u + (uint32_t)(wb + s) * 128u +
                                                     (uint32_t)col * 16u
                                               : kOutOfRange;
-                    xa[s][i][q] = bload16(rx_, off, 0u);
+                    if constexpr (DMA)
+                        bload16_lds(rx_, dtile + ((s * MBLK + i) * 4 + q) * 1024, off);
+                    else
+                        xa[s][i][q] = bload16(rx_, off, 0u);
                 }
             }
         }
+        // the weight loads below stay behind the DMA loads (vmcnt counts in
+        // issue order; the wait before the tiles are read relies on it)
+        if constexpr (DMA) asm volatile("" ::: "memory");
     }
 
     // Weight (and pre-quantised activation) fragments, all in flight.
@@ -308,9 +336,22 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
     }
 
     // ---- 2b. (kAmDirect / kAmBf16) the coalesced activation chunks go through
-    // this wave's LDS slab into fragment order: lane L then holds the 64 bytes
-    // of row 32 (mb0 + i) + L % 32, group 2 (wb + s) + L / 32.
-    if constexpr (REGA) {
+    // this wave's LDS tiles or slab into fragment order: lane L then holds the
+    // 64 bytes of row 32 (mb0 + i) + L % 32, group 2 (wb + s) + L / 32.
+    if constexpr (DMA) {
+        // every weight load is issued; wait until at most those are still
+        // outstanding, i.e. every DMA load has landed
+        asm volatile("" ::: "memory");
+        wait_vmcnt<2 * KR * NBLK>();
+#pragma unroll
+        for (int s = 0; s < KR; ++s)
+#pragma unroll
+            for (int i = 0; i < MBLK; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    xa[s][i][c] = *(const u32x4*)(dtile + (s * MBLK + i) * kDmaTile +
+                                                  dma_slot(L & 31, 4 * (L >> 5) + c));
+    } else if constexpr (REGA) {
         constexpr int SR = slab_steps(KR);
         uint8_t* slab = lds + (size_t)wave * (MBLK * SR * kRowBlock * kSlabRow);
 #pragma unroll
@@ -667,9 +708,11 @@ static GemmFn find_kernel(const Plan& plan, int kr) {
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
     const size_t a_op = plan.amode == kAmLds ? (size_t)plan.mb * steps_per_split * 64 * 17 : 0;
     size_t out = gemm_red_bytes(plan.wn, plan.wk, plan.mb, plan.nb) + gemm_stage_bytes(plan.wn, plan.mb, plan.nb);
-    if (plan.amode == kAmDirect || plan.amode == kAmBf16) {   // the slabs alias the epilogue's buffers
+    if (plan.amode == kAmDirect || plan.amode == kAmBf16) {   // tiles or slabs alias the epilogue's buffers
+        const int nw = plan.wn * plan.wk;
+        const int kr = gemm_kr_for((steps_per_split + plan.wk - 1) / plan.wk);
         const size_t slab =
-            gemm_slab_bytes(plan.wn * plan.wk, plan.mb, gemm_kr_for((steps_per_split + plan.wk - 1) / plan.wk));
+            gemm_uses_dma(nw, plan.mb, kr) ? gemm_dma_bytes(nw, plan.mb, kr) : gemm_slab_bytes(nw, plan.mb, kr);
         out = slab > out ? slab : out;
     }
     return a_op > out ? a_op : out;
