@@ -275,6 +275,46 @@ def test_gemm_kernels_take_preloaded_arguments():
     assert seen > 100
 
 
+def test_lds_dma_tiles_are_read_only_after_their_loads_land():
+    """In every GEMM kernel that loads activation tiles straight into LDS, the
+    first vmcnt wait after the last such load lets through only loads issued
+    after it: at least that many other vector loads (the weight fragments)
+    come between the two, no vector store does, and no LDS read of a tile
+    comes before the wait.  Vector-memory operations of one wave complete in
+    issue order, so the wait then implies that every tile has landed."""
+    import glob
+    build = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "_build")
+    asms = glob.glob(os.path.join(build, "mx4_gemm_kr*.s"))
+    if not asms:
+        pytest.skip("no device assembly under _build (run the package build first)")
+    vmem_load = re.compile(r"^\s*(buffer|global|flat|scratch)_load\w*")
+    vmem_store = re.compile(r"^\s*(buffer|global|flat|scratch)_(store|atomic)\w*")
+    checked = 0
+    for path in asms:
+        text = open(path).read()
+        for m in re.finditer(r"^(_ZN3mx411gemm_kernel\S*):.*?s_endpgm", text, re.S | re.M):
+            body = m.group(0).splitlines()
+            dma = [k for k, ln in enumerate(body) if vmem_load.match(ln) and ln.rstrip().endswith(" lds")]
+            if not dma:
+                continue
+            last = dma[-1]
+            loads = 0
+            for ln in body[last + 1:]:
+                assert not vmem_store.match(ln), (m.group(1), ln)
+                assert not ln.strip().startswith("ds_read"), (m.group(1), "LDS read before the vmcnt wait")
+                w = re.search(r"s_waitcnt\s.*vmcnt\((\d+)\)", ln)
+                if w:
+                    assert loads >= int(w.group(1)), (m.group(1), loads, ln)
+                    break
+                if vmem_load.match(ln):
+                    assert not ln.rstrip().endswith(" lds")
+                    loads += 1
+            else:
+                raise AssertionError("%s: no vmcnt wait after its LDS loads" % m.group(1))
+            checked += 1
+    assert checked > 50
+
+
 def test_shapes_past_the_addressing_limit_are_refused():
     """rows * K * 2 >= 2^31 for an operand (32-bit buffer offsets) is refused
     before any launch; just below it is accepted."""
