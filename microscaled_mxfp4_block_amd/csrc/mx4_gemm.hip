@@ -134,7 +134,11 @@ __device__ __forceinline__ void store_bf16x4(const GemmParams& p, int m, int n0,
 // kernel derives both operands' layouts from them with the host's own
 // operand_geom, so of the parameter block it reads only what the
 // last-arrival split-K finish needs (counters, splits, mtiles).
-template <int MBLK, int NBLK, int WN, int WK, int AM, int KR>
+// RQ (kAmDirect / kAmBf16 with one 32-row block): how many 8-row chunks of
+// the block each K step loads; rows from 8 RQ on are past M, feed only
+// outputs that are never stored, and are not loaded (for M <= 8 or <= 16 a
+// fourth or a half of the activation traffic).
+template <int MBLK, int NBLK, int WN, int WK, int AM, int KR, int RQ>
 __global__ void __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(2)))
 gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_buf, int lda, int ldc, int M, int N, int K,
             int steps_per_split, GemmParams p) {
@@ -273,6 +277,10 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
             for (int i = 0; i < MBLK; ++i) {
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
+                    if (q >= RQ) {   // rows 8q .. 8q + 7 are past M (resolved at compile time)
+                        if constexpr (!DMA) xa[s][i][q] = u32x4{0u, 0u, 0u, 0u};
+                        continue;
+                    }
                     const int c = q * 64 + L;
                     const int r = c >> 3;
                     const int col = DMA ? (c & 7) ^ ((r >> 1) & 7) : (c & 7);
@@ -604,8 +612,9 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
 // ---------------------------------------------------------------------------
 // Instantiation table.  This file is compiled once per K-step budget KR
 // (-DMX4_KR=1, 2, 4 or 8); each object instantiates MBLK, NBLK in {1, 2},
-// WN in {1, 2}, WK in {1, 2, 4, 8, 16} (at most 16 waves) and the three
-// activation modes.
+// WN in {1, 2}, WK in {1, 2, 4, 8, 16} (at most 16 waves) and the four
+// activation modes with all four row chunks (RQ = 4), and the register modes
+// with MBLK = WN = 1 also with RQ = 1 and 2.
 
 #ifndef MX4_KR
 #error "compile with -DMX4_KR=<K steps per wave>"
@@ -613,15 +622,15 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
 
 typedef GemmKernelFn GemmFn;
 
-template <int MBLK, int NBLK, int WN, int AM>
+template <int MBLK, int NBLK, int WN, int AM, int RQ>
 static GemmFn pick_wk(int wk) {
     constexpr int KR = MX4_KR;
     switch (wk) {
-        case 1: return gemm_kernel<MBLK, NBLK, WN, 1, AM, KR>;
-        case 2: return gemm_kernel<MBLK, NBLK, WN, 2, AM, KR>;
-        case 4: return gemm_kernel<MBLK, NBLK, WN, 4, AM, KR>;
-        case 8: return gemm_kernel<MBLK, NBLK, WN, 8, AM, KR>;
-        case 16: return WN == 1 ? gemm_kernel<MBLK, NBLK, WN, (WN == 1 ? 16 : 8), AM, KR> : nullptr;
+        case 1: return gemm_kernel<MBLK, NBLK, WN, 1, AM, KR, RQ>;
+        case 2: return gemm_kernel<MBLK, NBLK, WN, 2, AM, KR, RQ>;
+        case 4: return gemm_kernel<MBLK, NBLK, WN, 4, AM, KR, RQ>;
+        case 8: return gemm_kernel<MBLK, NBLK, WN, 8, AM, KR, RQ>;
+        case 16: return WN == 1 ? gemm_kernel<MBLK, NBLK, WN, (WN == 1 ? 16 : 8), AM, KR, RQ> : nullptr;
         default: return nullptr;
     }
 }
@@ -629,8 +638,8 @@ static GemmFn pick_wk(int wk) {
 template <int MBLK, int NBLK, int AM>
 static GemmFn pick_wn(int wn, int wk) {
     switch (wn) {
-        case 1: return pick_wk<MBLK, NBLK, 1, AM>(wk);
-        case 2: return pick_wk<MBLK, NBLK, 2, AM>(wk);
+        case 1: return pick_wk<MBLK, NBLK, 1, AM, 4>(wk);
+        case 2: return pick_wk<MBLK, NBLK, 2, AM, 4>(wk);
         default: return nullptr;
     }
 }
@@ -644,9 +653,22 @@ static GemmFn pick_tile(const Plan& plan) {
     return nullptr;
 }
 
+// The RQ < 4 kernels (register modes, MBLK = WN = 1).
+template <int AM, int RQ>
+static GemmFn pick_rows(const Plan& plan) {
+    if (plan.nb == 1) return pick_wk<1, 1, 1, AM, RQ>(plan.wk);
+    if (plan.nb == 2) return pick_wk<1, 2, 1, AM, RQ>(plan.wk);
+    return nullptr;
+}
+
 #define MX4_CAT2(a, b) a##b
 #define MX4_CAT(a, b) MX4_CAT2(a, b)
-GemmFn MX4_CAT(find_gemm_kr, MX4_KR)(const Plan& plan) {
+GemmFn MX4_CAT(find_gemm_kr, MX4_KR)(const Plan& plan, int rq) {
+    const bool reg = plan.amode == kAmDirect || plan.amode == kAmBf16;
+    if (rq < 4 && reg && plan.mb == 1 && plan.wn == 1) {
+        if (plan.amode == kAmDirect) return rq == 1 ? pick_rows<kAmDirect, 1>(plan) : pick_rows<kAmDirect, 2>(plan);
+        return rq == 1 ? pick_rows<kAmBf16, 1>(plan) : pick_rows<kAmBf16, 2>(plan);
+    }
     switch (plan.amode) {
         case kAmLds: return pick_tile<kAmLds>(plan);
         case kAmPrequant: return pick_tile<kAmPrequant>(plan);
@@ -685,9 +707,9 @@ __global__ void __launch_bounds__(256) reduce_kernel(GemmParams p) {
     }
 }
 
-GemmFn find_gemm_kr2(const Plan& plan);
-GemmFn find_gemm_kr4(const Plan& plan);
-GemmFn find_gemm_kr8(const Plan& plan);
+GemmFn find_gemm_kr2(const Plan& plan, int rq);
+GemmFn find_gemm_kr4(const Plan& plan, int rq);
+GemmFn find_gemm_kr8(const Plan& plan, int rq);
 
 int gemm_kr_for(int steps_per_wave) {
     for (int kr = 1; kr <= kStepsPerWaveMax; kr *= 2)
@@ -695,14 +717,21 @@ int gemm_kr_for(int steps_per_wave) {
     return 0;
 }
 
-static GemmFn find_kernel(const Plan& plan, int kr) {
+static GemmFn find_kernel(const Plan& plan, int kr, int rq = 4) {
     switch (kr) {
-        case 1: return find_gemm_kr1(plan);
-        case 2: return find_gemm_kr2(plan);
-        case 4: return find_gemm_kr4(plan);
-        case 8: return find_gemm_kr8(plan);
+        case 1: return find_gemm_kr1(plan, rq);
+        case 2: return find_gemm_kr2(plan, rq);
+        case 4: return find_gemm_kr4(plan, rq);
+        case 8: return find_gemm_kr8(plan, rq);
         default: return nullptr;
     }
+}
+
+// Row chunks a call needs loaded (the kernels' RQ): with a single M tile of
+// one 32-row block, the chunks that hold rows below M; else all four.
+static int row_chunks(const Plan& plan, const GemmParams& p) {
+    if (p.RBm != 1 || plan.mb != 1) return 4;
+    return p.M <= 8 ? 1 : p.M <= 16 ? 2 : 4;
 }
 
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
@@ -724,7 +753,7 @@ bool gemm_plan_supported(const Plan& plan) {
 
 bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
     const int per_wave = (p.steps_per_split + plan.wk - 1) / plan.wk;
-    GemmFn fn = find_kernel(plan, gemm_kr_for(per_wave));
+    GemmFn fn = find_kernel(plan, gemm_kr_for(per_wave), row_chunks(plan, p));
     if (!fn) return false;
     *out = GemmLaunch{fn, (unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits, (unsigned)(64 * plan.wn * plan.wk),
                       gemm_lds_bytes(plan, p.steps_per_split), plan.amode == kAmPrequant};
