@@ -159,19 +159,24 @@ def graph_loop(torch, st, ncap=100, reps=20):
     return e0.elapsed_time(e1) * 1e3 / (reps * ncap)
 
 
-def launch_floor(torch, ncap=100, reps=20):
+def launch_floor(torch, same_bytes, ncap=100, reps=20):
     """What any kernel costs on this GPU, replayed from a HIP graph so that the
-    host is out of the loop: a near-empty kernel (torch's one-cycle sleep)
-    and a plain 1 MiB device copy over rotating buffers."""
+    host is out of the loop: a near-empty kernel (torch's one-cycle sleep),
+    a plain 1 MiB device copy, and a device copy that moves `same_bytes` HBM
+    bytes (same_bytes / 2 read + the same written), over rotating buffers."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     n = 1 << 20
     src = [torch.ones(n, dtype=torch.uint8, device="cuda:0") for _ in range(ncap)]
     dst = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(ncap)]
+    h = same_bytes // 2
+    src2 = [torch.ones(h, dtype=torch.uint8, device="cuda:0") for _ in range(ncap)]
+    dst2 = [torch.empty(h, dtype=torch.uint8, device="cuda:0") for _ in range(ncap)]
     torch.cuda.synchronize()
     out = {}
     for name, body in (("empty_kernel_us", lambda i: torch.cuda._sleep(1)),
-                       ("copy_1MiB_us", lambda i: dst[i].copy_(src[i]))):
+                       ("copy_1MiB_us", lambda i: dst[i].copy_(src[i])),
+                       ("copy_same_bytes_us", lambda i: dst2[i].copy_(src2[i]))):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
             for i in range(ncap):
@@ -186,7 +191,9 @@ def launch_floor(torch, ncap=100, reps=20):
             e1.record(s)
         torch.cuda.synchronize()
         out[name] = round(e0.elapsed_time(e1) * 1e3 / (reps * ncap), 3)
-    out["method"] = "HIP graph of %d launches replayed %d times, HIP events on the replay stream" % (ncap, reps)
+    out["same_bytes"] = 2 * h
+    out["method"] = ("HIP graph of %d launches replayed %d times, HIP events on the replay stream; the same-bytes "
+                     "copy moves as many HBM bytes as one call of the headline workload" % (ncap, reps))
     return out
 
 
@@ -232,7 +239,104 @@ def profile_run(torch, B, inputs, calls):
         torch.cuda.empty_cache()
 
 
-def summarize_profiles(trace_dir, fetch_dir, write_dir, calls_trace, calls_pmc):
+def profile_floor_run(torch, inputs, calls):
+    """Reference kernels for a rocprofv3 kernel trace, no timing: `calls`
+    near-empty kernels (torch's one-cycle sleep), then per workload, in the
+    workload order, `calls` plain device copies that move the same HBM bytes
+    as one GEMM call (algorithmic bytes / 2 read + the same written), over
+    rotating buffers with a >= 1 GiB working set like the GEMM calls."""
+    for _ in range(calls):
+        torch.cuda._sleep(1)
+    torch.cuda.synchronize()
+    print("profiled %d near-empty kernels" % calls, flush=True)
+    for w in inputs.WORKLOADS:
+        n = algorithmic_bytes(w.M, w.N, w.K) // 2
+        copies = max(4, WORKING_SET // (2 * n))
+        # torch.empty launches nothing, so the trace holds only the copies
+        src = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(copies)]
+        dst = [torch.empty(n, dtype=torch.uint8, device="cuda:0") for _ in range(copies)]
+        for i in range(calls):
+            dst[i % copies].copy_(src[i % copies])
+        torch.cuda.synchronize()
+        print("profiled %s: %d copies of %d bytes" % (w.name, calls, n), flush=True)
+        del src, dst
+        torch.cuda.empty_cache()
+
+
+def floor_lines(floor_dir, calls):
+    """Rows of the reference-kernel table from a trace of --profile-floor,
+    whose dispatches are exactly `calls` near-empty kernels, then `calls`
+    copies per workload in the workload order."""
+    import csv
+    from microscaled_mxfp4_block_amd import inputs
+    rows = None
+    for f in sorted(os.listdir(floor_dir)):
+        if f.endswith("kernel_trace.csv"):
+            with open(os.path.join(floor_dir, f)) as fh:
+                rows = list(csv.DictReader(fh))
+    if rows is None:
+        raise SystemExit("no *kernel_trace.csv under %s" % floor_dir)
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    labels = ["near-empty kernel (torch.cuda._sleep(1))"] + [
+        "device copy moving %d HBM bytes, as one %s call" % (2 * (algorithmic_bytes(w.M, w.N, w.K) // 2), w.name)
+        for w in inputs.WORKLOADS]
+    rows = rows[-calls * len(labels):]
+    if len(rows) != calls * len(labels):
+        raise SystemExit("expected %d dispatches in the floor trace" % (calls * len(labels)))
+    out = []
+    for li, label in enumerate(labels):
+        part = rows[li * calls:(li + 1) * calls]
+        ds = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in part]
+        short = part[0]["Kernel_Name"].split("(")[0].replace("void ", "")[:60]
+        out.append("| %s | `%s` | %d | %.3f | %.3f | %.3f |" % (
+            label, short, len(part), statistics.mean(ds), statistics.median(ds), min(ds)))
+    return out
+
+
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_F6F4", "SQ_INSTS_VALU_MFMA_MOPS_F6F4", "SQ_VALU_MFMA_BUSY_CYCLES",
+                 "GRBM_GUI_ACTIVE")
+
+
+def mfma_lines(mfma_dir, calls, trace_us):
+    """Rows of the MFMA table from one --pmc pass over the MFMA counters of
+    a --profile run: per GEMM kernel, the fp4 MFMA instructions and their
+    flops (MOPS x 512) against 2MNK, the MFMA-busy share of the 1024 SIMDs'
+    cycles over the kernel's traced duration `trace_us[(kernel, grid)]` at
+    the 2.4 GHz peak clock, and the useful fp4 rate 2MNK / duration against
+    the dense MXFP4 peak."""
+    import collections
+    import csv
+    import re
+    from microscaled_mxfp4_block_amd import inputs
+    rows = None
+    for f in sorted(os.listdir(mfma_dir)):
+        if f.endswith("counter_collection.csv"):
+            with open(os.path.join(mfma_dir, f)) as fh:
+                rows = list(csv.DictReader(fh))
+    if rows is None:
+        raise SystemExit("no *counter_collection.csv under %s" % mfma_dir)
+    per = collections.OrderedDict()   # (kernel, grid) -> dispatch id -> counter -> value
+    for r in rows:
+        grid = int(r["Grid_Size"]) if "Grid_Size" in r else int(r["Grid_Size_X"])
+        key = (re.sub(r"\(.*", "", r["Kernel_Name"]).replace("void ", ""), grid)
+        d = per.setdefault(key, collections.OrderedDict()).setdefault(r.get("Dispatch_Id", r.get("Correlation_Id")), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    gemms = [(k, v) for k, v in per.items() if k[0].startswith("mx4::gemm_kernel") and len(v) == calls]
+    out = []
+    for w, ((name, grid), disp) in zip(inputs.WORKLOADS, gemms):
+        med = {c: statistics.median(d.get(c, 0.0) for d in disp.values()) for c in MFMA_COUNTERS}
+        flops = med["SQ_INSTS_VALU_MFMA_MOPS_F6F4"] * 512
+        us = trace_us.get((name, grid))
+        busy = med["SQ_VALU_MFMA_BUSY_CYCLES"] / (us * 2400.0 * 1024) if us else float("nan")
+        useful = 2.0 * w.M * w.N * w.K / (us * 1e-6) / (FP4_PEAK_TFLOPS * 1e12) if us else float("nan")
+        out.append("| %s | `%s` | %d | %.0f | %.4g | %.4g | %.3f | %.0f | %.3f | %.2f %% | %.2f %% |" % (
+            w.name, name, grid, med["SQ_INSTS_VALU_MFMA_F6F4"], flops, 2.0 * w.M * w.N * w.K,
+            flops / (2.0 * w.M * w.N * w.K), med["SQ_VALU_MFMA_BUSY_CYCLES"], us or float("nan"),
+            100 * busy, 100 * useful))
+    return out
+
+
+def summarize_profiles(trace_dir, fetch_dir, write_dir, calls_trace, calls_pmc, floor_dir=None, mfma_dir=None):
     """Write profiles/gemm_kernels_trace.md (per-kernel durations from a
     rocprofv3 kernel trace of `bench.py --profile`, HBM bytes from the
     FETCH_SIZE and WRITE_SIZE passes) and profiles/gemm_traffic.json (the
@@ -313,6 +417,30 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, calls_trace, calls_pmc):
                 "fetch_bytes": None if fb is None else round(fb),
                 "write_bytes": None if wb is None else round(wb),
                 "hbm_bytes_per_launch": None if fb is None or wb is None else round(fb + wb)}
+    if floor_dir:
+        lines += ["", "## Reference kernels", "",
+                  "What any launch costs here, from `rocprofv3 --kernel-trace --stats -f csv -d %s -o floor -- "
+                  "python3 bench.py --profile-floor %d`: the near-empty kernel is the floor of every dispatch, and "
+                  "each copy reads and writes as many HBM bytes as one GEMM call of its workload moves (cold, "
+                  "rotating buffers), so it is the time a kernel that only moved those bytes would take."
+                  % (floor_dir, calls_trace), "",
+                  "| reference | kernel | dispatches | avg us | median us | min us |", "|---|---|---|---|---|---|"]
+        lines += floor_lines(floor_dir, calls_trace)
+    if mfma_dir:
+        lines += ["", "## MFMA counters", "",
+                  "`rocprofv3 --pmc %s -f csv -d %s -o mfma -- python3 bench.py --profile %d`, medians over the "
+                  "GEMM dispatches of each workload (counters summed over all XCDs and shader engines). MOPS x 512 "
+                  "is the counter's flop count; it equals 2MNK when no MFMA work goes to padding rows or padding "
+                  "K steps. MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (traced duration x 2.4 GHz x 1024 SIMDs); "
+                  "fp4 utilisation = 2MNK / traced duration / %.1f PFLOP/s (dense MXFP4 peak). The duration is the "
+                  "kernel's average in the trace above." % (" ".join(MFMA_COUNTERS), mfma_dir, calls_pmc,
+                                                           FP4_PEAK_TFLOPS / 1e3), "",
+                  "| workload | kernel | grid | fp4 MFMA insts | MOPS x 512 | 2MNK | ratio | MFMA busy cycles | "
+                  "traced us | MFMA busy | fp4 utilisation |", "|---|---|---|---|---|---|---|---|---|---|---|"]
+        trace_us = {}
+        for (name, grid), ds in durations.items():
+            trace_us[(re.sub(r"\(.*", "", name).replace("void ", ""), int(grid))] = statistics.mean(ds)
+        lines += mfma_lines(mfma_dir, calls_pmc, trace_us)
     out = os.path.join(ROOT, "profiles")
     with open(os.path.join(out, "gemm_kernels_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -334,11 +462,16 @@ def main():
                          "calls per workload, for running under rocprofv3")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: summarise rocprofv3 output of --profile runs into profiles/")
+    ap.add_argument("--profile-floor", type=int, default=0, metavar="CALLS",
+                    help="no timing: CALLS near-empty kernels, then CALLS device copies per workload that move "
+                         "the bytes of one of its GEMM calls, for running under rocprofv3")
+    ap.add_argument("--floor-dir", help="with --summarize: rocprofv3 trace directory of a --profile-floor run")
+    ap.add_argument("--mfma-dir", help="with --summarize: rocprofv3 --pmc directory of the MFMA counter pass")
     ap.add_argument("--summarize-calls", nargs=2, type=int, default=[200, 20], metavar=("TRACE", "PMC"),
                     help="the --profile CALLS of the trace and of the counter runs being summarised")
     args = ap.parse_args()
     if args.summarize:
-        summarize_profiles(*args.summarize, *args.summarize_calls)
+        summarize_profiles(*args.summarize, *args.summarize_calls, floor_dir=args.floor_dir, mfma_dir=args.mfma_dir)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode (run with --gpus 1)",
@@ -351,6 +484,9 @@ def main():
 
     if args.profile:
         profile_run(torch, B, inputs, args.profile)
+        return
+    if args.profile_floor:
+        profile_floor_run(torch, inputs, args.profile_floor)
         return
 
     per_workload = {}
@@ -420,7 +556,7 @@ def main():
             "bytes_per_launch": nbytes,
         },
         "per_workload": per_workload,
-        "launch_floor": launch_floor(torch),
+        "launch_floor": launch_floor(torch, nbytes),
     }
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(HEADLINE, inputs)
