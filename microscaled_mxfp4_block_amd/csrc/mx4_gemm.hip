@@ -115,14 +115,15 @@ __device__ __forceinline__ f32x4 load_partial_agent(const float* src) {
                  __uint_as_float((uint32_t)hi), __uint_as_float((uint32_t)(hi >> 32))};
 }
 
-// 4 consecutive bf16 outputs (n0..n0+3) of row m, masked at N.
+// 4 consecutive bf16 outputs (n0..n0+3) of row m, masked at N.  C is written
+// once and never read back here, so its stores are non-temporal: they do not
+// leave dirty lines in L2 for the end of the kernel to write back.
 __device__ __forceinline__ void store_bf16x4(const GemmParams& p, int m, int n0, const float (&v)[4]) {
     uint16_t* dst = p.C + (size_t)m * p.ldc + n0;
     if (p.c_vec && n0 + 3 < p.N) {
-        uint2 w;
-        w.x = pack_bf16x2(v[0], v[1]);
-        w.y = pack_bf16x2(v[2], v[3]);
-        *(uint2*)dst = w;
+        typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+        __builtin_nontemporal_store(w, (u32x2*)dst);
     } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
@@ -588,7 +589,8 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
     }
     __syncthreads();
     // the staged tile leaves in 16-byte row chunks: consecutive lanes write
-    // consecutive bytes of a row of C
+    // consecutive bytes of a row of C, non-temporal (C is not read again
+    // here; the split-K partials above stay cached for their reader)
     const int m_base = mb0 * kRowBlock;
     const int n_base = nt * WN * NBLK * kRowBlock;
     const bool vec16 = ((uintptr_t)p.C % 16 == 0) && (p.ldc % 8 == 0);
@@ -599,7 +601,7 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
         const u32x4 v = *(const u32x4*)(stage + row * SROW + 8 * c8);
         uint16_t* dst = p.C + (size_t)m * p.ldc + n;
         if (vec16 && n + 7 < p.N) {
-            *(u32x4*)dst = v;
+            __builtin_nontemporal_store(v, (u32x4*)dst);
         } else {
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -680,13 +682,16 @@ GemmFn MX4_CAT(find_gemm_kr, MX4_KR)(const Plan& plan, int rq) {
 
 #if MX4_KR == 1
 // The split-K reduction and the launch helpers live in one object only.
-// Grid (ceil(N / 4 / 256), rows): one thread per 4 consecutive n of row m
-// (rows past 65535 are walked by the y workgroups).  The partials of each
+// Grid (ceil(N / 4 / 64), rows) of one-wave workgroups: one thread per 4
+// consecutive n of row m (rows past 65535 are walked by the y workgroups).
+// Small workgroups spread the loads over more CUs: at M = 16, N = 2112 the
+// 144 one-wave workgroups finish 0.15 us sooner than 48 four-wave ones.  The partials of each
 // batch of 8 splits are all loaded before the first add (padding splits read
 // zeros through the buffer bound), then added in split order.
 constexpr int kReduceBatch = 8;
-__global__ void __launch_bounds__(256) reduce_kernel(GemmParams p) {
-    const int n0 = 4 * (int)(blockIdx.x * 256u + threadIdx.x);
+constexpr int kReduceThreads = 64;
+__global__ void __launch_bounds__(kReduceThreads) reduce_kernel(GemmParams p) {
+    const int n0 = 4 * (int)(blockIdx.x * (unsigned)kReduceThreads + threadIdx.x);
     if (n0 >= p.N) return;
     const Rsrc rp_ = make_rsrc(p.partial, p.partial_bytes);
     const uint32_t split_stride = (uint32_t)p.M * (uint32_t)p.ldp * 4u;
@@ -767,9 +772,9 @@ hipError_t launch_gemm(const GemmLaunch& gl, const GemmParams& p, hipStream_t s)
 }
 
 hipError_t launch_reduce(const GemmParams& p, hipStream_t s) {
-    const unsigned gx = (unsigned)(((p.N + 3) / 4 + 255) / 256);
+    const unsigned gx = (unsigned)(((p.N + 3) / 4 + kReduceThreads - 1) / kReduceThreads);
     const unsigned gy = (unsigned)(p.M < 65535 ? p.M : 65535);
-    return launch_kernel(reduce_kernel, dim3(gx, gy), dim3(256), 0, s, p);
+    return launch_kernel(reduce_kernel, dim3(gx, gy), dim3(kReduceThreads), 0, s, p);
 }
 #endif
 
