@@ -133,8 +133,8 @@ __device__ __forceinline__ void store_bf16x4(const GemmParams& p, int m, int n0,
 
 // The leading scalar arguments arrive preloaded in SGPRs (GemmKernelFn); the
 // kernel derives both operands' layouts from them with the host's own
-// operand_geom, so of the parameter block it reads only what the
-// last-arrival split-K finish needs (counters, splits, mtiles).
+// operand_geom.  The last three (counters, splits, mtiles) are read only by
+// the last-arrival split-K finish.
 // RQ (kAmDirect / kAmBf16 with one 32-row block): how many 8-row chunks of
 // the block each K step loads; rows from 8 RQ on are past M, feed only
 // outputs that are never stored, and are not loaded (for M <= 8 or <= 16 a
@@ -142,7 +142,8 @@ __device__ __forceinline__ void store_bf16x4(const GemmParams& p, int m, int n0,
 template <int MBLK, int NBLK, int WN, int WK, int AM, int KR, int RQ>
 __global__ void __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(2)))
 gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_buf, int lda, int ldc, int M, int N, int K,
-            int steps_per_split, GemmParams p) {
+            int steps_per_split, uint32_t* counters, int splits, int mtiles) {
+    GemmParams p = {};
     {
         const OperandGeom ga = operand_geom(M, K), gb = operand_geom(N, K);
         if constexpr (AM == kAmPrequant) {
@@ -169,6 +170,9 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
         p.RBn = gb.RB;
         p.ldp = gb.RB * kRowBlock;
         p.steps_per_split = steps_per_split;
+        p.counters = counters;
+        p.splits = splits;
+        p.mtiles = mtiles;
     }
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     constexpr bool FUSED = AM == kAmLds;
@@ -768,7 +772,7 @@ bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
 hipError_t launch_gemm(const GemmLaunch& gl, const GemmParams& p, hipStream_t s) {
     const void* a_src = gl.prequant ? (const void*)p.aop : (const void*)p.A;
     return launch_kernel(gl.fn, dim3(gl.gx, gl.gy, gl.gz), dim3(gl.block), gl.lds, s, a_src, p.bp, p.C, p.partial,
-                         p.lda, p.ldc, p.M, p.N, p.K, p.steps_per_split, p);
+                         p.lda, p.ldc, p.M, p.N, p.K, p.steps_per_split, p.counters, p.splits, p.mtiles);
 }
 
 hipError_t launch_reduce(const GemmParams& p, hipStream_t s) {

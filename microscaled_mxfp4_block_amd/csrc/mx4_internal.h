@@ -86,15 +86,18 @@ constexpr int kAmBf16 = 3;       // not at all: bf16 A x dequantised B (the a16w
 bool gemm_plan_supported(const Plan& p);
 int gemm_kr_for(int steps_per_wave);   // K-step budget KR of the kernel for that many steps (0: none)
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split);
-// The GEMM kernels take the call's pointers and shape as ten scalar arguments
-// ahead of the parameter block: the activation source (A, or the
-// pre-quantised operand in the workspace), bp, C, partial, lda, ldc, M, N, K,
-// steps_per_split -- 14 SGPRs.  The kernel sources are compiled with
-// -amdgpu-kernarg-preload-count=14, so the dispatcher places these in SGPRs
-// at wave launch and the first loads wait on no scalar-memory round trip to
-// the argument segment; everything else the common path needs is derived
-// from them.
-typedef void (*GemmKernelFn)(const void*, const uint8_t*, uint16_t*, float*, int, int, int, int, int, int, GemmParams);
+// The GEMM kernels take the call as thirteen scalar arguments (72 bytes of
+// argument segment): the activation source (A, or the pre-quantised operand
+// in the workspace), bp, C, partial, lda, ldc, M, N, K, steps_per_split --
+// the first 14 SGPRs -- then what only the last-arrival split-K finish reads:
+// counters, splits, mtiles.  The kernel sources are compiled with
+// -amdgpu-kernarg-preload-count=14, so the dispatcher places the first ten in
+// SGPRs at wave launch and the first loads wait on no scalar-memory round
+// trip to the argument segment; everything else the kernel needs is derived
+// from them.  A short argument segment also keeps the host's launch cheap:
+// the runtime writes it to device memory on every launch.
+typedef void (*GemmKernelFn)(const void*, const uint8_t*, uint16_t*, float*, int, int, int, int, int, int, uint32_t*,
+                             int, int);
 
 // A resolved GEMM launch: kernel, grid, block and dynamic LDS for a plan.
 struct GemmLaunch {

@@ -254,8 +254,10 @@ def test_planner_rejects_every_spilling_kernel():
 
 def test_gemm_kernels_take_preloaded_arguments():
     """Every GEMM kernel's descriptor asks for its 14 leading argument SGPRs
-    (the scalar fields ahead of the parameter block) to be preloaded at wave
-    launch; the reduction kernel takes the block alone and preloads nothing."""
+    (pointers and shape) to be preloaded at wave launch, and its whole
+    argument segment is the 72 bytes of its thirteen scalars (no parameter
+    block, no hidden arguments); the reduction kernel takes the parameter
+    block alone and preloads nothing."""
     import glob
     build = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "_build")
     asms = glob.glob(os.path.join(build, "mx4_gemm_kr*.s"))
@@ -269,6 +271,8 @@ def test_gemm_kernels_take_preloaded_arguments():
             n = int(re.search(r"\.amdhsa_user_sgpr_kernarg_preload_length (\d+)", body).group(1))
             if "gemm_kernel" in name:
                 assert n == 14, (name, n)
+                size = int(re.search(r"\.amdhsa_kernarg_size (\d+)", body).group(1))
+                assert size == 72, (name, size)
                 seen += 1
             elif "reduce_kernel" in name:
                 assert n == 0, (name, n)
