@@ -118,16 +118,17 @@ __device__ __forceinline__ f32x4 load_partial_agent(const float* src) {
 // 4 consecutive bf16 outputs (n0..n0+3) of row m, masked at N.  C is written
 // once and never read back here, so its stores are non-temporal: they do not
 // leave dirty lines in L2 for the end of the kernel to write back.
-__device__ __forceinline__ void store_bf16x4(const GemmParams& p, int m, int n0, const float (&v)[4]) {
-    uint16_t* dst = p.C + (size_t)m * p.ldc + n0;
-    if (p.c_vec && n0 + 3 < p.N) {
+__device__ __forceinline__ void store_bf16x4(uint16_t* C, int ldc, int N, bool c_vec, int m, int n0,
+                                             const float (&v)[4]) {
+    uint16_t* dst = C + (size_t)m * ldc + n0;
+    if (c_vec && n0 + 3 < N) {
         typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
         const u32x2 w = {pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
         __builtin_nontemporal_store(w, (u32x2*)dst);
     } else {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-            if (n0 + q < p.N) dst[q] = (uint16_t)bf16_rne(v[q]);
+            if (n0 + q < N) dst[q] = (uint16_t)bf16_rne(v[q]);
     }
 }
 
@@ -691,28 +692,33 @@ GemmFn MX4_CAT(find_gemm_kr, MX4_KR)(const Plan& plan, int rq) {
 // Small workgroups spread the loads over more CUs: at M = 16, N = 2112 the
 // 144 one-wave workgroups finish 0.15 us sooner than 48 four-wave ones.  The partials of each
 // batch of 8 splits are all loaded before the first add (padding splits read
-// zeros through the buffer bound), then added in split order.
+// zeros through the buffer bound), then added in split order.  Its arguments
+// are ten scalars (48 bytes, preloaded in SGPRs; the row stride of the y
+// workgroups is one of them, so no hidden arguments), which keeps the host's
+// launch cheap.
 constexpr int kReduceBatch = 8;
 constexpr int kReduceThreads = 64;
-__global__ void __launch_bounds__(kReduceThreads) reduce_kernel(GemmParams p) {
+__global__ void __launch_bounds__(kReduceThreads)
+reduce_kernel(const float* partial, uint16_t* C, uint32_t partial_bytes, int M, int N, int ldp, int ldc, int splits,
+              int c_vec, int mstep) {
     const int n0 = 4 * (int)(blockIdx.x * (unsigned)kReduceThreads + threadIdx.x);
-    if (n0 >= p.N) return;
-    const Rsrc rp_ = make_rsrc(p.partial, p.partial_bytes);
-    const uint32_t split_stride = (uint32_t)p.M * (uint32_t)p.ldp * 4u;
-    for (int m = blockIdx.y; m < p.M; m += gridDim.y) {
-        const uint32_t base = ((uint32_t)m * (uint32_t)p.ldp + (uint32_t)n0) * 4u;
+    if (n0 >= N) return;
+    const Rsrc rp_ = make_rsrc(partial, partial_bytes);
+    const uint32_t split_stride = (uint32_t)M * (uint32_t)ldp * 4u;
+    for (int m = blockIdx.y; m < M; m += mstep) {
+        const uint32_t base = ((uint32_t)m * (uint32_t)ldp + (uint32_t)n0) * 4u;
         f32x4 s = __builtin_bit_cast(f32x4, bload16(rp_, base, 0u));
-        for (int k0 = 1; k0 < p.splits; k0 += kReduceBatch) {
+        for (int k0 = 1; k0 < splits; k0 += kReduceBatch) {
             u32x4 x[kReduceBatch];
 #pragma unroll
             for (int q = 0; q < kReduceBatch; ++q)
-                x[q] = bload16(rp_, k0 + q < p.splits ? base + (uint32_t)(k0 + q) * split_stride : 0x80000000u, 0u);
+                x[q] = bload16(rp_, k0 + q < splits ? base + (uint32_t)(k0 + q) * split_stride : 0x80000000u, 0u);
 #pragma unroll
             for (int q = 0; q < kReduceBatch; ++q)
-                if (k0 + q < p.splits) s += __builtin_bit_cast(f32x4, x[q]);
+                if (k0 + q < splits) s += __builtin_bit_cast(f32x4, x[q]);
         }
         const float v[4] = {s.x, s.y, s.z, s.w};
-        store_bf16x4(p, m, n0, v);
+        store_bf16x4(C, ldc, N, c_vec != 0, m, n0, v);
     }
 }
 
@@ -778,7 +784,8 @@ hipError_t launch_gemm(const GemmLaunch& gl, const GemmParams& p, hipStream_t s)
 hipError_t launch_reduce(const GemmParams& p, hipStream_t s) {
     const unsigned gx = (unsigned)(((p.N + 3) / 4 + kReduceThreads - 1) / kReduceThreads);
     const unsigned gy = (unsigned)(p.M < 65535 ? p.M : 65535);
-    return launch_kernel(reduce_kernel, dim3(gx, gy), dim3(kReduceThreads), 0, s, p);
+    return launch_kernel(reduce_kernel, dim3(gx, gy), dim3(kReduceThreads), 0, s, (const float*)p.partial, p.C,
+                         p.partial_bytes, p.M, p.N, p.ldp, p.ldc, p.splits, p.c_vec, (int)gy);
 }
 #endif
 

@@ -20,16 +20,22 @@
 
 namespace mx4 {
 
-// Natural-layout quantiser.  Grid (ceil(K / 8 / 256), min(rows, 65535)): one
-// lane per 16-byte column of a row (rows past 65535 walked by y); each lane
-// writes its 8 codes as one dword, the first lane of a quad the scale byte.
+// No kernel here reads blockDim or gridDim (the two that walk rows take the
+// grid's y extent as an argument), so each argument segment holds only the
+// kernel's own scalars, no hidden arguments: the host writes that segment on
+// every launch.
+
+// Natural-layout quantiser.  Grid (ceil(K / 8 / 256), rstep = min(rows,
+// 65535)): one lane per 16-byte column of a row (rows past 65535 walked by
+// y); each lane writes its 8 codes as one dword, the first lane of a quad the
+// scale byte.
 __global__ void __launch_bounds__(256) quant_natural_kernel(const uint16_t* __restrict__ x, int rows,
                                                             int K, int ld, uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales) {
+                                                            uint8_t* __restrict__ scales, int rstep) {
     const int c = (int)(blockIdx.x * 256u + threadIdx.x);
     // whole quads leave together: K / 8 is a multiple of 4 and blocks are 256 wide
     if (c >= K / 8) return;
-    for (int r = (int)blockIdx.y; r < rows; r += (int)gridDim.y) {
+    for (int r = (int)blockIdx.y; r < rows; r += rstep) {
         const u32x4 v = load16(x + (size_t)r * ld + (size_t)c * 8);
         uint32_t byte;
         const uint32_t q = quad_quant8(v, byte);
@@ -39,7 +45,7 @@ __global__ void __launch_bounds__(256) quant_natural_kernel(const uint16_t* __re
 }
 
 // Packed-layout quantiser, coalesced.  Grid (ceil(KW * 32 / 256),
-// min(RB * 32, 65535)): one lane per 16-byte column c of row r of the operand
+// rstep = min(RB * 32, 65535)): one lane per 16-byte column c of row r of the operand
 // padded to RB * 32 rows and KW * 4 K steps (rows past 65535 walked by y).
 // The quad of group g = c / 4 quantises it; lane q of the quad writes dword q
 // of the 16-byte code fragment of slot (rb, t, L) = (r / 32, g / 2,
@@ -48,12 +54,12 @@ __global__ void __launch_bounds__(256) quant_natural_kernel(const uint16_t* __re
 // zero codes and byte 0; steps past KS exist only as scale-word bytes.
 __global__ void __launch_bounds__(256) pack_kernel(const uint16_t* __restrict__ x, int rows, int K, int ld,
                                                    uint8_t* __restrict__ packed, int RB, int KS, int KW,
-                                                   size_t code_bytes) {
+                                                   size_t code_bytes, int rstep) {
     const int c = (int)(blockIdx.x * 256u + threadIdx.x);
     if (c >= KW * 32) return;   // whole quads leave together
     const int g = c >> 2, q = c & 3, t = g >> 1, h = g & 1;
     const bool group_live = g < K / kGroup;
-    for (int r = (int)blockIdx.y; r < RB * kRowBlock; r += (int)gridDim.y) {
+    for (int r = (int)blockIdx.y; r < RB * kRowBlock; r += rstep) {
         u32x4 v = {0u, 0u, 0u, 0u};
         if (r < rows && group_live) v = load16(x + (size_t)r * ld + (size_t)c * 8);
         uint32_t byte;
@@ -70,7 +76,7 @@ __global__ void __launch_bounds__(256) pack_kernel(const uint16_t* __restrict__ 
 __global__ void __launch_bounds__(256) unpack_kernel(const uint8_t* __restrict__ packed, int rows, int K,
                                                      int RB, int KS, int KW, size_t code_bytes,
                                                      uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
-    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
     const long long total = (long long)RB * KS * 64;
     if (gid >= total) return;
     const int L = (int)(gid & 63);
@@ -93,7 +99,7 @@ __global__ void __launch_bounds__(256) import_kernel(const uint8_t* __restrict__
                                                      const uint8_t* __restrict__ scales, int rows, int K,
                                                      uint8_t* __restrict__ packed, int RB, int KS, int KW,
                                                      size_t code_bytes) {
-    const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
     const long long total = (long long)RB * KW * kStepsPerWord * 64;
     if (gid >= total) return;
     const int L = (int)(gid & 63);
@@ -116,7 +122,7 @@ hipError_t launch_quant_natural(const uint16_t* x, int rows, int K, int ld, uint
                                 hipStream_t s) {
     const unsigned gx = (unsigned)((K / 8 + 255) / 256);
     const unsigned gy = (unsigned)(rows < 65535 ? rows : 65535);
-    return launch_kernel(quant_natural_kernel, dim3(gx, gy), dim3(256), 0, s, x, rows, K, ld, codes, scales);
+    return launch_kernel(quant_natural_kernel, dim3(gx, gy), dim3(256), 0, s, x, rows, K, ld, codes, scales, (int)gy);
 }
 
 hipError_t launch_pack(const uint16_t* x, int rows, int K, int ld, uint8_t* packed, hipStream_t s) {
@@ -124,7 +130,7 @@ hipError_t launch_pack(const uint16_t* x, int rows, int K, int ld, uint8_t* pack
     const unsigned gx = (unsigned)((g.KW * 32 + 255) / 256);
     const unsigned gy = (unsigned)(g.RB * kRowBlock < 65535 ? g.RB * kRowBlock : 65535);
     return launch_kernel(pack_kernel, dim3(gx, gy), dim3(256), 0, s, x, rows, K, ld, packed, g.RB, g.KS, g.KW,
-                         g.code_bytes);
+                         g.code_bytes, (int)gy);
 }
 
 hipError_t launch_import(const uint8_t* codes, const uint8_t* scales, int rows, int K, uint8_t* packed,

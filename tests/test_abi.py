@@ -256,8 +256,8 @@ def test_gemm_kernels_take_preloaded_arguments():
     """Every GEMM kernel's descriptor asks for its 14 leading argument SGPRs
     (pointers and shape) to be preloaded at wave launch, and its whole
     argument segment is the 72 bytes of its thirteen scalars (no parameter
-    block, no hidden arguments); the reduction kernel takes the parameter
-    block alone and preloads nothing."""
+    block, no hidden arguments); the reduction kernel's is the 48 bytes of
+    its ten scalars, all preloaded."""
     import glob
     build = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "_build")
     asms = glob.glob(os.path.join(build, "mx4_gemm_kr*.s"))
@@ -275,8 +275,25 @@ def test_gemm_kernels_take_preloaded_arguments():
                 assert size == 72, (name, size)
                 seen += 1
             elif "reduce_kernel" in name:
-                assert n == 0, (name, n)
+                size = int(re.search(r"\.amdhsa_kernarg_size (\d+)", body).group(1))
+                assert (n, size) == (12, 48), (name, n, size)
     assert seen > 100
+
+
+def test_quantiser_kernels_have_no_hidden_arguments():
+    """The quantisation kernels (the per-call activation quantisers among
+    them) read no blockDim or gridDim, so their argument segments hold only
+    their own scalars (at most 64 bytes), with no hidden-argument block."""
+    path = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "_build", "mx4_quant.s")
+    if not os.path.exists(path):
+        pytest.skip("no device assembly under _build (run the package build first)")
+    text = open(path).read()
+    seen = 0
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S):
+        size = int(re.search(r"\.amdhsa_kernarg_size (\d+)", m.group(2)).group(1))
+        assert size <= 64, (m.group(1), size)
+        seen += 1
+    assert seen == 4
 
 
 def test_lds_dma_tiles_are_read_only_after_their_loads_land():
