@@ -172,7 +172,8 @@ Plan choose_plan_a16w4(int M, int N, int K) {
 
 // Everything of a call that depends on the shape and plan only: checked
 // once, then kept in a small per-thread cache, so that a repeated call only
-// checks its pointers, patches them into the parameter block and launches.
+// checks its pointers, patches them into its copy of the call's GemmParams and
+// launches.
 struct Prepared {
     int M, N, K, lda, ldc;
     Plan plan;

@@ -41,9 +41,12 @@ inline hipError_t launch_kernel(void (*kernel)(P...), dim3 grid, dim3 block, siz
 constexpr size_t kCounterBytes = 16384;
 constexpr int kMaxCounters = (int)(kCounterBytes / 4);
 
-// Arguments of the GEMM and reduction kernels.  The MFMA's first operand is
-// the weight tile (rows = N), the second the activation tile (rows = M), so
-// each lane's 16 outputs are runs of 4 consecutive n for one m.
+// Everything a GEMM call needs: its pointers, shape and derived layout.  The
+// host builds it once per prepared call; the launches pass the kernels the
+// few scalars they take from it, and the GEMM kernel rebuilds the rest from
+// those scalars in a local copy.  The MFMA's first operand is the weight tile
+// (rows = N), the second the activation tile (rows = M), so each lane's 16
+// outputs are runs of 4 consecutive n for one m.
 struct GemmParams {
     const uint16_t* A;        // bf16 activations [M, lda] (quantised in the GEMM when fused)
     int lda;
