@@ -40,9 +40,13 @@ def algorithmic_bytes(M, N, K):
 
 
 def kernel_source_hash():
+    """Hash of the sources the GPU code is built from (the .hip files and the
+    headers they include), not of the host-only sources."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "microscaled_mxfp4_block_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
+        if not name.endswith((".hip", ".h")):
+            continue
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]

@@ -54,7 +54,7 @@ enum {
     MX_EINVAL = -1,   /* bad shape or leading dimension (M, N, K <= 0, K % 32 != 0, ld too small) */
     MX_EALIGN = -2,   /* null or misaligned pointer */
     MX_ESPACE = -3,   /* output, packed or workspace buffer too small */
-    MX_EHIP = -4,     /* a HIP launch failed (hipGetLastError after the launch) */
+    MX_EHIP = -4,     /* a HIP launch failed (the status hipLaunchKernel returned) */
     MX_EPLAN = -5     /* an explicit plan that the library cannot run for this shape */
 };
 
