@@ -224,7 +224,7 @@ def cpu_baseline(idx, inputs, seconds=10.0):
                       "B quantised once outside the timing" % (len(times), w.name)}
 
 
-def profile_run(torch, B, inputs, calls):
+def profile_run(torch, B, inputs, calls, graph=False):
     n = 256 << 20
     src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
     dst = torch.empty_like(src)
@@ -235,10 +235,27 @@ def profile_run(torch, B, inputs, calls):
     del src, dst
     for idx in range(len(inputs.WORKLOADS)):
         st = Setup(idx, torch, B, inputs)
-        for i in range(calls):
-            st.call(i)
+        if graph:
+            # the calls captured once into a HIP graph and replayed: the
+            # dispatches then follow each other as in an untraced eager loop
+            s = torch.cuda.Stream()
+            s.wait_stream(torch.cuda.current_stream())
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=s):
+                handle = torch.cuda.current_stream().cuda_stream
+                for i in range(calls):
+                    if st.fn(*st.args[i % st.copies][:-1], handle):
+                        raise RuntimeError("mx_gemm failed under capture")
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            del g
+        else:
+            for i in range(calls):
+                st.call(i)
         torch.cuda.synchronize()
-        print("profiled %s plan %s: %d calls" % (st.w.name, st.plan, calls), flush=True)
+        print("profiled %s plan %s: %d calls%s" % (st.w.name, st.plan, calls, " (graph replay)" if graph else ""),
+              flush=True)
         del st
         torch.cuda.empty_cache()
 
@@ -466,6 +483,8 @@ def main():
                          "calls per workload, for running under rocprofv3")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: summarise rocprofv3 output of --profile runs into profiles/")
+    ap.add_argument("--graph", action="store_true",
+                    help="with --profile: capture each workload's calls into a HIP graph and replay it once")
     ap.add_argument("--profile-floor", type=int, default=0, metavar="CALLS",
                     help="no timing: CALLS near-empty kernels, then CALLS device copies per workload that move "
                          "the bytes of one of its GEMM calls, for running under rocprofv3")
@@ -487,7 +506,7 @@ def main():
     from microscaled_mxfp4_block_amd import inputs
 
     if args.profile:
-        profile_run(torch, B, inputs, args.profile)
+        profile_run(torch, B, inputs, args.profile, graph=args.graph)
         return
     if args.profile_floor:
         profile_floor_run(torch, inputs, args.profile_floor)
