@@ -343,3 +343,22 @@ def test_shapes_past_the_addressing_limit_are_refused():
         B.mx_gemm_workspace_bytes(1, 32768, 32768)
     assert e.value.code == B.MX_EINVAL
     assert B.mx_gemm_workspace_bytes(64, 32768, 32736) > 0
+
+
+def test_bench_algorithmic_bytes_of_the_workloads():
+    """The roofline numerator of bench.py: A bf16 in + packed B (e2m1 codes
+    and e8m0 scales) + C bf16 out per call, counted by hand from the five
+    shapes (2MK + NK/2 + NK/32 + 2MN)."""
+    import importlib.util
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("mx4_bench", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    expected = {(4, 2880, 512): 4096 + 737280 + 46080 + 23040,
+                (32, 4096, 512): 32768 + 1048576 + 65536 + 262144,
+                (16, 2112, 7168): 229376 + 7569408 + 473088 + 67584,
+                (64, 7168, 2048): 262144 + 7340032 + 458752 + 917504,
+                (256, 3072, 1536): 786432 + 2359296 + 147456 + 1572864}
+    assert [bench.algorithmic_bytes(w.M, w.N, w.K) for w in WORKLOADS] == \
+        [expected[(w.M, w.N, w.K)] for w in WORKLOADS]
+    assert sorted(expected.values()) == sorted([810496, 1409024, 8339456, 8978432, 4866048])
