@@ -633,3 +633,55 @@ def test_gemm_from_several_host_threads():
     for t in threads:
         t.join(timeout=120)
     assert not errors, errors
+
+
+@pytest.mark.gpu
+def test_random_shapes_and_plans():
+    """150 seeded random cases: M in [1, ~315], N in [1, ~720], K a multiple
+    of 32 up to 3072, half of them with one binade per 32-element group
+    (2^-20 .. 2^20).  Each case checks the activation codes and scales
+    bit-exactly, C of the chosen plan and of one random plan the planner
+    accepts (any activation mode, split and finish) to the C tolerance, and
+    the a16wfp4 product against its oracle."""
+    import itertools
+    import random
+    rng = random.Random(20261203)
+    fields = ["mb", "nb", "wn", "wk", "splits", "amode", "finish"]
+    cands = list(itertools.product([1, 2], [1, 2], [1, 2], [1, 2, 4, 8, 16], [1, 2, 3, 4, 7, 8], [0, 1, 2], [0, 1]))
+    for case in range(150):
+        M = max(1, int(round(2 ** rng.uniform(0, 8.3))))
+        N = max(1, int(round(2 ** rng.uniform(0, 9.5))))
+        K = 32 * rng.randint(1, 96)
+        g = torch.Generator().manual_seed(rng.randrange(1 << 30))
+        A = torch.randn(M, K, generator=g)
+        Bf = torch.randn(N, K, generator=g)
+        if rng.random() < 0.5:
+            A = A * torch.pow(2.0, torch.randint(-20, 21, (M, K // 32), generator=g).float()).repeat_interleave(32, 1)
+            Bf = Bf * torch.pow(2.0, torch.randint(-20, 21, (N, K // 32), generator=g).float()).repeat_interleave(32, 1)
+        A, Bm = A.to(torch.bfloat16), Bf.to(torch.bfloat16)
+        Ab, Bb = inputs.bits(A), inputs.bits(Bm)
+        plans = [None]
+        for _ in range(50):
+            pl = dict(zip(fields, rng.choice(cands)))
+            if pl["splits"] == 1 and pl["finish"] == 1:
+                continue
+            try:
+                B.mx_gemm_workspace_bytes(M, N, K, pl)
+            except B.MxError:
+                continue
+            plans.append(pl)
+            break
+        say("random case %d: M=%d N=%d K=%d plans %s" % (case, M, N, K, plans))
+        Ad, Bd = to_dev(A), to_dev(Bm)
+        packed = B.mx_pack_weight(Bd)
+        ref = oracle.gemm(Ab, Bb)
+        for pl in plans:
+            assert_c_close(gpu_bits(B.mx_gemm(Ad, packed, N, plan=pl)), ref,
+                           "random case %d %s plan %s" % (case, (M, N, K), pl))
+        codes, scales = B.mx_quant_act(Ad)
+        rc, rs = oracle.quant(Ab)
+        torch.cuda.synchronize()
+        assert np.array_equal(codes.cpu().numpy(), rc) and np.array_equal(scales.cpu().numpy(), rs), \
+            "random case %d: activation codes or scales differ" % case
+        assert_c_close(gpu_bits(B.mx_gemm_a16w4(Ad, packed, N)), oracle.gemm_a16w4(Ab, Bb),
+                       "random case %d %s a16wfp4" % (case, (M, N, K)))
