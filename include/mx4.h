@@ -138,7 +138,8 @@ typedef struct mx_plan {
     int nb;          /* 32-column blocks of N per wave (1 or 2) */
     int wn;          /* waves along N per workgroup (1 or 2) */
     int wk;          /* waves along K per workgroup (1, 2, 4, 8 or 16; wn*wk <= 16) */
-    int splits;      /* workgroups along K; > 1 adds a reduction kernel */
+    int splits;      /* workgroups along K; > 1 adds a reduction kernel
+                        unless finish is MX_FINISH_LAST_ARRIVAL */
     int amode;       /* where A is quantised: one of MX_AMODE_* */
     int finish;      /* who sums the split-K partials: one of MX_FINISH_* */
 } mx_plan;
@@ -148,8 +149,10 @@ enum {
     MX_AMODE_LDS = 0,       /* each GEMM workgroup quantises its slice of A into
                                LDS, shared by its waves */
     MX_AMODE_PREQUANT = 1,  /* a first kernel quantises A into the workspace */
-    MX_AMODE_DIRECT = 2,    /* each wave quantises the A fragments it consumes
-                               in registers (no LDS, no barrier) */
+    MX_AMODE_DIRECT = 2,    /* each wave loads the A rows of the fragments it
+                               consumes (through its own LDS tiles) and
+                               quantises them in registers; no workgroup
+                               barrier before the MFMAs */
     MX_AMODE_BF16 = 3       /* A is NOT quantised: the a16wfp4 product of
                                mx_gemm_a16w4 (a different result) */
 };
