@@ -105,8 +105,13 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
     return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two fp32 -> two bf16 (lo in the low half), round to nearest even: the
+// gfx950 v_cvt_pk_bf16_f32, which rounds by the kernel's fp32 round mode
+// (nearest even) and keeps fp32 denormals (the kernels' denormal mode), so
+// it equals bf16_rne on every finite input.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-    return bf16_rne(lo) | (bf16_rne(hi) << 16);
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // One block-scaled fp4 x fp4 MFMA step: acc += (A_tile * 2^sa) x (B_tile * 2^sb)^T

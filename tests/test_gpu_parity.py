@@ -685,3 +685,38 @@ def test_random_shapes_and_plans():
             "random case %d: activation codes or scales differ" % case
         assert_c_close(gpu_bits(B.mx_gemm_a16w4(Ad, packed, N)), oracle.gemm_a16w4(Ab, Bb),
                        "random case %d %s a16wfp4" % (case, (M, N, K)))
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("scale_exp", [0, -67], ids=["normal", "subnormal"])
+def test_gemm_bf16_rounding_ties_bit_exact(scale_exp):
+    """The epilogue's fp32 -> bf16 rounding, bit-exactly: with A and B made of
+    0 and 2^e (e = 0, or -67 so that each product is 2^-134, below bf16's
+    normal range), C[m, n] = 2^(2e) * (count of common ones) is an exact fp32
+    sum, and the counts 200..512 hit bf16 ties (odd counts above 256, and odd
+    multiples of 2^-134, halfway between bf16 subnormals).  Round to nearest
+    even must give the oracle's once-rounded result exactly, on every plan
+    mode and split."""
+    M, N, K = 8, 160, 512
+    v = 2.0 ** scale_exp
+    rows_a = [200 + 39 * m for m in range(M)]                 # ones in A's first k_m columns
+    rows_b = [201 + 2 * n for n in range(N)]                  # ones in B's first k_n columns
+    A = torch.zeros(M, K)
+    for m, k in enumerate(rows_a):
+        A[m, :min(k, K)] = v
+    Bf = torch.zeros(N, K)
+    for n, k in enumerate(rows_b):
+        Bf[n, :min(k, K)] = v
+    A, Bm = A.to(torch.bfloat16), Bf.to(torch.bfloat16)
+    ref = oracle.gemm(inputs.bits(A), inputs.bits(Bm))
+    Ad, packed = to_dev(A), B.mx_pack_weight(to_dev(Bm))
+    for plan in [None, dict(mb=1, nb=1, wn=1, wk=4, splits=1, amode=0, finish=0),
+                 dict(mb=1, nb=1, wn=1, wk=2, splits=1, amode=1, finish=0),
+                 dict(mb=1, nb=1, wn=1, wk=1, splits=4, amode=2, finish=0),
+                 dict(mb=1, nb=1, wn=1, wk=2, splits=2, amode=2, finish=1)]:
+        say("rounding ties, scale 2^%d, plan %s" % (scale_exp, plan))
+        got = gpu_bits(B.mx_gemm(Ad, packed, N, plan=plan))
+        assert np.array_equal(got, ref), "plan %s: %d outputs differ from round-to-nearest-even" % (
+            plan, int((got != ref).sum()))
+    got16 = gpu_bits(B.mx_gemm_a16w4(Ad, packed, N))
+    assert np.array_equal(got16, oracle.gemm_a16w4(inputs.bits(A), inputs.bits(Bm)))
