@@ -42,7 +42,8 @@
 //      rounded to bf16, staged in LDS and stored in 16-byte row chunks.
 //      When K is split over workgroups, each writes fp32 partials and
 //      either reduce_kernel sums them in split order (a second launch), or
-//      the last workgroup of a tile to arrive does (one launch): its arrival
+//      the last workgroup of a tile to arrive does (one launch): once every
+//      wave has waited for its own partial stores to complete, its arrival
 //      is counted by an agent-scope atomic on a per-tile counter, the
 //      partials are written and read with agent-scope (L2-coherent across
 //      XCDs) accesses, and that workgroup returns the counter to zero.
@@ -566,8 +567,12 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
     }
     if (partial) {
         if (!finish_here) return;   // reduce_kernel sums the partials
-        // Every wave's partial stores have completed (the barrier waits for
-        // them); one atomic per workgroup counts the arrival at this tile.
+        // A workgroup barrier does not wait for vector memory: every wave
+        // first waits until its own partial stores have completed (vmcnt
+        // counts stores on gfx9; they are agent-scope, so complete means
+        // visible to every XCD), then the barrier, then one atomic per
+        // workgroup counts the arrival at this tile.
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
         if (tid == 0) {
             uint32_t* counter = p.counters + (nt * p.mtiles + mt);

@@ -361,3 +361,33 @@ def test_bench_algorithmic_bytes_of_the_workloads():
     assert [bench.algorithmic_bytes(w.M, w.N, w.K) for w in WORKLOADS] == \
         [expected[(w.M, w.N, w.K)] for w in WORKLOADS]
     assert sorted(expected.values()) == sorted([810496, 1409024, 8339456, 8978432, 4866048])
+
+
+def test_split_k_partials_complete_before_arrival():
+    """In every GEMM kernel, the last-arrival split-K finish counts a
+    workgroup's arrival (the agent-scope atomic add on the tile counter) only
+    after a full vmcnt(0) wait that follows the wave's last agent-scope
+    (sc1) partial store: a workgroup barrier does not wait for vector
+    memory, so without that wait the last workgroup could sum partials that
+    have not landed."""
+    import glob
+    build = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "_build")
+    asms = glob.glob(os.path.join(build, "mx4_gemm_kr*.s"))
+    if not asms:
+        pytest.skip("no device assembly under _build (run the package build first)")
+    checked = 0
+    for path in asms:
+        text = open(path).read()
+        for m in re.finditer(r"^(_ZN3mx411gemm_kernel\S*):.*?s_endpgm", text, re.S | re.M):
+            body = m.group(0).splitlines()
+            atomics = [k for k, ln in enumerate(body) if re.match(r"^\s*global_atomic_add\b", ln)]
+            if not atomics:
+                continue
+            stores = [k for k, ln in enumerate(body[:atomics[0]])
+                      if re.match(r"^\s*global_store\w*\s.*\bsc1\b", ln)]
+            assert stores, (m.group(1), "no agent-scope partial store before the arrival atomic")
+            between = body[stores[-1] + 1:atomics[0]]
+            assert any(re.search(r"s_waitcnt\s.*vmcnt\(0\)", ln) for ln in between), \
+                (m.group(1), "arrival counted before the partial stores completed")
+            checked += 1
+    assert checked > 50

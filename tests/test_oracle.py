@@ -363,3 +363,81 @@ def test_a16w4_all_ones():
         A = np.full((2, K), 0x3F80, np.uint16)
         B = np.full((3, K), 0x3F80, np.uint16)
         assert np.all(oracle.gemm_a16w4(A, B) == oracle.bf16_from_double(float(K)))
+
+
+def _bitlevel_e2m1(q32: np.ndarray) -> np.ndarray:
+    """A second e2m1 encoder, vectorised and independent of the oracle: the
+    bit-level method of the kernelindex.com amd-mxfp4-mm pages (submission
+    755056, section "Software MXFP4 quant"), written out from its idea.
+    For |q| >= 6 the code saturates at 7.  Below 1 the fp32 adder does the
+    rounding: adding 2^22 leaves a sum whose ulp is 0.5, so the hardware's
+    round-to-nearest-even puts |q| on the e2m1 subnormal grid {0, 0.5, 1},
+    and the sum's bit pattern minus that of 2^22 counts the halves.  From 1
+    to 6 the code is the fp32 pattern with the exponent rebased from 127 to
+    e2m1's bias 1 and the 22 low significand bits dropped by an integer
+    round-half-to-even (add 2^21 - 1 plus the kept low bit, then shift).
+    The sign bit of q becomes bit 3 of the code."""
+    u = q32.view(np.uint32)
+    sign = (u >> 31).astype(np.uint32)
+    a = (u & np.uint32(0x7FFFFFFF)).view(np.float32)
+    au = a.view(np.uint32)
+    with np.errstate(over="ignore"):
+        small = ((a + np.float32(4194304.0)).view(np.uint32) - np.float32(4194304.0).view(np.uint32)) & 0xFF
+    keep = (au >> 22) & 1
+    normal = ((au - np.uint32(126 << 23) + np.uint32((1 << 21) - 1) + keep) >> 22) & 0xFF
+    code = np.where(a >= np.float32(6.0), 7, np.where(a < np.float32(1.0), small, normal)).astype(np.uint32)
+    return (code | (sign << 3)).astype(np.int64)
+
+
+def test_encoder_matches_the_pages_bit_level_method():
+    """oracle.e2m1_code against the pages' bit-level encoder (fp32 adder
+    rounding below 1, integer round-half-even above) for every bf16 q in
+    [0, 8) of both signs, and for every fp32 q in [0, 8) on a 2^-14 grid
+    plus the neighbours of each tie point."""
+    h = np.arange(0, 0x4100, dtype=np.uint32)            # bf16 0 .. 8 (0x4100 = 8.0)
+    pos = (h << 16).view(np.float32)
+    qs = [pos, -pos, np.arange(0, 8 * 16384, dtype=np.float64).astype(np.float32) / np.float32(16384)]
+    for m in (0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0):
+        m32 = np.float32(m)
+        qs.append(np.array([np.nextafter(m32, np.float32(0)), m32, np.nextafter(m32, np.float32(9))], np.float32))
+    q = np.concatenate(qs).astype(np.float32)
+    ref = _bitlevel_e2m1(q)
+    got = np.array([oracle.e2m1_code(abs(float(v))) | (8 if np.signbit(v) else 0) for v in q], np.int64)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(float(q[i]), int(got[i]), int(ref[i])) for i in bad[:10]]
+
+
+@pytest.mark.parametrize("byte", [0, 1, 2, 100, 125, 126, 127, 128, 200, 253])
+def test_quant_matches_the_pages_bit_level_method(byte):
+    """oracle.quant against the bit-level encoder on whole groups: every
+    finite bf16 value whose group scale is 2^(byte - 127) sits in a group
+    next to an element that fixes that scale; the codes must equal the
+    bit-level encoding of x * 2^-s (exact in fp32 here)."""
+    s = byte - 127
+    # R = 2^(s+2) gives this scale byte; at byte 253 (the largest a finite
+    # input reaches) the largest finite bf16 rounds up to R = 2^128
+    amax = np.ldexp(1.0, s + 2) if byte < 253 else float((np.uint32(0x7F7F) << 16).view(np.float32))
+    h = np.arange(0, 0x7F80, dtype=np.uint32)
+    xs = (h << 16).view(np.float32).astype(np.float64)
+    keep = (xs <= amax) & (xs * np.ldexp(1.0, -s) >= np.ldexp(1.0, -120))   # no fp32 underflow in q
+    if byte <= 2:
+        keep = xs <= amax
+    xs = np.concatenate([xs[keep], -xs[keep]])
+    x_b = (xs.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    n = x_b.size
+    rows = (n + 30) // 31
+    grid = np.zeros((rows, 32), np.uint16)
+    flat = np.zeros(rows * 31, np.uint16)
+    flat[:n] = x_b
+    grid[:, 1:] = flat.reshape(rows, 31)
+    grid[:, 0] = np.uint16(np.float32(amax).view(np.uint32) >> 16)
+    codes, scales = oracle.quant(grid)
+    assert (scales[:, 0] == byte).all()
+    got = np.empty((rows, 32), np.int64)
+    got[:, 0::2] = codes & 0xF
+    got[:, 1::2] = codes >> 4
+    got = got[:, 1:].reshape(-1)[:n]
+    q = (xs * np.ldexp(1.0, -max(s, -127))).astype(np.float32)
+    if byte == 0:
+        q = (xs * np.ldexp(1.0, 127)).astype(np.float32)
+    np.testing.assert_array_equal(got, _bitlevel_e2m1(q))
