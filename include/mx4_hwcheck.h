@@ -1,0 +1,45 @@
+/*
+ * mx4_hwcheck.h -- one-wave checks of the gfx950 instructions the MXFP4 path
+ * is built on (libmx4hw.so).  Test infrastructure only: the product library
+ * libmx4.so does not contain or call these.  Each kernel goes through the
+ * same device wrappers as the GEMM and quantisation kernels, so a test can
+ * compare the instructions' results with a host model element by element.
+ *
+ * All pointers are device pointers; each call enqueues one launch on
+ * `stream` (a hipStream_t, NULL for the default stream) and returns 0, or -1
+ * for a bad size or null pointer, -2 for a misaligned pointer, -4 when the
+ * launch failed.  Nothing is allocated.
+ */
+#ifndef MX4_HWCHECK_H
+#define MX4_HWCHECK_H
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* e2m1 codes of n bf16 values (n % 8 == 0, finite, x_dev 16-byte aligned)
+ * under the scale operand of every scale byte 0 .. bytes-1 (bytes <= 255):
+ * codes_dev receives bytes * n / 2 bytes, row b holding the codes of x under
+ * byte b, two per byte with element 2j in the low nibble -- the conversion
+ * (v_cvt_scalef32_pk_fp4_bf16) the quantisers of the MXFP4 rule use. */
+int mxhw_cvt_fp4(const void* x_dev, int n, int bytes, void* codes_dev, void* stream);
+
+/* All 16 e2m1 codes widened to bf16 times 2^(byte-127) for every scale
+ * byte 0 .. bytes-1 (v_cvt_scalef32_pk_bf16_fp4, as the a16wfp4 product
+ * widens its weight): out_dev receives bytes x 16 bf16, 16-byte aligned. */
+int mxhw_widen_fp4(int bytes, void* out_dev, void* stream);
+
+/* One block-scaled fp4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, both
+ * operands e2m1) from a zero accumulator on one wave: lane L passes the 16
+ * bytes a_dev[16L..16L+15] and b_dev[16L..16L+15] as its first and second
+ * operand fragments and the 32-bit words sa_dev[L] and sb_dev[L] as its
+ * scale registers; out_dev[16L + e] receives element e of lane L's
+ * accumulator (fp32, 64 x 16). */
+int mxhw_mfma_fp4(const void* a_dev, const void* b_dev, const void* sa_dev, const void* sb_dev,
+                  void* out_dev, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MX4_HWCHECK_H */

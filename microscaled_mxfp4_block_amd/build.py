@@ -66,6 +66,8 @@ def _device_asm(item):
 
 
 EXT = os.path.join(HERE, "_mx4ext.so")
+HWLIB = os.path.join(HERE, "libmx4hw.so")
+HWSRC = ("mx4_hwcheck.hip", [], "mx4_hwcheck")
 
 
 def build_ext():
@@ -79,15 +81,20 @@ def build_ext():
 
 
 def build(verbose: bool = False) -> str:
-    """Compile every source and link libmx4.so (plus the fast-call module); returns its path."""
+    """Compile every source and link libmx4.so (plus the fast-call module and
+    the hardware-check library of the tests); returns libmx4.so's path."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    kernels = [s for s in SOURCES if s[0].endswith(".hip")]
+    kernels = [s for s in SOURCES if s[0].endswith(".hip")] + [HWSRC]
     with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+        objs = list(ex.map(_compile, SOURCES + [HWSRC]))
         list(ex.map(_device_asm, kernels))
+    hw_obj = objs.pop()
     tmp = LIB + ".tmp%d" % os.getpid()
     _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp] + objs)
     os.replace(tmp, LIB)
+    tmp = HWLIB + ".tmp%d" % os.getpid()
+    _run([HIPCC, "-shared", "-fPIC", "--offload-arch=" + ARCH, "-o", tmp, hw_obj])
+    os.replace(tmp, HWLIB)
     build_ext()
     if verbose:
         print("built", LIB, "and", EXT)

@@ -1,0 +1,92 @@
+// mx4_hwcheck.hip -- one-wave checks of the two gfx950 instructions the MXFP4
+// path rests on, through the same device wrappers the GEMM and quantisation
+// kernels use (mx4_device.h).  Test infrastructure: built into its own
+// library (libmx4hw.so, include/mx4_hwcheck.h), never linked into libmx4.so.
+//
+//   mxhw_cvt_fp4   every input bf16 converted to an e2m1 code under the scale
+//                  operand of each scale byte (v_cvt_scalef32_pk_fp4_bf16 via
+//                  cvt8 / scale_operand), as the quantisers convert;
+//   mxhw_widen_fp4 every e2m1 code widened to bf16 under each scale byte
+//                  (v_cvt_scalef32_pk_bf16_fp4 via widen8_fp4), as the
+//                  a16wfp4 product does;
+//   mxhw_mfma_fp4  one v_mfma_scale_f32_32x32x64_f8f6f4 on per-lane fragments
+//                  and scale registers given by the caller (mfma_fp4_32x32x64),
+//                  writing every lane's 16 accumulators.
+#include "mx4_device.h"
+#include "../../include/mx4_hwcheck.h"
+
+namespace mx4 {
+
+// Grid (ceil(n / 8 / 64), bytes): lane i of block x converts the 8 bf16
+// x[8 i .. 8 i + 7] under scale byte blockIdx.y into one dword of codes.
+__global__ void __launch_bounds__(64) hw_cvt_kernel(const uint16_t* __restrict__ x, int n8,
+                                                    uint32_t* __restrict__ codes) {
+    const int i = (int)(blockIdx.x * 64u + threadIdx.x);
+    if (i >= n8) return;
+    const u32x4 v = *(const u32x4*)(x + 8 * (size_t)i);
+    const float sc = scale_operand(blockIdx.y);
+    codes[(size_t)blockIdx.y * n8 + i] = cvt8(v.x, v.y, v.z, v.w, sc);
+}
+
+// Grid (bytes): lane L < 2 widens the codes 8 L .. 8 L + 7 (all 16 codes)
+// under scale byte blockIdx.x into 8 bf16.
+__global__ void __launch_bounds__(64) hw_widen_kernel(uint16_t* __restrict__ out) {
+    const int L = threadIdx.x;
+    if (L >= 2) return;
+    // codes 8 L .. 8 L + 7, element e in nibble e
+    const uint32_t codes = L == 0 ? 0x76543210u : 0xFEDCBA98u;
+    const bf16x8 v = widen8_fp4(codes, scale_operand(blockIdx.x));
+    *(bf16x8*)(out + (size_t)blockIdx.x * 16 + 8 * L) = v;
+}
+
+// One wave: lane L passes fragment bytes a[16 L .. 16 L + 15] and
+// b[16 L .. 16 L + 15] and the scale registers sa[L], sb[L] to one scaled
+// MFMA from a zero accumulator; out[16 L + e] is its element e.
+__global__ void __launch_bounds__(64) hw_mfma_kernel(const uint8_t* __restrict__ a, const uint8_t* __restrict__ b,
+                                                     const uint32_t* __restrict__ sa,
+                                                     const uint32_t* __restrict__ sb, float* __restrict__ out) {
+    const int L = threadIdx.x;
+    const u32x4 fa = *(const u32x4*)(a + 16 * L);
+    const u32x4 fb = *(const u32x4*)(b + 16 * L);
+    f32x16 acc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+    acc = mfma_fp4_32x32x64(fa, fb, acc, sa[L], sb[L]);
+    mfma_result_fence(acc);
+#pragma unroll
+    for (int e = 0; e < 16; ++e) out[16 * L + e] = acc[e];
+}
+
+}  // namespace mx4
+
+extern "C" {
+
+int mxhw_cvt_fp4(const void* x_dev, int n, int bytes, void* codes_dev, void* stream) {
+    if (n <= 0 || n % 8 != 0 || bytes <= 0 || bytes > 255 || !x_dev || !codes_dev) return -1;
+    if ((uintptr_t)x_dev % 16 || (uintptr_t)codes_dev % 4) return -2;
+    const int n8 = n / 8;
+    hipLaunchKernelGGL(mx4::hw_cvt_kernel, dim3((unsigned)((n8 + 63) / 64), (unsigned)bytes), dim3(64), 0,
+                       (hipStream_t)stream, (const uint16_t*)x_dev, n8, (uint32_t*)codes_dev);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int mxhw_widen_fp4(int bytes, void* out_dev, void* stream) {
+    if (bytes <= 0 || bytes > 255 || !out_dev) return -1;
+    if ((uintptr_t)out_dev % 16) return -2;
+    hipLaunchKernelGGL(mx4::hw_widen_kernel, dim3((unsigned)bytes), dim3(64), 0, (hipStream_t)stream,
+                       (uint16_t*)out_dev);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int mxhw_mfma_fp4(const void* a_dev, const void* b_dev, const void* sa_dev, const void* sb_dev, void* out_dev,
+                  void* stream) {
+    if (!a_dev || !b_dev || !sa_dev || !sb_dev || !out_dev) return -1;
+    if ((uintptr_t)a_dev % 16 || (uintptr_t)b_dev % 16 || (uintptr_t)sa_dev % 4 || (uintptr_t)sb_dev % 4 ||
+        (uintptr_t)out_dev % 4)
+        return -2;
+    hipLaunchKernelGGL(mx4::hw_mfma_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, (const uint8_t*)a_dev,
+                       (const uint8_t*)b_dev, (const uint32_t*)sa_dev, (const uint32_t*)sb_dev, (float*)out_dev);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+}  // extern "C"

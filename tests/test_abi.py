@@ -391,3 +391,18 @@ def test_split_k_partials_complete_before_arrival():
                 (m.group(1), "arrival counted before the partial stores completed")
             checked += 1
     assert checked > 50
+
+
+def test_hwcheck_library_exports_its_header():
+    """libmx4hw.so (the tests' hardware checks) exports every function that
+    include/mx4_hwcheck.h declares, and libmx4.so exports none of them."""
+    hdr = open(os.path.join(ROOT, "include", "mx4_hwcheck.h")).read()
+    names = sorted(set(re.findall(r"^\s*int\s+(mxhw_\w+)\s*\(", hdr, re.M)))
+    assert len(names) == 3
+    hwlib = os.path.join(ROOT, "microscaled_mxfp4_block_amd", "libmx4hw.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", hwlib], stdout=subprocess.PIPE, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
+    assert set(names) <= exported
+    main = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], stdout=subprocess.PIPE, text=True,
+                          check=True).stdout
+    assert "mxhw_" not in main
