@@ -24,7 +24,9 @@
  *     tensors); *_host pointers are host memory.
  *   - The caller owns every buffer.  The library never allocates, frees or
  *     synchronises; each call only enqueues work on `stream` (a hipStream_t,
- *     NULL for the default stream) and returns.
+ *     NULL for the default stream) and returns.  (mx_gemm_noalloc, for
+ *     callers that cannot allocate, uses a static device array of the
+ *     library instead of a caller's workspace.)
  *   - Arguments are validated on the host before any HIP call; on error the
  *     call returns a negative MX_E* code, enqueues nothing and writes nothing.
  *   - Device pointers read with 128-bit loads must be 16-byte aligned (bf16
@@ -191,6 +193,25 @@ int mx_gemm_a16w4(const void* A_dev, int M, int K, int lda,
                   const void* packed_dev, int N,
                   void* C_dev, int ldc,
                   void* ws_dev, size_t ws_bytes, void* stream);
+
+/* For callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * product, plan, arguments and return codes as mx_gemm, but with no
+ * workspace argument: the workspace lives in a static device array of
+ * MX_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  The call allocates and frees nothing.  On its first call on
+ * a device (the one current on the calling thread, which must be the
+ * stream's) it looks up that device's copy of the array and enqueues one
+ * small kernel that zeroes its arrival counters.
+ *   Returns MX_ESPACE when the shape's workspace (mx_gemm_workspace_bytes)
+ * exceeds MX_NOALLOC_SCRATCH_BYTES, before any HIP call.
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ * call's contents: calls that may overlap in time on one GPU (other streams,
+ * other threads) race on it and must be serialised by the caller. */
+#define MX_NOALLOC_SCRATCH_BYTES (8u << 20)
+int mx_gemm_noalloc(const void* A_dev, int M, int K, int lda,
+                    const void* packed_dev, int N,
+                    void* C_dev, int ldc, void* stream);
 
 #ifdef __cplusplus
 }

@@ -34,8 +34,10 @@ EXPORTS = [
     "mx_strerror", "mx_packed_weight_bytes", "mx_pack_weight", "mx_unpack_weight",
     "mx_import_weight", "mx_quant_act", "mx_gemm_workspace_bytes", "mx_gemm", "mx_gemm_plan",
     "mx_gemm_plan_workspace_bytes", "mx_gemm_with_plan",
-    "mx_gemm_a16w4_plan", "mx_gemm_a16w4_workspace_bytes", "mx_gemm_a16w4",
+    "mx_gemm_a16w4_plan", "mx_gemm_a16w4_workspace_bytes", "mx_gemm_a16w4", "mx_gemm_noalloc",
 ]
+# bytes of the static device workspace of mx_gemm_noalloc (MX_NOALLOC_SCRATCH_BYTES)
+MX_NOALLOC_SCRATCH_BYTES = 8 << 20
 
 
 class MxPlan(ctypes.Structure):
@@ -92,6 +94,7 @@ def lib() -> ctypes.CDLL:
         L.mx_gemm_a16w4_plan.argtypes = [I, I, I, PP]
         L.mx_gemm_a16w4_workspace_bytes.argtypes = [I, I, I, PS]
         L.mx_gemm_a16w4.argtypes = [P, I, I, I, P, I, P, I, P, S, P]
+        L.mx_gemm_noalloc.argtypes = [P, I, I, I, P, I, P, I, P]
         for name in EXPORTS[1:]:
             getattr(L, name).restype = I
         _lib = L
@@ -251,4 +254,19 @@ def mx_gemm_a16w4(A: torch.Tensor, packed: torch.Tensor, N: int, C: Optional[tor
     rc = ext().gemm_a16w4(A.data_ptr(), M, K, lda, packed.data_ptr(), N, C.data_ptr(), ldc, workspace.data_ptr(),
                           workspace.numel(), _stream(stream))
     _check(rc, "mx_gemm_a16w4")
+    return C
+
+
+def mx_gemm_noalloc(A: torch.Tensor, packed: torch.Tensor, N: int, C: Optional[torch.Tensor] = None,
+                    stream=None) -> torch.Tensor:
+    """mx_gemm with the library's static per-GPU workspace instead of a caller's
+    (for callers that cannot allocate); calls on one GPU must not overlap."""
+    M, K, lda = _bf16_matrix(A, "A")
+    if C is None:
+        C = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    Mc, Nc, ldc = _bf16_matrix(C, "C")
+    if (Mc, Nc) != (M, N):
+        raise ValueError("C must be [%d, %d]" % (M, N))
+    _check(lib().mx_gemm_noalloc(A.data_ptr(), M, K, lda, packed.data_ptr(), N, C.data_ptr(), ldc,
+                                 _stream(stream)), "mx_gemm_noalloc")
     return C

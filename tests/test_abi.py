@@ -406,3 +406,18 @@ def test_hwcheck_library_exports_its_header():
     main = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], stdout=subprocess.PIPE, text=True,
                           check=True).stdout
     assert "mxhw_" not in main
+
+
+def test_noalloc_validates_before_any_hip_call():
+    """mx_gemm_noalloc rejects a bad shape (MX_EINVAL) and a shape whose
+    workspace exceeds its static array (MX_ESPACE: 4096^3 pre-quantises an
+    8.4 MB activation) on the host, with fake pointers, before any HIP call;
+    the workloads' workspaces fit."""
+    L = B.lib()
+    assert B.mx_gemm_workspace_bytes(4096, 4096, 4096) > B.MX_NOALLOC_SCRATCH_BYTES
+    assert L.mx_gemm_noalloc(FAKE, 4096, 4096, 4096, FAKE, 4096, FAKE, 4096, None) == B.MX_ESPACE
+    assert L.mx_gemm_noalloc(FAKE, 4, 33, 40, FAKE, 64, FAKE, 64, None) == B.MX_EINVAL
+    for w in WORKLOADS:
+        assert B.mx_gemm_workspace_bytes(w.M, w.N, w.K) <= B.MX_NOALLOC_SCRATCH_BYTES
+    hdr = open(HEADER).read()
+    assert "#define MX_NOALLOC_SCRATCH_BYTES (8u << 20)" in hdr and B.MX_NOALLOC_SCRATCH_BYTES == 8 << 20
