@@ -76,7 +76,8 @@ int mx_packed_weight_bytes(int N, int K, size_t* bytes_host);
 /* One-time weight packing: the MXFP4 rule above applied to B along K (the
  * weight is quantised the same way as the activation), written into the
  * GEMM's tile layout.
- *   B_dev       bf16 [N, K], row stride ldb elements (ldb >= K, ldb % 8 == 0)
+ *   B_dev       bf16 [N, K], row stride ldb elements (ldb >= K, ldb % 8 == 0,
+ *               N * ldb * 2 < 2^31)
  *   packed_dev  output, packed_bytes >= mx_packed_weight_bytes(N, K), 16-B aligned */
 int mx_pack_weight(const void* B_dev, int N, int K, int ldb,
                    void* packed_dev, size_t packed_bytes, void* stream);
@@ -113,7 +114,7 @@ int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host);
 /* C = A x B^T with A quantised on the fly (quantisation, block-scaled MFMA
  * contraction with fp32 accumulation, split-K reduction when planned, bf16
  * round-to-nearest-even epilogue).
- *   A_dev      bf16 [M, K], lda >= K, lda % 8 == 0
+ *   A_dev      bf16 [M, K], lda >= K, lda % 8 == 0, M * lda * 2 < 2^31
  *   packed_dev weight packed by mx_pack_weight for (N, K)
  *   C_dev      bf16 [M, N] output, ldc >= N
  *   ws_dev     workspace of ws_bytes >= mx_gemm_workspace_bytes(M, N, K),
@@ -137,7 +138,8 @@ int mx_gemm(const void* A_dev, int M, int K, int lda,
  * over K / splits of the reduction; its wk waves share that K range. */
 typedef struct mx_plan {
     int mb;          /* 32-row blocks of M per wave (1 or 2) */
-    int nb;          /* 32-column blocks of N per wave (1 or 2) */
+    int nb;          /* 32-column blocks of N per wave (1 or 2; 1, 2 or 4 in
+                        MX_AMODE_STREAM) */
     int wn;          /* waves along N per workgroup (1 or 2) */
     int wk;          /* waves along K per workgroup (1, 2, 4, 8 or 16; wn*wk <= 16) */
     int splits;      /* workgroups along K; > 1 adds a reduction kernel
@@ -155,8 +157,12 @@ enum {
                                consumes (through its own LDS tiles) and
                                quantises them in registers; no workgroup
                                barrier before the MFMAs */
-    MX_AMODE_BF16 = 3       /* A is NOT quantised: the a16wfp4 product of
+    MX_AMODE_BF16 = 3,      /* A is NOT quantised: the a16wfp4 product of
                                mx_gemm_a16w4 (a different result) */
+    MX_AMODE_STREAM = 4     /* as MX_AMODE_DIRECT, but each wave loops over its
+                               K steps with the loads of several steps in
+                               flight (any K per wave; mb = wn = 1,
+                               nb in {1, 2, 4}) */
 };
 
 /* Split-K finishes of a plan (no effect when splits == 1). */

@@ -38,6 +38,17 @@ int mxhw_widen_fp4(int bytes, void* out_dev, void* stream);
 int mxhw_mfma_fp4(const void* a_dev, const void* b_dev, const void* sa_dev, const void* sb_dev,
                   void* out_dev, void* stream);
 
+/* Measurement reference, no arithmetic: `wgs` workgroups of `waves` waves;
+ * workgroup g reads bytes [g*stride, g*stride + chunk) of buf_dev (clipped at
+ * `bytes`, < 2^31; chunk > 0, chunk % 16 == 0) with 128-bit non-temporal
+ * buffer loads, lpl (1, 2, 4, 8 or 16) in flight per lane, starting at byte
+ * (g*rot) % chunk of its piece and wrapping (rot % 16 == 0), and stores one
+ * xor dword per wave to out_dev[g*waves + wave].  stride = chunk streams
+ * disjoint pieces (HBM); stride = 0 has every workgroup read the same piece
+ * (L2). */
+int mxhw_stream_read(const void* buf_dev, unsigned bytes, int wgs, int waves, int lpl,
+                     unsigned chunk, unsigned stride, unsigned rot, void* out_dev, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

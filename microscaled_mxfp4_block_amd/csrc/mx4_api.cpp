@@ -18,8 +18,9 @@ using mx4::kAmBf16;
 using mx4::kAmDirect;
 using mx4::kAmLds;
 using mx4::kAmPrequant;
+using mx4::kAmStream;
 static_assert(kAmLds == MX_AMODE_LDS && kAmPrequant == MX_AMODE_PREQUANT && kAmDirect == MX_AMODE_DIRECT &&
-                  kAmBf16 == MX_AMODE_BF16,
+                  kAmBf16 == MX_AMODE_BF16 && kAmStream == MX_AMODE_STREAM,
               "activation modes of the C ABI and the kernels differ");
 
 namespace {
@@ -78,12 +79,15 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     Layout l;
     l.steps_per_split = (gb.KS + plan.splits - 1) / plan.splits;
     l.splits = (gb.KS + l.steps_per_split - 1) / l.steps_per_split;  // every split non-empty
-    if ((l.steps_per_split + plan.wk - 1) / plan.wk > mx4::kStepsPerWaveMax) return MX_EPLAN;
+    // The stream mode loops over its K steps; the other modes hold all of a
+    // wave's steps in registers at once.
+    const bool stream = plan.amode == kAmStream;
+    if (!stream && (l.steps_per_split + plan.wk - 1) / plan.wk > mx4::kStepsPerWaveMax) return MX_EPLAN;
     // Register budget (no plan may run a kernel that spills).  kAmDirect and
     // kAmBf16 hold the raw bf16 of every fragment of the wave (16 VGPRs per K
     // step and m block) while the weight loads are in flight: at most 128.
     // A 16-wave workgroup leaves each wave 128 VGPRs in all: half that again.
-    {
+    if (!stream) {
         const int kr = mx4::gemm_kr_for((l.steps_per_split + plan.wk - 1) / plan.wk);
         const bool rega = plan.amode == kAmDirect || plan.amode == kAmBf16;
         const bool waves16 = plan.wn * plan.wk == 16;
@@ -317,6 +321,7 @@ int mx_pack_weight(const void* B_dev, int N, int K, int ldb, void* packed_dev, s
     int rc = check_operand_shape(N, K);
     if (rc) return rc;
     if (ldb < K || ldb % 8 != 0) return MX_EINVAL;
+    if ((unsigned long long)N * ldb * 2 >= (1ULL << 31)) return MX_EINVAL;   // 32-bit buffer offsets
     if (!aligned(B_dev, 16) || !aligned(packed_dev, 16)) return MX_EALIGN;
     if (packed_bytes < mx4::operand_geom(N, K).total_bytes) return MX_ESPACE;
     return hip_status(mx4::launch_pack((const uint16_t*)B_dev, N, K, ldb, (uint8_t*)packed_dev, (hipStream_t)stream));

@@ -755,6 +755,7 @@ static int row_chunks(const Plan& plan, const GemmParams& p) {
 }
 
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
+    if (plan.amode == kAmStream) return stream_lds_bytes(plan);
     const size_t a_op = plan.amode == kAmLds ? (size_t)plan.mb * steps_per_split * 64 * 17 : 0;
     size_t out = gemm_red_bytes(plan.wn, plan.wk, plan.mb, plan.nb) + gemm_stage_bytes(plan.wn, plan.mb, plan.nb);
     if (plan.amode == kAmDirect || plan.amode == kAmBf16) {   // tiles or slabs alias the epilogue's buffers
@@ -768,12 +769,14 @@ size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
 }
 
 bool gemm_plan_supported(const Plan& plan) {
+    if (plan.amode == kAmStream) return plan.splits >= 1 && find_stream_kernel(plan, 4) != nullptr;
     return plan.splits >= 1 && find_kernel(plan, 1) != nullptr;
 }
 
 bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
     const int per_wave = (p.steps_per_split + plan.wk - 1) / plan.wk;
-    GemmFn fn = find_kernel(plan, gemm_kr_for(per_wave), row_chunks(plan, p));
+    GemmFn fn = plan.amode == kAmStream ? find_stream_kernel(plan, row_chunks(plan, p))
+                                        : find_kernel(plan, gemm_kr_for(per_wave), row_chunks(plan, p));
     if (!fn) return false;
     *out = GemmLaunch{fn, (unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits, (unsigned)(64 * plan.wn * plan.wk),
                       gemm_lds_bytes(plan, p.steps_per_split), plan.amode == kAmPrequant};

@@ -12,6 +12,12 @@
 //   mxhw_mfma_fp4  one v_mfma_scale_f32_32x32x64_f8f6f4 on per-lane fragments
 //                  and scale registers given by the caller (mfma_fp4_32x32x64),
 //                  writing every lane's 16 accumulators.
+//
+// And one measurement reference, mxhw_stream_read: a kernel that only reads
+// bytes with the GEMM's kind of loads (128-bit buffer loads, several in
+// flight per lane, non-temporal) and stores one dword per wave, so that a
+// GEMM's time can be set against what merely streaming its bytes costs with
+// the same grid.
 #include "mx4_device.h"
 #include "../../include/mx4_hwcheck.h"
 
@@ -57,9 +63,55 @@ __global__ void __launch_bounds__(64) hw_mfma_kernel(const uint8_t* __restrict__
     for (int e = 0; e < 16; ++e) out[16 * L + e] = acc[e];
 }
 
+// Workgroup g reads bytes [g * stride, g * stride + chunk) of buf (clipped
+// at `bytes`: past it the buffer bound reads zeros), LPL 16-byte loads per
+// lane in flight per round, and xors them into one dword per wave.
+// Workgroup g starts its walk through the piece at byte (g * rot) % chunk and
+// wraps around, so that workgroups reading one piece need not all ask for
+// the same lines at the same time.
+template <int LPL>
+__global__ void __launch_bounds__(1024) hw_stream_kernel(const uint8_t* buf, uint32_t bytes, uint32_t chunk,
+                                                         uint32_t stride, uint32_t rot, uint32_t* out) {
+    const Rsrc r = make_rsrc(buf, bytes);
+    const uint32_t nt = blockDim.x;
+    const uint32_t base = blockIdx.x * stride;
+    const uint32_t start = (uint32_t)(((uint64_t)blockIdx.x * rot) % chunk);
+    u32x4 acc = {0u, 0u, 0u, 0u};
+    for (uint32_t off = 0; off < chunk; off += nt * 16u * LPL) {
+        u32x4 v[LPL];
+#pragma unroll
+        for (int i = 0; i < LPL; ++i) {
+            uint32_t o = off + ((uint32_t)i * nt + threadIdx.x) * 16u;
+            const bool in = o < chunk;
+            o += start;
+            o = o >= chunk ? o - chunk : o;
+            v[i] = bload16<kNonTemporal>(r, in ? base + o : 0x80000000u, 0u);
+        }
+#pragma unroll
+        for (int i = 0; i < LPL; ++i) acc ^= v[i];
+    }
+    const uint32_t x = acc.x ^ acc.y ^ acc.z ^ acc.w;
+    if ((threadIdx.x & 63) == 0) out[blockIdx.x * (nt / 64) + threadIdx.x / 64] = x;
+}
+
 }  // namespace mx4
 
 extern "C" {
+
+int mxhw_stream_read(const void* buf_dev, unsigned bytes, int wgs, int waves, int lpl, unsigned chunk,
+                     unsigned stride, unsigned rot, void* out_dev, void* stream) {
+    if (!buf_dev || !out_dev || wgs <= 0 || waves <= 0 || waves > 16 || bytes >= 0x80000000u || chunk == 0)
+        return -1;
+    if ((uintptr_t)buf_dev % 16 || (uintptr_t)out_dev % 4 || chunk % 16 || rot % 16) return -2;
+    auto k = lpl == 1 ? mx4::hw_stream_kernel<1> : lpl == 2 ? mx4::hw_stream_kernel<2>
+           : lpl == 4 ? mx4::hw_stream_kernel<4> : lpl == 8 ? mx4::hw_stream_kernel<8>
+           : lpl == 16 ? mx4::hw_stream_kernel<16> : nullptr;
+    if (!k) return -1;
+    hipLaunchKernelGGL(k, dim3((unsigned)wgs), dim3((unsigned)(64 * waves)), 0, (hipStream_t)stream,
+                       (const uint8_t*)buf_dev, (uint32_t)bytes, (uint32_t)chunk, (uint32_t)stride,
+                       (uint32_t)rot, (uint32_t*)out_dev);
+    return hipGetLastError() == hipSuccess ? 0 : -4;
+}
 
 int mxhw_cvt_fp4(const void* x_dev, int n, int bytes, void* codes_dev, void* stream) {
     if (n <= 0 || n % 8 != 0 || bytes <= 0 || bytes > 255 || !x_dev || !codes_dev) return -1;

@@ -85,6 +85,7 @@ constexpr int kAmLds = 0;        // by the workgroup, into LDS
 constexpr int kAmPrequant = 1;   // by pack_kernel, into the workspace
 constexpr int kAmDirect = 2;     // by each wave, in registers
 constexpr int kAmBf16 = 3;       // not at all: bf16 A x dequantised B (the a16wfp4 product)
+constexpr int kAmStream = 4;     // by each wave, in registers, in a K loop (gemm_stream_kernel)
 
 bool gemm_plan_supported(const Plan& p);
 int gemm_kr_for(int steps_per_wave);   // K-step budget KR of the kernel for that many steps (0: none)
@@ -110,6 +111,11 @@ struct GemmLaunch {
     bool prequant;   // the activation source is the pre-quantised operand
 };
 bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out);
+// The K-looped kernels of the stream mode (mx4_stream.hip): one M block and
+// one wave along N per workgroup (mb = wn = 1), nb in {1, 2, 4}, wk in
+// {1, 2, 4, 8, 16} (nb <= 2 at 16 waves), rq activation row chunks per step.
+GemmKernelFn find_stream_kernel(const Plan& plan, int rq);
+size_t stream_lds_bytes(const Plan& plan);
 hipError_t launch_gemm(const GemmLaunch& gl, const GemmParams& p, hipStream_t s);
 hipError_t launch_reduce(const GemmParams& p, hipStream_t s);
 

@@ -2,8 +2,9 @@
 //
 //   quant_natural_kernel : bf16 [rows, K] -> codes [rows, K/2] + scales [rows, K/32]
 //   pack_kernel          : bf16 [rows, K] -> packed operand layout (mx4_layout.h),
-//                          coalesced row loads, one DPP quad per group;
-//                          used once for the weight B and per call for A
+//                          one wave per 32 x 64 operand tile, coalesced row
+//                          loads and tile stores; used once for the weight B
+//                          and per call for A
 //   unpack_kernel        : packed operand layout -> natural codes + scales
 //   import_kernel        : natural codes + scales (already quantised elsewhere)
 //                          -> packed operand layout, bytes moved unchanged
@@ -44,31 +45,54 @@ __global__ void __launch_bounds__(256) quant_natural_kernel(const uint16_t* __re
     }
 }
 
-// Packed-layout quantiser, coalesced.  Grid (ceil(KW * 32 / 256),
-// rstep = min(RB * 32, 65535)): one lane per 16-byte column c of row r of the operand
-// padded to RB * 32 rows and KW * 4 K steps (rows past 65535 walked by y).
-// The quad of group g = c / 4 quantises it; lane q of the quad writes dword q
-// of the 16-byte code fragment of slot (rb, t, L) = (r / 32, g / 2,
-// r % 32 + 32 (g % 2)) (mx4_layout.h), the quad's first lane the scale byte
-// into byte t % 4 of that lane's scale word.  Padding rows and groups get
-// zero codes and byte 0; steps past KS exist only as scale-word bytes.
+// Packed-layout quantiser: one wave per operand tile (32 rows x 64 K), four
+// waves per workgroup on four consecutive K steps; grid (ceil(KS / 4),
+// rbstep = min(RB, 65535)), row blocks past 65535 walked by y.  The wave
+// loads its tile's rows whole (8 lanes per 128-byte row segment, four
+// 1 KiB loads) into its own padded LDS slab, reads back the 64 bytes of the
+// 32-element group its lane quantises in the MFMA lane order (row L % 32,
+// group L / 32 of the step), quantises it in registers and stores the tile
+// as the 1 KiB it occupies (16 bytes per lane, one coalesced store) and the
+// scale byte into byte t % 4 of its lane's scale word.  Rows past the matrix
+// and a group past K read zeros (zero codes, byte 0); the wave of the last
+// step also zeroes the scale bytes of the steps past KS in its word.
+constexpr int kPackSlabRow = 144;   // 128 bytes of a row plus 16 of padding
 __global__ void __launch_bounds__(256) pack_kernel(const uint16_t* __restrict__ x, int rows, int K, int ld,
                                                    uint8_t* __restrict__ packed, int RB, int KS, int KW,
-                                                   size_t code_bytes, int rstep) {
-    const int c = (int)(blockIdx.x * 256u + threadIdx.x);
-    if (c >= KW * 32) return;   // whole quads leave together
-    const int g = c >> 2, q = c & 3, t = g >> 1, h = g & 1;
-    const bool group_live = g < K / kGroup;
-    for (int r = (int)blockIdx.y; r < RB * kRowBlock; r += rstep) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (r < rows && group_live) v = load16(x + (size_t)r * ld + (size_t)c * 8);
-        uint32_t byte;
-        const uint32_t codes = quad_quant8(v, byte);
-        const int rb = r >> 5, L = (r & 31) + 32 * h;
-        if (t < KS) *(uint32_t*)(packed + ((size_t)(rb * KS + t) * 64 + L) * 16 + 4 * q) = codes;
-        if (q == 0)
-            packed[code_bytes + ((size_t)(rb * KW + t / kStepsPerWord) * 64 + L) * 4 + t % kStepsPerWord] =
-                (uint8_t)byte;
+                                                   uint32_t code_bytes, int rbstep) {
+    __shared__ __attribute__((aligned(16))) uint8_t slab[4][kRowBlock * kPackSlabRow];
+    const int wave = threadIdx.x >> 6;
+    const int L = threadIdx.x & 63;
+    const int t = (int)blockIdx.x * 4 + wave;
+    if (t >= KS) return;   // whole waves leave; no barrier below
+    const int G = K / kGroup;
+    const Rsrc rx = make_rsrc(x, (uint32_t)rows * (uint32_t)ld * 2u);
+    uint8_t* my = slab[wave];
+    for (int rb = (int)blockIdx.y; rb < RB; rb += rbstep) {
+        u32x4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = q * 64 + L;
+            const int r = c >> 3, j = c & 7;
+            const bool live = 2 * t + (j >> 2) < G;
+            const uint32_t off = (uint32_t)(rb * kRowBlock + r) * (uint32_t)ld * 2u + (uint32_t)t * 128u + j * 16u;
+            v[q] = bload16(rx, live ? off : 0x80000000u, 0u);   // rows past the matrix read zeros
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int c = q * 64 + L;
+            *(u32x4*)(my + (c >> 3) * kPackSlabRow + (c & 7) * 16) = v[q];
+        }
+        u32x4 g[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) g[c] = *(const u32x4*)(my + (L & 31) * kPackSlabRow + (L >> 5) * 64 + c * 16);
+        u32x4 codes;
+        const uint32_t byte = quant_group32(g, codes);
+        *(u32x4*)(packed + ((size_t)(rb * KS + t) * 64 + L) * 16) = codes;
+        uint8_t* word = packed + code_bytes + ((size_t)(rb * KW + t / kStepsPerWord) * 64 + L) * 4;
+        word[t % kStepsPerWord] = (uint8_t)byte;
+        if (t == KS - 1)
+            for (int t2 = KS; t2 < KW * kStepsPerWord; ++t2) word[t2 % kStepsPerWord] = 0;
     }
 }
 
@@ -127,10 +151,10 @@ hipError_t launch_quant_natural(const uint16_t* x, int rows, int K, int ld, uint
 
 hipError_t launch_pack(const uint16_t* x, int rows, int K, int ld, uint8_t* packed, hipStream_t s) {
     const OperandGeom g = operand_geom(rows, K);
-    const unsigned gx = (unsigned)((g.KW * 32 + 255) / 256);
-    const unsigned gy = (unsigned)(g.RB * kRowBlock < 65535 ? g.RB * kRowBlock : 65535);
+    const unsigned gx = (unsigned)((g.KS + 3) / 4);
+    const unsigned gy = (unsigned)(g.RB < 65535 ? g.RB : 65535);
     return launch_kernel(pack_kernel, dim3(gx, gy), dim3(256), 0, s, x, rows, K, ld, packed, g.RB, g.KS, g.KW,
-                         g.code_bytes, (int)gy);
+                         (uint32_t)g.code_bytes, (int)gy);
 }
 
 hipError_t launch_import(const uint8_t* codes, const uint8_t* scales, int rows, int K, uint8_t* packed,

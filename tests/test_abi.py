@@ -166,7 +166,11 @@ def test_explicit_plan_rejections():
            dict(mb=1, nb=1, wn=1, wk=3, splits=1, amode=1),      # no such wave count
            dict(mb=1, nb=1, wn=4, wk=8, splits=4, amode=0),      # no such wave count along N
            dict(mb=1, nb=1, wn=2, wk=16, splits=4, amode=2),     # more than 16 waves
-           dict(mb=1, nb=1, wn=1, wk=4, splits=4, amode=4),      # no such activation mode
+           dict(mb=1, nb=1, wn=1, wk=4, splits=4, amode=5),      # no such activation mode
+           dict(mb=2, nb=1, wn=1, wk=4, splits=1, amode=4),      # stream mode: one M block per workgroup
+           dict(mb=1, nb=1, wn=2, wk=4, splits=1, amode=4),      # stream mode: one wave along N
+           dict(mb=1, nb=4, wn=1, wk=16, splits=1, amode=4),     # stream mode: nb <= 2 at 16 waves
+           dict(mb=1, nb=4, wn=1, wk=4, splits=1, amode=0),      # nb = 4 only in the stream mode
            dict(mb=1, nb=1, wn=1, wk=4, splits=4, amode=0, finish=2),   # no such split-K finish
            dict(mb=1, nb=1, wn=1, wk=4, splits=0, amode=1),
            dict(mb=1, nb=1, wn=1, wk=4, splits=1000, amode=1),   # more splits than K steps
@@ -398,7 +402,7 @@ def test_hwcheck_library_exports_its_header():
     include/mx4_hwcheck.h declares, and libmx4.so exports none of them."""
     hdr = open(os.path.join(ROOT, "include", "mx4_hwcheck.h")).read()
     names = sorted(set(re.findall(r"^\s*int\s+(mxhw_\w+)\s*\(", hdr, re.M)))
-    assert len(names) == 3
+    assert len(names) == 4
     hwlib = os.path.join(ROOT, "microscaled_mxfp4_block_amd", "libmx4hw.so")
     out = subprocess.run(["nm", "-D", "--defined-only", hwlib], stdout=subprocess.PIPE, text=True, check=True).stdout
     exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
@@ -421,3 +425,26 @@ def test_noalloc_validates_before_any_hip_call():
         assert B.mx_gemm_workspace_bytes(w.M, w.N, w.K) <= B.MX_NOALLOC_SCRATCH_BYTES
     hdr = open(HEADER).read()
     assert "#define MX_NOALLOC_SCRATCH_BYTES (8u << 20)" in hdr and B.MX_NOALLOC_SCRATCH_BYTES == 8 << 20
+
+
+def test_stream_kernels_preload_arguments_and_never_spill():
+    """The K-looped stream-mode kernels take the GEMM kernels' 72-byte scalar
+    argument segment with its 14 leading SGPRs preloaded, and none spills
+    VGPRs or uses scratch memory."""
+    path = os.path.join(ROOT, "_build", "mx4_stream.s")
+    if not os.path.exists(path):
+        pytest.skip("no device assembly under _build (run the package build first)")
+    text = open(path).read()
+    seen = 0
+    for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S):
+        name, body = m.group(1), m.group(2)
+        if "gemm_stream_kernel" not in name:
+            continue
+        assert int(re.search(r"\.amdhsa_user_sgpr_kernarg_preload_length (\d+)", body).group(1)) == 14, name
+        assert int(re.search(r"\.amdhsa_kernarg_size (\d+)", body).group(1)) == 72, name
+        assert int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", body).group(1)) == 0, name
+        seen += 1
+    assert seen == 42
+    for block in text.split("  - .agpr_count:")[1:]:
+        if "gemm_stream_kernel" in re.search(r"\.name:\s+(\S+)", block).group(1):
+            assert int(re.search(r"\.vgpr_spill_count:\s+(\d+)", block).group(1)) == 0

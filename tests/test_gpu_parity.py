@@ -262,6 +262,11 @@ PLANS = [
     dict(mb=2, nb=2, wn=1, wk=1, splits=6, amode=1, finish=1),
     dict(mb=1, nb=2, wn=2, wk=4, splits=3, amode=2, finish=1),
     dict(mb=2, nb=1, wn=1, wk=16, splits=2, amode=0, finish=1),
+    dict(mb=1, nb=1, wn=1, wk=1, splits=1, amode=4),
+    dict(mb=1, nb=2, wn=1, wk=4, splits=1, amode=4),
+    dict(mb=1, nb=4, wn=1, wk=8, splits=1, amode=4),
+    dict(mb=1, nb=2, wn=1, wk=16, splits=3, amode=4),
+    dict(mb=1, nb=4, wn=1, wk=2, splits=2, amode=4, finish=1),
 ]
 
 # The a16wfp4 product (amode 3) against its own oracle.
