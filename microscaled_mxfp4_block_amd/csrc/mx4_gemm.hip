@@ -377,6 +377,7 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
                 for (int i = 0; i < MBLK; ++i)
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
+                        if (s0 + ds >= KR) continue;   // odd KR: the last pass holds one step
                         const int c = q * 64 + L;
                         *(u32x4*)(slab + ((i * SR + ds) * kRowBlock + (c >> 3)) * kSlabRow + (c & 7) * 16) =
                             xa[s0 + ds][i][q];
@@ -386,9 +387,11 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
 #pragma unroll
                 for (int i = 0; i < MBLK; ++i)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
+                    for (int c = 0; c < 4; ++c) {
+                        if (s0 + ds >= KR) continue;
                         xa[s0 + ds][i][c] = *(const u32x4*)(slab + ((i * SR + ds) * kRowBlock + (L & 31)) * kSlabRow +
                                                             (L >> 5) * 64 + c * 16);
+                    }
         }
     }
 
@@ -623,7 +626,7 @@ gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_bu
 
 // ---------------------------------------------------------------------------
 // Instantiation table.  This file is compiled once per K-step budget KR
-// (-DMX4_KR=1, 2, 4 or 8); each object instantiates MBLK, NBLK in {1, 2},
+// (-DMX4_KR=1, 2, 3, 4 or 8); each object instantiates MBLK, NBLK in {1, 2},
 // WN in {1, 2}, WK in {1, 2, 4, 8, 16} (at most 16 waves) and the four
 // activation modes with all four row chunks (RQ = 4), and the register modes
 // with MBLK = WN = 1 also with RQ = 1 and 2.
@@ -728,11 +731,15 @@ reduce_kernel(const float* partial, uint16_t* C, uint32_t partial_bytes, int M, 
 }
 
 GemmFn find_gemm_kr2(const Plan& plan, int rq);
+GemmFn find_gemm_kr3(const Plan& plan, int rq);
 GemmFn find_gemm_kr4(const Plan& plan, int rq);
 GemmFn find_gemm_kr8(const Plan& plan, int rq);
 
+// The smallest compiled K-step budget that holds a wave's steps (3 steps per
+// wave -- 24 K steps over 8 waves -- would otherwise run a padding step).
 int gemm_kr_for(int steps_per_wave) {
-    for (int kr = 1; kr <= kStepsPerWaveMax; kr *= 2)
+    static const int kBudgets[] = {1, 2, 3, 4, 8};
+    for (int kr : kBudgets)
         if (steps_per_wave <= kr) return kr;
     return 0;
 }
@@ -741,6 +748,7 @@ static GemmFn find_kernel(const Plan& plan, int kr, int rq = 4) {
     switch (kr) {
         case 1: return find_gemm_kr1(plan, rq);
         case 2: return find_gemm_kr2(plan, rq);
+        case 3: return find_gemm_kr3(plan, rq);
         case 4: return find_gemm_kr4(plan, rq);
         case 8: return find_gemm_kr8(plan, rq);
         default: return nullptr;
