@@ -31,6 +31,8 @@ import statistics
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -532,6 +534,108 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, calls):
     print("\n".join(lines))
 
 
+# The shape grid of the pages (submission 754569, synthesized config CSV):
+# 19 (N, K) weight shapes x batch sizes 1 .. 256.
+GRID_DIM_PAIRS = [
+    (2880, 512), (2112, 7168), (4096, 512), (7168, 2048), (3072, 1536),
+    (2880, 1536), (4096, 1536), (2112, 512), (2112, 2048),
+    (7168, 512), (7168, 1536), (7168, 7168), (3072, 512),
+    (3072, 7168), (3072, 2048), (4096, 2048), (4096, 7168),
+    (2880, 2048), (2880, 7168),
+]
+GRID_BATCH = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+
+
+def regret_candidates(B, M, N, K):
+    """Plans timed against the library's own for one grid shape: the
+    register-quantising mode over wave and split counts and two N widths,
+    the pre-quantising mode over its tile shapes, the LDS mode; only those
+    the planner accepts."""
+    cands = []
+    for nb in (1, 2):
+        for wk in (2, 4, 8):
+            for sp in (1, 2, 4, 7, 8, 14):
+                cands.append(dict(mb=1, nb=nb, wn=1, wk=wk, splits=sp, amode=2, finish=0))
+    for mb, nb, wn, wk in ((1, 1, 1, 8), (2, 1, 1, 8), (2, 2, 1, 8), (1, 1, 1, 4), (2, 1, 2, 8), (2, 2, 1, 4)):
+        for sp in (1, 2, 4):
+            cands.append(dict(mb=mb, nb=nb, wn=wn, wk=wk, splits=sp, amode=1, finish=0))
+    for sp in (1, 2, 4):
+        cands.append(dict(mb=1, nb=1, wn=1, wk=8, splits=sp, amode=0, finish=0))
+    out = []
+    for p in cands:
+        try:
+            B.mx_gemm_workspace_bytes(M, N, K, p)
+        except B.MxError:
+            continue
+        out.append(p)
+    return out
+
+
+def plan_regret(torch, B, inputs, only=None):
+    """Graph-replay GPU time per call of the library's plan and of the
+    candidate plans for every grid shape (weights rotating over copies
+    >= 256 MiB); writes profiles/plan_regret.md and .json."""
+    dev = "cuda:0"
+    results = []
+    pairs = GRID_DIM_PAIRS if only is None else [GRID_DIM_PAIRS[i] for i in only]
+    for (N, K) in pairs:
+        gen = torch.Generator("cpu").manual_seed(5000 + N + K)
+        P0 = B.mx_pack_weight(inputs.bf16_randn(N, K, gen).to(dev))
+        copies = min(200, max(4, -(-(256 << 20) // P0.numel())))
+        Ps = [P0] + [P0.clone() for _ in range(copies - 1)]
+        for M in GRID_BATCH:
+            A0 = inputs.bf16_randn(M, K, gen).to(dev)
+            C0 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            lib_plan = B.mx_gemm_plan(M, N, K)
+            fn = B.ext().gemm_with_plan
+            rows = []
+            for p in [lib_plan] + [c for c in regret_candidates(B, M, N, K) if c != lib_plan]:
+                wsb = B.mx_gemm_workspace_bytes(M, N, K, p)
+                ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=dev)
+                pa = (p["mb"], p["nb"], p["wn"], p["wk"], p["splits"], p["amode"], p["finish"])
+
+                def call(i, stream):
+                    if fn(A0.data_ptr(), M, K, K, Ps[i % copies].data_ptr(), N, C0.data_ptr(), N, ws.data_ptr(),
+                          ws.numel(), *pa, stream):
+                        raise RuntimeError("mx_gemm_with_plan failed")
+                rows.append((graph_time(torch, call, copies, min_seconds=0.02), p))
+                del ws
+            lib_us = rows[0][0]
+            best_us, best = min(rows, key=lambda r: r[0])
+            results.append({"M": M, "N": N, "K": K, "plan": lib_plan, "us": round(lib_us, 3), "best_plan": best,
+                            "best_us": round(best_us, 3), "regret": round(lib_us / best_us, 3),
+                            "candidates": len(rows)})
+            print("regret %4d x %4d x %4d  plan %.3f us  best %.3f us  x%.3f  %s" % (
+                M, N, K, lib_us, best_us, lib_us / best_us, best), file=sys.stderr, flush=True)
+            del A0, C0
+        del Ps, P0
+        torch.cuda.empty_cache()
+    regrets = [r["regret"] for r in results]
+    geo = float(np.exp(np.mean(np.log(regrets)))) if regrets else float("nan")
+    lines = ["# Planner regret on the pages' shape grid", "",
+             "`python3 bench.py --plan-regret`: for each of the %d shapes (19 (N, K) weight shapes of the "
+             "kernelindex.com amd-mxfp4-mm pages' synthesized config CSV, submission 754569, times M = 1 .. 256), "
+             "the HIP-graph-replay GPU time per call of the plan mx_gemm picks (the measured table for the five "
+             "workloads, the model elsewhere) against the fastest of up to %d candidate plans (register-quantising "
+             "mode over waves, splits and N widths; pre-quantising mode over its tiles; LDS mode), weights rotating "
+             "over copies of >= 256 MiB. Regret = plan time / best time; geometric mean %.3f, worst %.3f." % (
+                 len(results), max((r["candidates"] for r in results), default=0), geo, max(regrets, default=0)),
+             "", "| M | N | K | plan (mb nb wn wk splits amode) | us | best plan | best us | regret |",
+             "|---|---|---|---|---|---|---|---|"]
+
+    def ps(p):
+        return "%d %d %d %d %d %d" % (p["mb"], p["nb"], p["wn"], p["wk"], p["splits"], p["amode"])
+    for r in results:
+        lines.append("| %d | %d | %d | %s | %.3f | %s | %.3f | %.3f |" % (
+            r["M"], r["N"], r["K"], ps(r["plan"]), r["us"], ps(r["best_plan"]), r["best_us"], r["regret"]))
+    with open(os.path.join(ROOT, "profiles", "plan_regret.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(ROOT, "profiles", "plan_regret.json"), "w") as f:
+        json.dump({"geomean_regret": geo, "shapes": results}, f, indent=0)
+        f.write("\n")
+    print("\n".join(lines[:4]))
+
+
 def stats_markdown(stats_csv, command):
     """profiles/bench_kernel_stats.md: the rocprofv3 --stats summary of the
     mx4 kernels of one bench.py run under the tracer."""
@@ -565,6 +669,9 @@ def main():
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "MFMA_DIR"),
                     help="no GPU: summarise the rocprofv3 output of --profile runs into profiles/")
     ap.add_argument("--summarize-calls", type=int, default=100, help="the --profile CALLS being summarised")
+    ap.add_argument("--plan-regret", nargs="?", const="all", default=None, metavar="PAIRS",
+                    help="time the library's plan against candidate plans on the pages' shape grid (PAIRS: "
+                         "comma-separated indices of the (N, K) pairs, default all) and write profiles/plan_regret.*")
     ap.add_argument("--stats-md", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="no GPU: profiles/bench_kernel_stats.md from a rocprofv3 --stats kernel_stats.csv")
     args = ap.parse_args()
@@ -586,6 +693,10 @@ def main():
 
     if args.profile:
         profile_run(torch, B, inputs, hw, args.profile)
+        return
+    if args.plan_regret:
+        only = None if args.plan_regret == "all" else [int(i) for i in args.plan_regret.split(",")]
+        plan_regret(torch, B, inputs, only)
         return
 
     per_workload = {}

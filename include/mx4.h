@@ -141,7 +141,8 @@ typedef struct mx_plan {
     int nb;          /* 32-column blocks of N per wave (1 or 2; 1, 2 or 4 in
                         MX_AMODE_STREAM) */
     int wn;          /* waves along N per workgroup (1 or 2) */
-    int wk;          /* waves along K per workgroup (1, 2, 4, 8 or 16; wn*wk <= 16) */
+    int wk;          /* waves along K per workgroup (1, 2, 4, 8 or 16; wn*wk <= 16);
+                        in MX_AMODE_SHARED the quantiser waves */
     int splits;      /* workgroups along K; > 1 adds a reduction kernel
                         unless finish is MX_FINISH_LAST_ARRIVAL */
     int amode;       /* where A is quantised: one of MX_AMODE_* */
@@ -159,10 +160,18 @@ enum {
                                barrier before the MFMAs */
     MX_AMODE_BF16 = 3,      /* A is NOT quantised: the a16wfp4 product of
                                mx_gemm_a16w4 (a different result) */
-    MX_AMODE_STREAM = 4     /* as MX_AMODE_DIRECT, but each wave loops over its
+    MX_AMODE_STREAM = 4,    /* as MX_AMODE_DIRECT, but each wave loops over its
                                K steps with the loads of several steps in
                                flight (any K per wave; mb = wn = 1,
                                nb in {1, 2, 4}) */
+    MX_AMODE_SHARED = 5     /* wk quantiser waves per workgroup quantise its
+                               32-row activation slice once into LDS for wn
+                               MFMA waves of nb N blocks each, which hold the
+                               weight of the whole K split in registers and
+                               need no cross-wave reduction (mb = 1;
+                               (nb, wn, wk) in {(1,2,2), (1,4,4), (2,2,2),
+                               (2,4,4)}; at most 32 K steps per split, 16
+                               with nb = 2 or wk = 2; finish 0) */
 };
 
 /* Split-K finishes of a plan (no effect when splits == 1). */

@@ -18,9 +18,10 @@ using mx4::kAmBf16;
 using mx4::kAmDirect;
 using mx4::kAmLds;
 using mx4::kAmPrequant;
+using mx4::kAmShared;
 using mx4::kAmStream;
 static_assert(kAmLds == MX_AMODE_LDS && kAmPrequant == MX_AMODE_PREQUANT && kAmDirect == MX_AMODE_DIRECT &&
-                  kAmBf16 == MX_AMODE_BF16 && kAmStream == MX_AMODE_STREAM,
+                  kAmBf16 == MX_AMODE_BF16 && kAmStream == MX_AMODE_STREAM && kAmShared == MX_AMODE_SHARED,
               "activation modes of the C ABI and the kernels differ");
 
 namespace {
@@ -79,9 +80,15 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     Layout l;
     l.steps_per_split = (gb.KS + plan.splits - 1) / plan.splits;
     l.splits = (gb.KS + l.steps_per_split - 1) / l.steps_per_split;  // every split non-empty
-    // The stream mode loops over its K steps; the other modes hold all of a
-    // wave's steps in registers at once.
-    const bool stream = plan.amode == kAmStream;
+    // The stream mode loops over its K steps; the shared mode's MFMA waves
+    // each hold a whole split (its kernels' own budgets, checked when the
+    // kernel is resolved); the other modes hold all of a wave's steps in
+    // registers at once.
+    const bool stream = plan.amode == kAmStream || plan.amode == kAmShared;
+    if (plan.amode == kAmShared) {
+        if (!mx4::find_shared_kernel(plan, l.steps_per_split)) return MX_EPLAN;
+        if (plan.finish != 0 && l.splits > 1) return MX_EPLAN;   // partials go to reduce_kernel
+    }
     if (!stream && (l.steps_per_split + plan.wk - 1) / plan.wk > mx4::kStepsPerWaveMax) return MX_EPLAN;
     // Register budget (no plan may run a kernel that spills).  kAmDirect and
     // kAmBf16 hold the raw bf16 of every fragment of the wave (16 VGPRs per K

@@ -764,6 +764,7 @@ static int row_chunks(const Plan& plan, const GemmParams& p) {
 
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
     if (plan.amode == kAmStream) return stream_lds_bytes(plan);
+    if (plan.amode == kAmShared) return shared_lds_bytes(plan, steps_per_split);
     const size_t a_op = plan.amode == kAmLds ? (size_t)plan.mb * steps_per_split * 64 * 17 : 0;
     size_t out = gemm_red_bytes(plan.wn, plan.wk, plan.mb, plan.nb) + gemm_stage_bytes(plan.wn, plan.mb, plan.nb);
     if (plan.amode == kAmDirect || plan.amode == kAmBf16) {   // tiles or slabs alias the epilogue's buffers
@@ -778,15 +779,19 @@ size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
 
 bool gemm_plan_supported(const Plan& plan) {
     if (plan.amode == kAmStream) return plan.splits >= 1 && find_stream_kernel(plan, 4) != nullptr;
+    if (plan.amode == kAmShared) return plan.splits >= 1 && find_shared_kernel(plan, 8) != nullptr;
     return plan.splits >= 1 && find_kernel(plan, 1) != nullptr;
 }
 
 bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
     const int per_wave = (p.steps_per_split + plan.wk - 1) / plan.wk;
-    GemmFn fn = plan.amode == kAmStream ? find_stream_kernel(plan, row_chunks(plan, p))
+    GemmFn fn = plan.amode == kAmStream   ? find_stream_kernel(plan, row_chunks(plan, p))
+              : plan.amode == kAmShared ? find_shared_kernel(plan, p.steps_per_split)
                                         : find_kernel(plan, gemm_kr_for(per_wave), row_chunks(plan, p));
     if (!fn) return false;
-    *out = GemmLaunch{fn, (unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits, (unsigned)(64 * plan.wn * plan.wk),
+    // the shared mode's workgroup is wn MFMA waves plus wk quantiser waves
+    const int waves = plan.amode == kAmShared ? plan.wn + plan.wk : plan.wn * plan.wk;
+    *out = GemmLaunch{fn, (unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits, (unsigned)(64 * waves),
                       gemm_lds_bytes(plan, p.steps_per_split), plan.amode == kAmPrequant};
     return true;
 }

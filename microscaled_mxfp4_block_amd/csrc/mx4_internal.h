@@ -86,6 +86,7 @@ constexpr int kAmPrequant = 1;   // by pack_kernel, into the workspace
 constexpr int kAmDirect = 2;     // by each wave, in registers
 constexpr int kAmBf16 = 3;       // not at all: bf16 A x dequantised B (the a16wfp4 product)
 constexpr int kAmStream = 4;     // by each wave, in registers, in a K loop (gemm_stream_kernel)
+constexpr int kAmShared = 5;     // by quantiser waves into LDS, for MFMA waves (gemm_shared_kernel)
 
 bool gemm_plan_supported(const Plan& p);
 int gemm_kr_for(int steps_per_wave);   // K-step budget KR of the kernel for that many steps (0: none)
@@ -116,6 +117,12 @@ bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out);
 // {1, 2, 4, 8, 16} (nb <= 2 at 16 waves), rq activation row chunks per step.
 GemmKernelFn find_stream_kernel(const Plan& plan, int rq);
 size_t stream_lds_bytes(const Plan& plan);
+// The kernels of the shared mode (mx4_shared.hip): plan.wn MFMA waves of
+// plan.nb N blocks each and plan.wk quantiser waves per workgroup (mb = 1),
+// (nb, wn, wk) in {(1, 2, 2), (1, 4, 4), (2, 2, 2), (2, 4, 4)}, at most 32
+// K steps per split (16 with nb = 2 or wk = 2); no last-arrival finish.
+GemmKernelFn find_shared_kernel(const Plan& plan, int steps_per_split);
+size_t shared_lds_bytes(const Plan& plan, int steps_per_split);
 hipError_t launch_gemm(const GemmLaunch& gl, const GemmParams& p, hipStream_t s);
 hipError_t launch_reduce(const GemmParams& p, hipStream_t s);
 

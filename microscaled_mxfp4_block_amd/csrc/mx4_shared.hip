@@ -1,0 +1,250 @@
+// mx4_shared.hip -- block-scaled MXFP4 GEMM for gfx950 (MI355X) with the
+// activation quantised once per workgroup by dedicated waves: the activation
+// mode MX_AMODE_SHARED.
+//
+//   C[M,N] = bf16_RNE( sum_k deq(A)[m,k] * deq(B)[n,k] )   (fp32 accumulation)
+//
+// The contraction is the block-scaled dot of the kernelindex.com
+// amd-mxfp4-mm pages (tl.dot_scaled(..., "e2m1", ..., "e2m1"), submission
+// 748756, kernel_fused_mxfp4_gemm) on v_mfma_scale_f32_32x32x64_f8f6f4; the
+// activation is quantised by the rule of submission 755056, "Software MXFP4
+// quant" (mx4_device.h).
+//
+// A workgroup owns 32 rows of C (one M block) and 32 NB WN columns over one K
+// split of at most KR 64-K steps, with two kinds of waves:
+//   - WN MFMA waves, each owning NB N blocks over the whole split: at launch
+//     each issues the 128-bit non-temporal loads of all its weight fragments
+//     and scale words (VGPRs), so the weight stream starts with the kernel
+//     and no wave ever waits for another's loads; after the barrier it reads
+//     its activation fragments from LDS and runs the MFMAs.  No two waves
+//     share a K range, so there is no cross-wave reduction.
+//   - QW quantiser waves, which stream the workgroup's activation slice (32
+//     rows x the split's K) with whole 128-byte row segments per 8 lanes,
+//     quantise each 32-element group across a DPP quad of lanes (amax, scale
+//     byte by the bit rule, e2m1 codes by the gfx950 fp4 convert) and write
+//     codes and scale bytes into LDS in MFMA lane order, once for all the
+//     MFMA waves; then they join the barrier.
+// The two kinds of loads are issued by different waves, so neither waits
+// for the other's (a wave's vector-memory counter runs in issue order).
+// Rows past M read zeros through the buffer bound (zero codes, scale byte
+// 0); steps past the split read zeros; a group past K (K % 64 == 32) is
+// zeroed explicitly.  The epilogue stages each MFMA wave's bf16 tile in LDS
+// and stores it in 16-byte row chunks; with K split over workgroups, fp32
+// partials go to the workspace and reduce_kernel sums them in split order.
+#include "mx4_device.h"
+#include "mx4_internal.h"
+
+namespace mx4 {
+
+// LDS: the quantised activation slice, [KR][64 lanes][16 B] codes then
+// [KR][64] scale bytes; the staged bf16 output tile aliases it after the
+// MFMAs.
+__host__ __device__ constexpr size_t shared_aop_bytes(int kr) { return (size_t)kr * 64 * 17; }
+__host__ __device__ constexpr size_t shared_stage_bytes(int nb, int wn) {
+    return (size_t)kRowBlock * (nb * wn * kRowBlock + 8) * 2;
+}
+
+template <int NB, int WN, int QW, int KR>
+__global__ void __launch_bounds__(64 * (WN + QW))
+gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_buf, int lda, int ldc, int M,
+                   int N, int K, int steps_per_split, uint32_t* counters, int splits, int mtiles) {
+    (void)counters;
+    (void)splits;
+    (void)mtiles;
+    constexpr uint32_t kOutOfRange = 0x80000000u;
+    const OperandGeom gb = operand_geom(N, K);
+    const int KS = gb.KS, KW = gb.KW, RBn = gb.RB;
+    const int G = K / kGroup;
+    const uint16_t* A = (const uint16_t*)a_src;
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    uint8_t* aop = lds;                             // codes, KR * 1 KiB
+    uint8_t* asc = lds + (size_t)KR * 1024;         // scale bytes, KR * 64
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int L = tid & 63;
+
+    const int nt = blockIdx.x;
+    const int mt = blockIdx.y;
+    const int split = blockIdx.z;
+    const int tb = split * steps_per_split;
+    const int te = min(tb + steps_per_split, KS);
+    const int T = te - tb;                          // steps of this split, <= KR
+    const bool mfma_wave = wave < WN;
+    const int nb0 = (nt * WN + wave) * NB;          // first N block of an MFMA wave
+
+    f32x16 acc[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
+
+    u32x4 bfrag[KR][NB];
+    uint32_t bscale[KR][NB];
+    if (mfma_wave) {
+        // ---- the weight: every fragment and scale word of the split in flight
+        // at once (steps past the split read zeros)
+        const Rsrc rb = make_rsrc(bp, (uint32_t)gb.total_bytes);
+#pragma unroll
+        for (int s = 0; s < KR; ++s) {
+            const bool on = s < T;
+            const int t = on ? tb + s : 0;
+#pragma unroll
+            for (int j = 0; j < NB; ++j) {
+                const int nb = min(nb0 + j, RBn - 1);   // clamped blocks are never stored
+                bfrag[s][j] = bload16<kNonTemporal>(rb, on ? (uint32_t)L * 16u : kOutOfRange,
+                                                    (uint32_t)(nb * KS + t) * 1024u);
+                bscale[s][j] = bload4(rb, on ? (uint32_t)L * 4u : kOutOfRange,
+                                      (uint32_t)gb.code_bytes + (uint32_t)(nb * KW + (t >> 2)) * 256u);
+            }
+        }
+    } else {
+        // ---- the activation slice: rows 32 mt .. 32 mt + 31, steps tb .. te - 1.
+        // 16-byte chunk c of the slice is row c / (8 T), column c % (8 T); a
+        // DPP quad (4 consecutive lanes, 4 consecutive chunks of one row) holds
+        // one 32-element group.
+        const Rsrc ra = make_rsrc(A, (uint32_t)M * (uint32_t)lda * 2u);
+        const int cpr = 8 * T;                      // chunks per slice row
+        const int nchunks = kRowBlock * cpr;
+        constexpr int NQ = QW * 64;
+        constexpr int PER = (kRowBlock * 8 * KR + NQ - 1) / NQ;   // chunks per lane, at most
+        const int q0 = (wave - WN) * 64 + L;
+        u32x4 xs[PER];
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int c = q0 + k * NQ;
+            const int r = c / cpr, col = c - (c / cpr) * cpr;
+            const bool live = c < nchunks && 2 * tb + (col >> 2) < G;
+            const uint32_t off = (uint32_t)(mt * kRowBlock + r) * (uint32_t)lda * 2u + (uint32_t)tb * 128u +
+                                 (uint32_t)col * 16u;
+            xs[k] = bload16(ra, live ? off : kOutOfRange, 0u);   // rows past M read zeros
+        }
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int c = q0 + k * NQ;
+            if (c - (L & 3) >= nchunks) break;   // whole quads leave together (cpr % 4 == 0)
+            uint32_t byte;
+            const uint32_t codes = quad_quant8(xs[k], byte);
+            const int r = c / cpr, col = c - (c / cpr) * cpr;
+            const int s = col >> 3, h = (col >> 2) & 1, q = col & 3;
+            const int u = s * 64 + r + 32 * h;      // MFMA lane slot of (row r, group 2 s + h)
+            *(uint32_t*)(aop + 16 * u + 4 * q) = codes;
+            if (q == 0) asc[u] = (uint8_t)byte;
+        }
+        // slots of steps past the split: zero codes and scale byte 0 (the
+        // MFMA waves multiply them by zero weight codes; the scale byte must
+        // still be a finite scale)
+        for (int u = q0; u < (KR - T) * 64; u += NQ) {
+            *(u32x4*)(aop + 16 * (T * 64 + u)) = u32x4{0u, 0u, 0u, 0u};
+            asc[T * 64 + u] = 0;
+        }
+    }
+    __syncthreads();   // the quantised slice is in LDS
+
+    if (mfma_wave) {
+#pragma unroll
+        for (int s = 0; s < KR; ++s) {
+            const u32x4 af = *(const u32x4*)(aop + 16 * (s * 64 + L));
+            const uint32_t as = asc[s * 64 + L];
+            const int sh = 8 * ((tb + s) & 3);      // byte of step tb + s in its scale word
+#pragma unroll
+            for (int j = 0; j < NB; ++j) acc[j] = mfma_fp4_32x32x64(bfrag[s][j], af, acc[j], bscale[s][j] >> sh, as);
+        }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) mfma_result_fence(acc[j]);
+    }
+    __syncthreads();   // every MFMA wave is done with the slice: the stage may reuse it
+
+    // ---- epilogue: lane L, element e of block j: m = 32 mt + L % 32,
+    // n = 32 (nb0 + j) + 8 (e / 4) + 4 (L / 32) + e % 4.
+    constexpr int TC = NB * WN * kRowBlock;
+    constexpr int SROW = TC + 8;
+    uint16_t* stage = (uint16_t*)lds;
+    const int m_lane = L & 31;
+    const int n_lane = 4 * (L >> 5);
+    const bool part = partial_buf != nullptr;
+    const int ldp = RBn * kRowBlock;
+    if (mfma_wave) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const f32x4 v = {acc[j][4 * r], acc[j][4 * r + 1], acc[j][4 * r + 2], acc[j][4 * r + 3]};
+                if (part) {
+                    const int m = mt * kRowBlock + m_lane;
+                    const int nb = nb0 + j;
+                    if (m < M && nb < RBn)
+                        *(f32x4*)(partial_buf + ((size_t)split * M + m) * ldp + nb * kRowBlock + 8 * r + n_lane) = v;
+                } else {
+                    const int col = (wave * NB + j) * kRowBlock + 8 * r + n_lane;
+                    uint2 w;
+                    w.x = pack_bf16x2(v.x, v.y);
+                    w.y = pack_bf16x2(v.z, v.w);
+                    *(uint2*)(stage + m_lane * SROW + col) = w;
+                }
+            }
+    }
+    if (part) return;   // reduce_kernel sums the partials
+    __syncthreads();
+    const int m_base = mt * kRowBlock;
+    const int n_base = nt * WN * NB * kRowBlock;
+    const bool vec16 = ((uintptr_t)C % 16 == 0) && (ldc % 8 == 0);
+    for (int c = tid; c < kRowBlock * TC / 8; c += 64 * (WN + QW)) {
+        const int row = c / (TC / 8), c8 = c % (TC / 8);
+        const int m = m_base + row, n = n_base + 8 * c8;
+        if (m >= M || n >= N) continue;
+        const u32x4 v = *(const u32x4*)(stage + row * SROW + 8 * c8);
+        uint16_t* dst = C + (size_t)m * ldc + n;
+        if (vec16 && n + 7 < N) {
+            __builtin_nontemporal_store(v, (u32x4*)dst);
+        } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                if (n + q < N) dst[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Instantiations: (NB, WN, QW) in {(1, 2, 2), (1, 4, 4), (2, 2, 2), (2, 4, 4)}
+// and KR in {8, 16, 24, 32}.
+
+// The weight registers bound NB * KR (<= 32 fragments per MFMA wave); the
+// activation loads in flight bound KR / QW (at most 32 chunks per lane).
+template <int NB, int WN, int QW>
+static GemmKernelFn shared_pick_kr(int kr) {
+    switch (kr) {
+        case 8: return gemm_shared_kernel<NB, WN, QW, 8>;
+        case 16: return gemm_shared_kernel<NB, WN, QW, 16>;
+        case 24: return (NB == 1 && QW == 4) ? gemm_shared_kernel<1, WN, 4, 24> : nullptr;
+        case 32: return (NB == 1 && QW == 4) ? gemm_shared_kernel<1, WN, 4, 32> : nullptr;
+        default: return nullptr;
+    }
+}
+
+int shared_kr_for(int steps) {
+    static const int kBudgets[] = {8, 16, 24, 32};
+    for (int kr : kBudgets)
+        if (steps <= kr) return kr;
+    return 0;
+}
+
+// Plan fields of this mode: nb N blocks per MFMA wave, wn MFMA waves, wk
+// quantiser waves (mb = 1).
+GemmKernelFn find_shared_kernel(const Plan& plan, int steps_per_split) {
+    if (plan.mb != 1) return nullptr;
+    const int kr = shared_kr_for(steps_per_split);
+    if (plan.nb == 1 && plan.wn == 2 && plan.wk == 2) return shared_pick_kr<1, 2, 2>(kr);
+    if (plan.nb == 1 && plan.wn == 4 && plan.wk == 4) return shared_pick_kr<1, 4, 4>(kr);
+    if (plan.nb == 2 && plan.wn == 2 && plan.wk == 2) return shared_pick_kr<2, 2, 2>(kr);
+    if (plan.nb == 2 && plan.wn == 4 && plan.wk == 4) return shared_pick_kr<2, 4, 4>(kr);
+    return nullptr;
+}
+
+size_t shared_lds_bytes(const Plan& plan, int steps_per_split) {
+    const size_t a = shared_aop_bytes(shared_kr_for(steps_per_split));
+    const size_t st = shared_stage_bytes(plan.nb, plan.wn);
+    return a > st ? a : st;
+}
+
+}  // namespace mx4

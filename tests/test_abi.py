@@ -171,6 +171,9 @@ def test_explicit_plan_rejections():
            dict(mb=1, nb=1, wn=2, wk=4, splits=1, amode=4),      # stream mode: one wave along N
            dict(mb=1, nb=4, wn=1, wk=16, splits=1, amode=4),     # stream mode: nb <= 2 at 16 waves
            dict(mb=1, nb=4, wn=1, wk=4, splits=1, amode=0),      # nb = 4 only in the stream mode
+           dict(mb=1, nb=1, wn=1, wk=1, splits=1, amode=5),      # shared mode: no such wave split
+           dict(mb=1, nb=1, wn=4, wk=4, splits=2, amode=5),      # shared mode: 56 K steps > 32 per split
+           dict(mb=1, nb=1, wn=4, wk=4, splits=4, amode=5, finish=1),   # shared mode: no last-arrival finish
            dict(mb=1, nb=1, wn=1, wk=4, splits=4, amode=0, finish=2),   # no such split-K finish
            dict(mb=1, nb=1, wn=1, wk=4, splits=0, amode=1),
            dict(mb=1, nb=1, wn=1, wk=4, splits=1000, amode=1),   # more splits than K steps
@@ -427,24 +430,27 @@ def test_noalloc_validates_before_any_hip_call():
     assert "#define MX_NOALLOC_SCRATCH_BYTES (8u << 20)" in hdr and B.MX_NOALLOC_SCRATCH_BYTES == 8 << 20
 
 
-def test_stream_kernels_preload_arguments_and_never_spill():
-    """The K-looped stream-mode kernels take the GEMM kernels' 72-byte scalar
-    argument segment with its 14 leading SGPRs preloaded, and none spills
-    VGPRs or uses scratch memory."""
-    path = os.path.join(ROOT, "_build", "mx4_stream.s")
+@pytest.mark.parametrize("src,kname,count", [("mx4_stream.s", "gemm_stream_kernel", 42),
+                                              ("mx4_shared.s", "gemm_shared_kernel", 12)])
+def test_mode_kernels_preload_arguments_and_never_spill(src, kname, count):
+    """The K-looped stream-mode kernels and the quantiser-wave shared-mode
+    kernels take the GEMM kernels' 72-byte scalar argument segment with its
+    14 leading SGPRs preloaded, and none spills VGPRs or uses scratch
+    memory."""
+    path = os.path.join(ROOT, "_build", src)
     if not os.path.exists(path):
         pytest.skip("no device assembly under _build (run the package build first)")
     text = open(path).read()
     seen = 0
     for m in re.finditer(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S):
         name, body = m.group(1), m.group(2)
-        if "gemm_stream_kernel" not in name:
+        if kname not in name:
             continue
         assert int(re.search(r"\.amdhsa_user_sgpr_kernarg_preload_length (\d+)", body).group(1)) == 14, name
         assert int(re.search(r"\.amdhsa_kernarg_size (\d+)", body).group(1)) == 72, name
         assert int(re.search(r"\.amdhsa_private_segment_fixed_size (\d+)", body).group(1)) == 0, name
         seen += 1
-    assert seen == 42
+    assert seen == count
     for block in text.split("  - .agpr_count:")[1:]:
-        if "gemm_stream_kernel" in re.search(r"\.name:\s+(\S+)", block).group(1):
+        if kname in re.search(r"\.name:\s+(\S+)", block).group(1):
             assert int(re.search(r"\.vgpr_spill_count:\s+(\d+)", block).group(1)) == 0

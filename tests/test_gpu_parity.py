@@ -267,6 +267,10 @@ PLANS = [
     dict(mb=1, nb=4, wn=1, wk=8, splits=1, amode=4),
     dict(mb=1, nb=2, wn=1, wk=16, splits=3, amode=4),
     dict(mb=1, nb=4, wn=1, wk=2, splits=2, amode=4, finish=1),
+    dict(mb=1, nb=1, wn=2, wk=2, splits=1, amode=5),
+    dict(mb=1, nb=1, wn=4, wk=4, splits=1, amode=5),
+    dict(mb=1, nb=2, wn=2, wk=2, splits=3, amode=5),
+    dict(mb=1, nb=2, wn=4, wk=4, splits=2, amode=5),
 ]
 
 # The a16wfp4 product (amode 3) against its own oracle.
