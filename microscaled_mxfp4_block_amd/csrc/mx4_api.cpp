@@ -120,33 +120,47 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     return MX_OK;
 }
 
-// Model for shapes without a table entry: quantise A inside the GEMM (each
-// wave its own fragments) up to 128 rows of A, where re-quantising it per
-// workgroup still costs less than a second launch; beyond that in a first
-// kernel, with two 32-row M blocks per wave when M allows; one N block per
-// wave, 8 waves along K (fewer for short K); then the fewest K
-// splits that keep every wave within its register budget and the activation
-// slice within LDS, doubled while the tiles leave most of the 256 CUs idle
-// and the fp32 partials stay small next to the weight.
+// Model for shapes without a table entry, fitted to the plan-regret sweep
+// over the pages' shape grid (19 (N, K) weight shapes x M = 1 .. 256, up to
+// 55 candidate plans each):
+//   - the activation is quantised in a first kernel when M has four or more
+//     32-row blocks and K more than 8 steps, unless M is exactly four blocks
+//     with N < 7168 and K <= 2048; every N tile would otherwise quantise it
+//     again, which costs more vector-ALU time than the second launch;
+//     there, two M blocks per wave and two waves along N (one for deep K);
+//   - otherwise each wave quantises its own fragments: two N blocks per wave
+//     from four M blocks on, from two at N >= 7168, and for deep K;
+//   - 8 waves along K (4 for K <= 512), and K split over workgroups only as
+//     far as the register budget needs, except that deep K (more than 64
+//     steps) with the register mode takes at least 4 splits for one M
+//     block and 2 for more: the N tiles alone leave most CUs idle.
 Plan model_plan(int M, int N, int K) {
     const OperandGeom ga = mx4::operand_geom(M, K);
     const OperandGeom gb = mx4::operand_geom(N, K);
+    const int RBm = ga.RB, KS = gb.KS;
+    const bool deep = KS > 64;
+    const bool pre = RBm >= 4 && KS > 8 && (RBm > 4 || N >= 7168 || KS > 32);
     Plan p;
-    p.amode = ga.RB > 4 ? kAmPrequant : kAmDirect;
-    p.mb = (p.amode == kAmPrequant && ga.RB >= 2) ? 2 : 1;
-    p.nb = 1;
-    p.wn = 1;
-    // about two K steps per wave: the measured optimum for every tabled shape
-    p.wk = pow2_floor(gb.KS < 16 ? (gb.KS + 1) / 2 : 8);
-    p.splits = 1;
     p.finish = 0;
+    p.splits = 1;
+    p.wk = KS <= 8 ? pow2_floor(KS >= 8 ? 4 : (KS + 1) / 2) : 8;
+    if (pre) {
+        p.amode = kAmPrequant;
+        p.mb = 2;
+        p.nb = 1;
+        p.wn = deep ? 1 : 2;
+    } else {
+        p.amode = kAmDirect;
+        p.mb = 1;
+        p.nb = (RBm >= 4 || (RBm >= 2 && N >= 7168) || deep) ? 2 : 1;
+        p.wn = 1;
+    }
     Layout l;
-    while (p.splits < gb.KS && plan_layout(p, M, N, K, &l) != MX_OK) ++p.splits;
-    const long long tiles = (long long)((ga.RB + p.mb - 1) / p.mb) * gb.RB;
-    const double weight = (double)N * K * 0.5;
-    while (tiles * p.splits < 128 && p.splits * 2 <= gb.KS &&
-           (double)M * N * 4.0 * 2 * p.splits * 2 <= 0.25 * weight)
-        p.splits *= 2;
+    while (p.splits < KS && plan_layout(p, M, N, K, &l) != MX_OK) ++p.splits;
+    if (deep && !pre) {
+        const int want = RBm <= 1 ? 4 : 2;
+        if (p.splits < want && want <= KS) p.splits = want;
+    }
     return p;
 }
 
