@@ -17,7 +17,9 @@
  * path"): codes [rows, K/2] bytes, element 2j in the low nibble of byte j;
  * scales [rows, K/32] bytes, group g covers k in [32g, 32g+32).
  *
- * Conventions for every entry point:
+ * Conventions for every entry point (those of the C launcher on submission
+ * 755056's page, quant_and_ck_gemm: an int status, buffers and scratch owned
+ * by the caller, work launched asynchronously on the caller's queue):
  *   - bf16 is passed as raw 16-bit patterns; matrices are row-major with an
  *     explicit leading dimension in elements.
  *   - Pointers named *_dev are device pointers (hipMalloc or torch CUDA
@@ -74,7 +76,8 @@ const char* mx_strerror(int code);
 int mx_packed_weight_bytes(int N, int K, size_t* bytes_host);
 
 /* One-time weight packing: the MXFP4 rule above applied to B along K (the
- * weight is quantised the same way as the activation), written into the
+ * weight is quantised the same way as the activation; on the pages the
+ * harness hands B over already quantised and shuffled), written into the
  * GEMM's tile layout.
  *   B_dev       bf16 [N, K], row stride ldb elements (ldb >= K, ldb % 8 == 0,
  *               N * ldb * 2 < 2^31)
@@ -96,7 +99,9 @@ int mx_unpack_weight(const void* packed_dev, int N, int K,
 int mx_import_weight(const void* codes_dev, const void* scales_dev, int N, int K,
                      void* packed_dev, size_t packed_bytes, void* stream);
 
-/* Stand-alone activation quantisation to the natural layouts.
+/* Stand-alone activation quantisation to the natural layouts (the rule
+ * above; the standalone quantiser of submission 755056's page writes the
+ * same codes and scales, in a shuffled scale layout).
  *   A_dev       bf16 [M, K], row stride lda (lda >= K, lda % 8 == 0)
  *   codes_dev   [M, K/2] bytes, scales_dev [M, K/32] bytes (dense) */
 int mx_quant_act(const void* A_dev, int M, int K, int lda,
@@ -113,7 +118,15 @@ int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host);
 
 /* C = A x B^T with A quantised on the fly (quantisation, block-scaled MFMA
  * contraction with fp32 accumulation, split-K reduction when planned, bf16
- * round-to-nearest-even epilogue).
+ * round-to-nearest-even epilogue).  The contraction is the block-scaled dot
+ * the pages write as tl.dot_scaled(a, a_scale, "e2m1", b, b_scale, "e2m1")
+ * (submission 748756, kernel_fused_mxfp4_gemm): every product of two e2m1
+ * values carries 2^(sa-127) * 2^(sb-127) of its two 32-element groups, and
+ * the sum runs over all of K; here it runs on the gfx950 scaled MFMA
+ * (v_mfma_scale_f32_32x32x64_f8f6f4).  The call only validates (host),
+ * enqueues and returns; results land when the stream reaches them.  Errors:
+ * MX_EINVAL (shape, lda or ldc), MX_EALIGN, MX_ESPACE (workspace too small),
+ * MX_EHIP (a launch failed; earlier launches of the call may be enqueued).
  *   A_dev      bf16 [M, K], lda >= K, lda % 8 == 0, M * lda * 2 < 2^31
  *   packed_dev weight packed by mx_pack_weight for (N, K)
  *   C_dev      bf16 [M, N] output, ldc >= N

@@ -13,7 +13,9 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmx4.so")
+# MX4_LIBRARY names another build of the same library (the host-sanitizer
+# build of the CPU tests); by default the one built next to this file.
+LIB_PATH = os.environ.get("MX4_LIBRARY") or os.path.join(_HERE, "libmx4.so")
 
 MX_OK = 0
 MX_EINVAL = -1

@@ -17,7 +17,8 @@
 //           byte b (0..3) of the word is the e8m0 byte of row 32 rb + L % 32
 //           in K step t = 4 w + b (group 2 t + L / 32).
 //
-// Rows past the matrix and K groups past K are zero codes with scale byte 127.
+// Rows past the matrix and K groups past K are zero codes with scale byte 0
+// (2^-127), as are the scale bytes of steps past the last one in its word.
 // The same layout carries the packed weight B (rows = N) and the quantised
 // activation operand A (rows = M) in the workspace.
 #pragma once

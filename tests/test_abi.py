@@ -454,3 +454,19 @@ def test_mode_kernels_preload_arguments_and_never_spill(src, kname, count):
     for block in text.split("  - .agpr_count:")[1:]:
         if kname in re.search(r"\.name:\s+(\S+)", block).group(1):
             assert int(re.search(r"\.vgpr_spill_count:\s+(\d+)", block).group(1)) == 0
+
+
+def test_headers_are_plain_c():
+    """include/*.h compile as C (gcc -std=c99 -Wall -Werror), on their own."""
+    for h in ("mx4.h", "mx4_hwcheck.h"):
+        r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-fsyntax-only", "-x", "c",
+                            os.path.join(ROOT, "include", h)], stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
+                           text=True)
+        assert r.returncode == 0, r.stdout
+
+
+def test_library_under_test_is_the_one_named():
+    """The binding loads MX4_LIBRARY when it is set (the sanitizer run), else
+    the library built next to the package."""
+    want = os.environ.get("MX4_LIBRARY") or os.path.join(ROOT, "microscaled_mxfp4_block_amd", "libmx4.so")
+    assert B.LIB_PATH == want
