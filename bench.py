@@ -561,6 +561,9 @@ def regret_candidates(B, M, N, K):
             cands.append(dict(mb=mb, nb=nb, wn=wn, wk=wk, splits=sp, amode=1, finish=0))
     for sp in (1, 2, 4):
         cands.append(dict(mb=1, nb=1, wn=1, wk=8, splits=sp, amode=0, finish=0))
+    for wn in (3, 4):
+        for sp in (1, 2, 4, 8):
+            cands.append(dict(mb=1, nb=1, wn=wn, wk=4, splits=sp, amode=5, finish=0))
     out = []
     for p in cands:
         try:
@@ -617,7 +620,7 @@ def plan_regret(torch, B, inputs, only=None):
              "kernelindex.com amd-mxfp4-mm pages' synthesized config CSV, submission 754569, times M = 1 .. 256), "
              "the HIP-graph-replay GPU time per call of the plan mx_gemm picks (the measured table for the five "
              "workloads, the model elsewhere) against the fastest of up to %d candidate plans (register-quantising "
-             "mode over waves, splits and N widths; pre-quantising mode over its tiles; LDS mode), weights rotating "
+             "mode over waves, splits and N widths; pre-quantising mode over its tiles; LDS mode; quantiser-wave shared mode), weights rotating "
              "over copies of >= 256 MiB. Regret = plan time / best time; geometric mean %.3f, worst %.3f." % (
                  len(results), max((r["candidates"] for r in results), default=0), geo, max(regrets, default=0)),
              "", "| M | N | K | plan (mb nb wn wk splits amode) | us | best plan | best us | regret |",
@@ -739,7 +742,8 @@ def main():
             "unit": "GB/s",
             "frac": rec["hbm_frac_cold"],
             "traffic": None if prof is None else prof.get("hbm_bytes_per_call"),
-            "kernel": "one mx_gemm call: pack_kernel (activation quantiser) + gemm_kernel",
+            "kernel": "one mx_gemm call: %s" % ("gemm_shared_kernel (one launch)" if rec["launches_per_call"] == 1
+                                                else "%d launches" % rec["launches_per_call"]),
             "kernel_us": rec["gpu_us_per_call_cold"],
             "kernel_us_method": "HIP graph replay of cold calls, HIP events on the replay stream (all launches "
                                 "of a call, host out of the loop)",

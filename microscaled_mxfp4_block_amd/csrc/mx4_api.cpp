@@ -52,7 +52,7 @@ const TableEntry kTable[] = {
     {32, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
     {16, 2112, 7168, {1, 2, 1, 4, 7, 2, 0}},
     {64, 7168, 2048, {1, 2, 1, 8, 1, 2, 0}},
-    {256, 3072, 1536, {1, 1, 1, 8, 1, 1, 0}},
+    {256, 3072, 1536, {1, 1, 3, 4, 1, 5, 0}},
 };
 
 int pow2_floor(int x) {
@@ -122,11 +122,14 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 
 // Model for shapes without a table entry, fitted to the plan-regret sweep
 // over the pages' shape grid (19 (N, K) weight shapes x M = 1 .. 256, up to
-// 55 candidate plans each):
-//   - the activation is quantised in a first kernel when M has four or more
-//     32-row blocks and K more than 8 steps, unless M is exactly four blocks
-//     with N < 7168 and K <= 2048; every N tile would otherwise quantise it
-//     again, which costs more vector-ALU time than the second launch;
+// 63 candidate plans each):
+//   - the activation is quantised once per workgroup by quantiser waves for
+//     three or four MFMA waves when M has at least eight 32-row blocks (or
+//     four, with K <= 512 or N >= 7168) and K is at most 32 steps;
+//   - else it is quantised in a first kernel when M has four or more 32-row
+//     blocks and K more than 8 steps, unless M is exactly four blocks with
+//     N < 7168 and K <= 2048: every wave of every N tile would otherwise
+//     quantise it again, which costs more vector-ALU time than the launch;
 //     there, two M blocks per wave and two waves along N (one for deep K);
 //   - otherwise each wave quantises its own fragments: two N blocks per wave
 //     from four M blocks on, from two at N >= 7168, and for deep K;
@@ -139,11 +142,23 @@ Plan model_plan(int M, int N, int K) {
     const OperandGeom gb = mx4::operand_geom(N, K);
     const int RBm = ga.RB, KS = gb.KS;
     const bool deep = KS > 64;
-    const bool pre = RBm >= 4 && KS > 8 && (RBm > 4 || N >= 7168 || KS > 32);
+    // quantiser waves for the whole workgroup: at least 8 M blocks, or 4
+    // with a short K or a wide N, when the split's K fits their budget
+    const bool shared = KS <= 32 && (RBm >= 8 || (RBm >= 4 && (KS <= 8 || N >= 7168)));
+    const bool pre = !shared && RBm >= 4 && KS > 8 && (RBm > 4 || N >= 7168 || KS > 32);
     Plan p;
     p.finish = 0;
     p.splits = 1;
     p.wk = KS <= 8 ? pow2_floor(KS >= 8 ? 4 : (KS + 1) / 2) : 8;
+    if (shared) {
+        // three MFMA waves when the N blocks divide by 3 (no ragged tile), else four
+        p.amode = kAmShared;
+        p.mb = 1;
+        p.nb = 1;
+        p.wn = gb.RB % 3 == 0 ? 3 : 4;
+        p.wk = 4;
+        return p;
+    }
     if (pre) {
         p.amode = kAmPrequant;
         p.mb = 2;
@@ -187,6 +202,15 @@ Plan choose_plan_a16w4(int M, int N, int K) {
     for (const TableEntry& e : kTableA16w4)
         if (e.M == M && e.N == N && e.K == K) return e.plan;
     Plan p = choose_plan(M, N, K);
+    if (p.amode == kAmShared || p.amode == kAmStream) {
+        // tilings of modes the bf16 kernels do not have: one wave along N,
+        // waves along K as the register mode takes them
+        const OperandGeom gk = mx4::operand_geom(N, K);
+        p.nb = 1;
+        p.wn = 1;
+        p.wk = gk.KS <= 8 ? pow2_floor(gk.KS >= 8 ? 4 : (gk.KS + 1) / 2) : 8;
+        p.splits = 1;
+    }
     p.amode = kAmBf16;
     p.mb = 1;
     const OperandGeom gb = mx4::operand_geom(N, K);

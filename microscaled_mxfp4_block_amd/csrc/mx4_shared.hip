@@ -15,15 +15,18 @@
 //   - WN MFMA waves, each owning NB N blocks over the whole split: at launch
 //     each issues the 128-bit non-temporal loads of all its weight fragments
 //     and scale words (VGPRs), so the weight stream starts with the kernel
-//     and no wave ever waits for another's loads; after the barrier it reads
-//     its activation fragments from LDS and runs the MFMAs.  No two waves
+//     (issued right after the activation's: a CU returns its waves' loads
+//     roughly in the order it takes them, and the activation must arrive
+//     first); after the barrier it reads its activation fragments from LDS
+//     and runs the MFMAs.  No two waves
 //     share a K range, so there is no cross-wave reduction.
-//   - QW quantiser waves, which stream the workgroup's activation slice (32
-//     rows x the split's K) with whole 128-byte row segments per 8 lanes,
-//     quantise each 32-element group across a DPP quad of lanes (amax, scale
-//     byte by the bit rule, e2m1 codes by the gfx950 fp4 convert) and write
-//     codes and scale bytes into LDS in MFMA lane order, once for all the
-//     MFMA waves; then they join the barrier.
+//   - QW quantiser waves, which load the workgroup's activation slice (32
+//     rows x the split's K) with whole 128-byte row segments per 8 lanes (a
+//     lane keeps one row and one 16-byte column of every K step, so no index
+//     needs a division), quantise each 32-element group across a DPP quad of
+//     lanes (amax, scale byte by the bit rule, e2m1 codes by the gfx950 fp4
+//     convert) and write codes and scale bytes into LDS in MFMA lane order,
+//     once for all the MFMA waves; then they join the barrier.
 // The two kinds of loads are issued by different waves, so neither waits
 // for the other's (a wave's vector-memory counter runs in issue order).
 // Rows past M read zeros through the buffer bound (zero codes, scale byte
@@ -80,6 +83,38 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
 
     u32x4 bfrag[KR][NB];
     uint32_t bscale[KR][NB];
+    // The activation loads go out before the weight's: a CU returns the loads
+    // of its waves roughly in the order it takes them, and the activation
+    // (L2-resident) must arrive early for the quantisers, while the weight
+    // (HBM) is consumed last.
+    constexpr int NQ = QW * 64;
+    constexpr int RPL = kRowBlock * 8 / NQ;          // slice rows per quantiser lane
+    u32x4 xs[RPL][KR];
+    const int li = (wave - WN) * 64 + L;
+    const int col = li & 7;                          // 16-byte column in the step's row segment
+    const int h = col >> 2, q = col & 3;             // group of the step, quarter of the group
+    if (!mfma_wave) {
+        // ---- the activation slice: rows 32 mt .. 32 mt + 31, steps tb .. te - 1.
+        // The QW quantiser waves hold 64 QW lanes: lane li takes slice rows
+        // li / 8 + 64 QW / 8 * i (i < 32 * 8 / (64 QW)) and, in every K step,
+        // the 16-byte column li % 8 of the row's 128-byte segment: 8 lanes
+        // read one row segment, a DPP quad (4 consecutive lanes) holds one
+        // 32-element group.
+        const Rsrc ra = make_rsrc(A, (uint32_t)M * (uint32_t)lda * 2u);
+#pragma unroll
+        for (int i = 0; i < RPL; ++i) {
+            const int r = (li >> 3) + (NQ / 8) * i;
+            const uint32_t rowoff = (uint32_t)(mt * kRowBlock + r) * (uint32_t)lda * 2u + (uint32_t)tb * 128u +
+                                    (uint32_t)col * 16u;
+#pragma unroll
+            for (int s = 0; s < KR; ++s) {
+                // steps past the split and a group past K (K % 64 == 32) read zeros
+                const bool live = s < T && 2 * (tb + s) + h < G;
+                xs[i][s] = bload16(ra, live ? rowoff + (uint32_t)s * 128u : kOutOfRange, 0u);
+            }
+        }
+    }
+    __syncthreads();   // the activation loads are issued
     if (mfma_wave) {
         // ---- the weight: every fragment and scale word of the split in flight
         // at once (steps past the split read zeros)
@@ -97,49 +132,24 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
                                       (uint32_t)gb.code_bytes + (uint32_t)(nb * KW + (t >> 2)) * 256u);
             }
         }
-    } else {
-        // ---- the activation slice: rows 32 mt .. 32 mt + 31, steps tb .. te - 1.
-        // 16-byte chunk c of the slice is row c / (8 T), column c % (8 T); a
-        // DPP quad (4 consecutive lanes, 4 consecutive chunks of one row) holds
-        // one 32-element group.
-        const Rsrc ra = make_rsrc(A, (uint32_t)M * (uint32_t)lda * 2u);
-        const int cpr = 8 * T;                      // chunks per slice row
-        const int nchunks = kRowBlock * cpr;
-        constexpr int NQ = QW * 64;
-        constexpr int PER = (kRowBlock * 8 * KR + NQ - 1) / NQ;   // chunks per lane, at most
-        const int q0 = (wave - WN) * 64 + L;
-        u32x4 xs[PER];
+    }
+    if (!mfma_wave) {
+        // each load is quantised as it lands; steps past the split quantise
+        // zeros: zero codes, scale byte 0
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int c = q0 + k * NQ;
-            const int r = c / cpr, col = c - (c / cpr) * cpr;
-            const bool live = c < nchunks && 2 * tb + (col >> 2) < G;
-            const uint32_t off = (uint32_t)(mt * kRowBlock + r) * (uint32_t)lda * 2u + (uint32_t)tb * 128u +
-                                 (uint32_t)col * 16u;
-            xs[k] = bload16(ra, live ? off : kOutOfRange, 0u);   // rows past M read zeros
-        }
+        for (int i = 0; i < RPL; ++i) {
+            const int r = (li >> 3) + (NQ / 8) * i;
 #pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int c = q0 + k * NQ;
-            if (c - (L & 3) >= nchunks) break;   // whole quads leave together (cpr % 4 == 0)
-            uint32_t byte;
-            const uint32_t codes = quad_quant8(xs[k], byte);
-            const int r = c / cpr, col = c - (c / cpr) * cpr;
-            const int s = col >> 3, h = (col >> 2) & 1, q = col & 3;
-            const int u = s * 64 + r + 32 * h;      // MFMA lane slot of (row r, group 2 s + h)
-            *(uint32_t*)(aop + 16 * u + 4 * q) = codes;
-            if (q == 0) asc[u] = (uint8_t)byte;
-        }
-        // slots of steps past the split: zero codes and scale byte 0 (the
-        // MFMA waves multiply them by zero weight codes; the scale byte must
-        // still be a finite scale)
-        for (int u = q0; u < (KR - T) * 64; u += NQ) {
-            *(u32x4*)(aop + 16 * (T * 64 + u)) = u32x4{0u, 0u, 0u, 0u};
-            asc[T * 64 + u] = 0;
+            for (int s = 0; s < KR; ++s) {
+                uint32_t byte;
+                const uint32_t codes = quad_quant8(xs[i][s], byte);
+                const int u = s * 64 + r + 32 * h;   // MFMA lane slot of (row r, group 2 s + h)
+                *(uint32_t*)(aop + 16 * u + 4 * q) = codes;
+                if (q == 0) asc[u] = (uint8_t)byte;
+            }
         }
     }
     __syncthreads();   // the quantised slice is in LDS
-
     if (mfma_wave) {
 #pragma unroll
         for (int s = 0; s < KR; ++s) {
@@ -149,6 +159,8 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
 #pragma unroll
             for (int j = 0; j < NB; ++j) acc[j] = mfma_fp4_32x32x64(bfrag[s][j], af, acc[j], bscale[s][j] >> sh, as);
         }
+    }
+    if (mfma_wave) {
 #pragma unroll
         for (int j = 0; j < NB; ++j) mfma_result_fence(acc[j]);
     }
@@ -206,11 +218,11 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
 }
 
 // ---------------------------------------------------------------------------
-// Instantiations: (NB, WN, QW) in {(1, 2, 2), (1, 4, 4), (2, 2, 2), (2, 4, 4)}
-// and KR in {8, 16, 24, 32}.
+// Instantiations: (NB, WN, QW) in {(1, 2, 2), (1, 3, 4), (1, 4, 4), (2, 2, 2),
+// (2, 4, 4)} and KR in {8, 16, 24, 32}.
 
 // The weight registers bound NB * KR (<= 32 fragments per MFMA wave); the
-// activation loads in flight bound KR / QW (at most 32 chunks per lane).
+// activation loads in flight bound KR * 8 / QW (at most 32 chunks per lane).
 template <int NB, int WN, int QW>
 static GemmKernelFn shared_pick_kr(int kr) {
     switch (kr) {
@@ -235,6 +247,7 @@ GemmKernelFn find_shared_kernel(const Plan& plan, int steps_per_split) {
     if (plan.mb != 1) return nullptr;
     const int kr = shared_kr_for(steps_per_split);
     if (plan.nb == 1 && plan.wn == 2 && plan.wk == 2) return shared_pick_kr<1, 2, 2>(kr);
+    if (plan.nb == 1 && plan.wn == 3 && plan.wk == 4) return shared_pick_kr<1, 3, 4>(kr);
     if (plan.nb == 1 && plan.wn == 4 && plan.wk == 4) return shared_pick_kr<1, 4, 4>(kr);
     if (plan.nb == 2 && plan.wn == 2 && plan.wk == 2) return shared_pick_kr<2, 2, 2>(kr);
     if (plan.nb == 2 && plan.wn == 4 && plan.wk == 4) return shared_pick_kr<2, 4, 4>(kr);

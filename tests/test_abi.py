@@ -134,10 +134,16 @@ def test_gemm_validation():
 def test_plans_for_workloads():
     for w in WORKLOADS:
         p = B.mx_gemm_plan(w.M, w.N, w.K)
-        assert p["mb"] in (1, 2) and p["nb"] in (1, 2) and p["wn"] in (1, 2)
-        assert p["amode"] in (B.MX_AMODE_LDS, B.MX_AMODE_PREQUANT, B.MX_AMODE_DIRECT)
+        assert p["amode"] in (B.MX_AMODE_LDS, B.MX_AMODE_PREQUANT, B.MX_AMODE_DIRECT, B.MX_AMODE_SHARED)
         assert p["finish"] in (B.MX_FINISH_KERNEL, B.MX_FINISH_LAST_ARRIVAL)
-        assert p["wk"] in (1, 2, 4, 8, 16) and p["wn"] * p["wk"] <= 16 and p["splits"] >= 1
+        if p["amode"] == B.MX_AMODE_SHARED:
+            # wn MFMA waves + wk quantiser waves
+            assert (p["mb"], p["nb"], p["wn"], p["wk"]) in ((1, 1, 2, 2), (1, 1, 3, 4), (1, 1, 4, 4), (1, 2, 2, 2),
+                                                            (1, 2, 4, 4))
+        else:
+            assert p["mb"] in (1, 2) and p["nb"] in (1, 2) and p["wn"] in (1, 2)
+            assert p["wk"] in (1, 2, 4, 8, 16) and p["wn"] * p["wk"] <= 16
+        assert p["splits"] >= 1
         ws = B.mx_gemm_workspace_bytes(w.M, w.N, w.K)
         if p["splits"] == 1 and p["amode"] != B.MX_AMODE_PREQUANT:
             assert ws == 0
@@ -431,7 +437,7 @@ def test_noalloc_validates_before_any_hip_call():
 
 
 @pytest.mark.parametrize("src,kname,count", [("mx4_stream.s", "gemm_stream_kernel", 42),
-                                              ("mx4_shared.s", "gemm_shared_kernel", 12)])
+                                              ("mx4_shared.s", "gemm_shared_kernel", 16)])
 def test_mode_kernels_preload_arguments_and_never_spill(src, kname, count):
     """The K-looped stream-mode kernels and the quantiser-wave shared-mode
     kernels take the GEMM kernels' 72-byte scalar argument segment with its
@@ -470,3 +476,20 @@ def test_library_under_test_is_the_one_named():
     the library built next to the package."""
     want = os.environ.get("MX4_LIBRARY") or os.path.join(ROOT, "microscaled_mxfp4_block_amd", "libmx4.so")
     assert B.LIB_PATH == want
+
+
+def test_library_plans_are_accepted_for_random_shapes():
+    """For 3000 seeded random shapes (M up to 600, N up to 3000, K up to
+    9600) and the pages' shape grid, the plan each product picks passes the
+    planner's own checks (a plan the model picks must never be refused)."""
+    import random
+    rnd = random.Random(7)
+    shapes = [(rnd.randint(1, 600), rnd.randint(1, 3000), 32 * rnd.randint(1, 300)) for _ in range(3000)]
+    import importlib.util
+    spec = importlib.util.spec_from_file_location("mx4_bench", os.path.join(ROOT, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    shapes += [(M, N, K) for (N, K) in bench.GRID_DIM_PAIRS for M in bench.GRID_BATCH]
+    for M, N, K in shapes:
+        assert B.mx_gemm_workspace_bytes(M, N, K) >= 0
+        assert B.mx_gemm_a16w4_workspace_bytes(M, N, K) >= 0
