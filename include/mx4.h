@@ -182,9 +182,10 @@ enum {
                                MFMA waves of nb N blocks each, which hold the
                                weight of the whole K split in registers and
                                need no cross-wave reduction (mb = 1;
-                               (nb, wn, wk) in {(1,2,2), (1,4,4), (2,2,2),
-                               (2,4,4)}; at most 32 K steps per split, 16
-                               with nb = 2 or wk = 2; finish 0) */
+                               (nb, wn, wk) in {(1,2,2), (1,3,4), (1,3,8),
+                               (1,4,4), (1,4,8), (2,2,2), (2,4,4)}; at most
+                               24 K steps per split, 16 with nb = 2;
+                               finish 0) */
 };
 
 /* Split-K finishes of a plan (no effect when splits == 1). */

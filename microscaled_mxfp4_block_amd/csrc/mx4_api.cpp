@@ -52,7 +52,7 @@ const TableEntry kTable[] = {
     {32, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
     {16, 2112, 7168, {1, 2, 1, 4, 7, 2, 0}},
     {64, 7168, 2048, {1, 2, 1, 8, 1, 2, 0}},
-    {256, 3072, 1536, {1, 1, 3, 4, 1, 5, 0}},
+    {256, 3072, 1536, {1, 1, 3, 8, 1, 5, 0}},
 };
 
 int pow2_floor(int x) {
@@ -79,6 +79,8 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     if (plan.splits > gb.KS) return MX_EPLAN;
     Layout l;
     l.steps_per_split = (gb.KS + plan.splits - 1) / plan.splits;
+    // the shared mode's splits start on a scale word (4 steps)
+    if (plan.amode == kAmShared) l.steps_per_split = (l.steps_per_split + 3) / 4 * 4;
     l.splits = (gb.KS + l.steps_per_split - 1) / l.steps_per_split;  // every split non-empty
     // The stream mode loops over its K steps; the shared mode's MFMA waves
     // each hold a whole split (its kernels' own budgets, checked when the
@@ -125,7 +127,7 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 // 63 candidate plans each):
 //   - the activation is quantised once per workgroup by quantiser waves for
 //     three or four MFMA waves when M has at least eight 32-row blocks (or
-//     four, with K <= 512 or N >= 7168) and K is at most 32 steps;
+//     four, with K <= 512 or N >= 7168) and K is at most 24 steps;
 //   - else it is quantised in a first kernel when M has four or more 32-row
 //     blocks and K more than 8 steps, unless M is exactly four blocks with
 //     N < 7168 and K <= 2048: every wave of every N tile would otherwise
@@ -144,7 +146,7 @@ Plan model_plan(int M, int N, int K) {
     const bool deep = KS > 64;
     // quantiser waves for the whole workgroup: at least 8 M blocks, or 4
     // with a short K or a wide N, when the split's K fits their budget
-    const bool shared = KS <= 32 && (RBm >= 8 || (RBm >= 4 && (KS <= 8 || N >= 7168)));
+    const bool shared = KS <= 24 && (RBm >= 8 || (RBm >= 4 && (KS <= 8 || N >= 7168)));
     const bool pre = !shared && RBm >= 4 && KS > 8 && (RBm > 4 || N >= 7168 || KS > 32);
     Plan p;
     p.finish = 0;
@@ -156,7 +158,7 @@ Plan model_plan(int M, int N, int K) {
         p.mb = 1;
         p.nb = 1;
         p.wn = gb.RB % 3 == 0 ? 3 : 4;
-        p.wk = 4;
+        p.wk = 8;
         return p;
     }
     if (pre) {

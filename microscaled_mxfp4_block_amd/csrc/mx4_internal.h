@@ -119,8 +119,9 @@ GemmKernelFn find_stream_kernel(const Plan& plan, int rq);
 size_t stream_lds_bytes(const Plan& plan);
 // The kernels of the shared mode (mx4_shared.hip): plan.wn MFMA waves of
 // plan.nb N blocks each and plan.wk quantiser waves per workgroup (mb = 1),
-// (nb, wn, wk) in {(1, 2, 2), (1, 4, 4), (2, 2, 2), (2, 4, 4)}, at most 32
-// K steps per split (16 with nb = 2 or wk = 2); no last-arrival finish.
+// (nb, wn, wk) in {(1, 2, 2), (1, 3, 4), (1, 3, 8), (1, 4, 4), (1, 4, 8),
+// (2, 2, 2), (2, 4, 4)}, at most 24
+// K steps per split (16 with nb = 2); no last-arrival finish.
 GemmKernelFn find_shared_kernel(const Plan& plan, int steps_per_split);
 size_t shared_lds_bytes(const Plan& plan, int steps_per_split);
 hipError_t launch_gemm(const GemmLaunch& gl, const GemmParams& p, hipStream_t s);

@@ -20,13 +20,13 @@
 //     first); after the barrier it reads its activation fragments from LDS
 //     and runs the MFMAs.  No two waves
 //     share a K range, so there is no cross-wave reduction.
-//   - QW quantiser waves, which load the workgroup's activation slice (32
-//     rows x the split's K) with whole 128-byte row segments per 8 lanes (a
-//     lane keeps one row and one 16-byte column of every K step, so no index
-//     needs a division), quantise each 32-element group across a DPP quad of
-//     lanes (amax, scale byte by the bit rule, e2m1 codes by the gfx950 fp4
-//     convert) and write codes and scale bytes into LDS in MFMA lane order,
-//     once for all the MFMA waves; then they join the barrier.
+//   - QW quantiser waves, which share out the K steps of the workgroup's
+//     activation slice (32 rows x the split's K): each loads its steps'
+//     bf16 tiles straight into LDS (whole 128-byte row segments per 8
+//     lanes), then every lane quantises one row's 32-element group of a step
+//     in registers (amax, scale byte by the bit rule, e2m1 codes by the
+//     gfx950 fp4 convert) and writes the MFMA fragment and scale byte into
+//     LDS, once for all the MFMA waves; then they join the barrier.
 // The two kinds of loads are issued by different waves, so neither waits
 // for the other's (a wave's vector-memory counter runs in issue order).
 // Rows past M read zeros through the buffer bound (zero codes, scale byte
@@ -39,10 +39,15 @@
 
 namespace mx4 {
 
-// LDS: the quantised activation slice, [KR][64 lanes][16 B] codes then
-// [KR][64] scale bytes; the staged bf16 output tile aliases it after the
-// MFMAs.
+// LDS: the quantised activation slice, [KR][64 lanes][16 B] codes then the
+// scale bytes as [KR / 4][64 lanes] words (byte b: step 4 w + b); the staged
+// bf16 output tile aliases it after the MFMAs.
 __host__ __device__ constexpr size_t shared_aop_bytes(int kr) { return (size_t)kr * 64 * 17; }
+// then the raw bf16 tiles of the slice, one 4 KiB tile per K step
+constexpr int kRawTile = kRowBlock * 128;
+__host__ __device__ constexpr size_t shared_raw_offset(int kr) { return (shared_aop_bytes(kr) + 255) / 256 * 256; }
+__host__ __device__ constexpr size_t shared_all_bytes(int kr) { return shared_raw_offset(kr) + (size_t)kr * kRawTile; }
+__host__ __device__ constexpr int raw_slot(int r, int j) { return r * 128 + ((j ^ ((r >> 1) & 7)) << 4); }
 __host__ __device__ constexpr size_t shared_stage_bytes(int nb, int wn) {
     return (size_t)kRowBlock * (nb * wn * kRowBlock + 8) * 2;
 }
@@ -62,6 +67,7 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     uint8_t* aop = lds;                             // codes, KR * 1 KiB
     uint8_t* asc = lds + (size_t)KR * 1024;         // scale bytes, KR * 64
+    uint8_t* raw = lds + shared_raw_offset(KR);      // bf16 tiles, KR * 4 KiB
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = tid & 63;
@@ -82,37 +88,38 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
         for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
 
     u32x4 bfrag[KR][NB];
-    uint32_t bscale[KR][NB];
+    uint32_t bscale[KR / 4][NB];   // one word per 4 steps (byte b: step 4 w + b when tb % 4 == 0)
     // The activation loads go out before the weight's: a CU returns the loads
     // of its waves roughly in the order it takes them, and the activation
     // (L2-resident) must arrive early for the quantisers, while the weight
     // (HBM) is consumed last.
-    constexpr int NQ = QW * 64;
-    constexpr int RPL = kRowBlock * 8 / NQ;          // slice rows per quantiser lane
-    u32x4 xs[RPL][KR];
-    const int li = (wave - WN) * 64 + L;
-    const int col = li & 7;                          // 16-byte column in the step's row segment
-    const int h = col >> 2, q = col & 3;             // group of the step, quarter of the group
+    // Quantiser wave w (0 .. QW - 1) takes the K steps w, w + QW, ... of the
+    // split: each step's 32 x 64 bf16 tile goes straight into LDS (gfx950
+    // buffer loads to LDS, four 1 KiB loads, 8 lanes per 128-byte row
+    // segment, 16-byte column j of row r at slot j ^ ((r >> 1) & 7)).
+    constexpr int KL = KR / QW;                      // steps per quantiser wave
+    static_assert(KR % QW == 0, "whole steps per quantiser wave");
+    const int qw = wave - WN;
     if (!mfma_wave) {
-        // ---- the activation slice: rows 32 mt .. 32 mt + 31, steps tb .. te - 1.
-        // The QW quantiser waves hold 64 QW lanes: lane li takes slice rows
-        // li / 8 + 64 QW / 8 * i (i < 32 * 8 / (64 QW)) and, in every K step,
-        // the 16-byte column li % 8 of the row's 128-byte segment: 8 lanes
-        // read one row segment, a DPP quad (4 consecutive lanes) holds one
-        // 32-element group.
+        // ---- the activation slice: rows 32 mt .. 32 mt + 31, steps tb .. te - 1
         const Rsrc ra = make_rsrc(A, (uint32_t)M * (uint32_t)lda * 2u);
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const int r = (li >> 3) + (NQ / 8) * i;
-            const uint32_t rowoff = (uint32_t)(mt * kRowBlock + r) * (uint32_t)lda * 2u + (uint32_t)tb * 128u +
-                                    (uint32_t)col * 16u;
+        for (int k = 0; k < KL; ++k) {
+            const int s = qw + QW * k;
 #pragma unroll
-            for (int s = 0; s < KR; ++s) {
-                // steps past the split and a group past K (K % 64 == 32) read zeros
-                const bool live = s < T && 2 * (tb + s) + h < G;
-                xs[i][s] = bload16(ra, live ? rowoff + (uint32_t)s * 128u : kOutOfRange, 0u);
+            for (int c4 = 0; c4 < 4; ++c4) {
+                const int c = c4 * 64 + L;
+                const int r = c >> 3;
+                const int j = (c & 7) ^ ((r >> 1) & 7);
+                // steps past the split and a group past K (K % 64 == 32) read
+                // zeros; rows past M read zeros through the buffer bound
+                const bool live = s < T && 2 * (tb + s) + (j >> 2) < G;
+                const uint32_t off = (uint32_t)(mt * kRowBlock + r) * (uint32_t)lda * 2u +
+                                     (uint32_t)(tb + s) * 128u + (uint32_t)j * 16u;
+                bload16_lds(ra, raw + (size_t)s * kRawTile + c4 * 1024, live ? off : kOutOfRange);
             }
         }
+        asm volatile("" ::: "memory");
     }
     __syncthreads();   // the activation loads are issued
     if (mfma_wave) {
@@ -128,36 +135,51 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
                 const int nb = min(nb0 + j, RBn - 1);   // clamped blocks are never stored
                 bfrag[s][j] = bload16<kNonTemporal>(rb, on ? (uint32_t)L * 16u : kOutOfRange,
                                                     (uint32_t)(nb * KS + t) * 1024u);
-                bscale[s][j] = bload4(rb, on ? (uint32_t)L * 4u : kOutOfRange,
-                                      (uint32_t)gb.code_bytes + (uint32_t)(nb * KW + (t >> 2)) * 256u);
+            }
+            // the scale word of steps tb + s .. tb + s + 3 (splits start at
+            // multiples of 4 steps, so these share one packed word)
+            if (s % 4 == 0) {
+#pragma unroll
+                for (int j = 0; j < NB; ++j) {
+                    const int nb = min(nb0 + j, RBn - 1);
+                    bscale[s / 4][j] = bload4(rb, on ? (uint32_t)L * 4u : kOutOfRange,
+                                              (uint32_t)gb.code_bytes + (uint32_t)(nb * KW + (t >> 2)) * 256u);
+                }
             }
         }
     }
     if (!mfma_wave) {
-        // each load is quantised as it lands; steps past the split quantise
-        // zeros: zero codes, scale byte 0
+        // every tile of this wave has landed (its only vector-memory operations
+        // are those loads); lane L quantises row L % 32, group L / 32 of each
+        // of its steps in registers and writes the MFMA fragment (16 bytes)
+        // and scale byte; steps past the split quantise zeros: zero codes,
+        // scale byte 0.
+        wait_vmcnt<0>();
+        asm volatile("" ::: "memory");
 #pragma unroll
-        for (int i = 0; i < RPL; ++i) {
-            const int r = (li >> 3) + (NQ / 8) * i;
+        for (int k = 0; k < KL; ++k) {
+            const int s = qw + QW * k;
+            const uint8_t* tile = raw + (size_t)s * kRawTile;
+            u32x4 x[4];
 #pragma unroll
-            for (int s = 0; s < KR; ++s) {
-                uint32_t byte;
-                const uint32_t codes = quad_quant8(xs[i][s], byte);
-                const int u = s * 64 + r + 32 * h;   // MFMA lane slot of (row r, group 2 s + h)
-                *(uint32_t*)(aop + 16 * u + 4 * q) = codes;
-                if (q == 0) asc[u] = (uint8_t)byte;
-            }
+            for (int c = 0; c < 4; ++c) x[c] = *(const u32x4*)(tile + raw_slot(L & 31, 4 * (L >> 5) + c));
+            u32x4 codes;
+            const uint32_t byte = quant_group32(x, codes);
+            *(u32x4*)(aop + 16 * (s * 64 + L)) = codes;
+            asc[((s >> 2) * 64 + L) * 4 + (s & 3)] = (uint8_t)byte;   // byte s % 4 of the lane's word
         }
     }
     __syncthreads();   // the quantised slice is in LDS
     if (mfma_wave) {
+        uint32_t aw = 0;
 #pragma unroll
         for (int s = 0; s < KR; ++s) {
             const u32x4 af = *(const u32x4*)(aop + 16 * (s * 64 + L));
-            const uint32_t as = asc[s * 64 + L];
-            const int sh = 8 * ((tb + s) & 3);      // byte of step tb + s in its scale word
+            if (s % 4 == 0) aw = *(const uint32_t*)(asc + ((s >> 2) * 64 + L) * 4);
+            const int sh = 8 * (s & 3);              // byte of step tb + s in both scale words
 #pragma unroll
-            for (int j = 0; j < NB; ++j) acc[j] = mfma_fp4_32x32x64(bfrag[s][j], af, acc[j], bscale[s][j] >> sh, as);
+            for (int j = 0; j < NB; ++j)
+                acc[j] = mfma_fp4_32x32x64(bfrag[s][j], af, acc[j], bscale[s / 4][j] >> sh, aw >> sh);
         }
     }
     if (mfma_wave) {
@@ -218,24 +240,23 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
 }
 
 // ---------------------------------------------------------------------------
-// Instantiations: (NB, WN, QW) in {(1, 2, 2), (1, 3, 4), (1, 4, 4), (2, 2, 2),
-// (2, 4, 4)} and KR in {8, 16, 24, 32}.
+// Instantiations: (NB, WN, QW) in {(1, 2, 2), (1, 3, 4), (1, 3, 8), (1, 4, 4),
+// (1, 4, 8), (2, 2, 2), (2, 4, 4)} and KR in {8, 16, 24} (24 with NB = 1).
 
-// The weight registers bound NB * KR (<= 32 fragments per MFMA wave); the
-// activation loads in flight bound KR * 8 / QW (at most 32 chunks per lane).
+// The weight registers bound NB * KR (<= 24 fragments per MFMA wave) and LDS
+// the slice (KR 4 KiB raw tiles plus the quantised operand: KR <= 24).
 template <int NB, int WN, int QW>
 static GemmKernelFn shared_pick_kr(int kr) {
     switch (kr) {
         case 8: return gemm_shared_kernel<NB, WN, QW, 8>;
         case 16: return gemm_shared_kernel<NB, WN, QW, 16>;
-        case 24: return (NB == 1 && QW == 4) ? gemm_shared_kernel<1, WN, 4, 24> : nullptr;
-        case 32: return (NB == 1 && QW == 4) ? gemm_shared_kernel<1, WN, 4, 32> : nullptr;
+        case 24: return NB == 1 ? gemm_shared_kernel<1, WN, QW, 24> : nullptr;
         default: return nullptr;
     }
 }
 
 int shared_kr_for(int steps) {
-    static const int kBudgets[] = {8, 16, 24, 32};
+    static const int kBudgets[] = {8, 16, 24};
     for (int kr : kBudgets)
         if (steps <= kr) return kr;
     return 0;
@@ -248,6 +269,8 @@ GemmKernelFn find_shared_kernel(const Plan& plan, int steps_per_split) {
     const int kr = shared_kr_for(steps_per_split);
     if (plan.nb == 1 && plan.wn == 2 && plan.wk == 2) return shared_pick_kr<1, 2, 2>(kr);
     if (plan.nb == 1 && plan.wn == 3 && plan.wk == 4) return shared_pick_kr<1, 3, 4>(kr);
+    if (plan.nb == 1 && plan.wn == 3 && plan.wk == 8) return shared_pick_kr<1, 3, 8>(kr);
+    if (plan.nb == 1 && plan.wn == 4 && plan.wk == 8) return shared_pick_kr<1, 4, 8>(kr);
     if (plan.nb == 1 && plan.wn == 4 && plan.wk == 4) return shared_pick_kr<1, 4, 4>(kr);
     if (plan.nb == 2 && plan.wn == 2 && plan.wk == 2) return shared_pick_kr<2, 2, 2>(kr);
     if (plan.nb == 2 && plan.wn == 4 && plan.wk == 4) return shared_pick_kr<2, 4, 4>(kr);
@@ -255,7 +278,7 @@ GemmKernelFn find_shared_kernel(const Plan& plan, int steps_per_split) {
 }
 
 size_t shared_lds_bytes(const Plan& plan, int steps_per_split) {
-    const size_t a = shared_aop_bytes(shared_kr_for(steps_per_split));
+    const size_t a = shared_all_bytes(shared_kr_for(steps_per_split));
     const size_t st = shared_stage_bytes(plan.nb, plan.wn);
     return a > st ? a : st;
 }

@@ -138,8 +138,8 @@ def test_plans_for_workloads():
         assert p["finish"] in (B.MX_FINISH_KERNEL, B.MX_FINISH_LAST_ARRIVAL)
         if p["amode"] == B.MX_AMODE_SHARED:
             # wn MFMA waves + wk quantiser waves
-            assert (p["mb"], p["nb"], p["wn"], p["wk"]) in ((1, 1, 2, 2), (1, 1, 3, 4), (1, 1, 4, 4), (1, 2, 2, 2),
-                                                            (1, 2, 4, 4))
+            assert (p["mb"], p["nb"], p["wn"], p["wk"]) in ((1, 1, 2, 2), (1, 1, 3, 4), (1, 1, 3, 8), (1, 1, 4, 4),
+                                                            (1, 1, 4, 8), (1, 2, 2, 2), (1, 2, 4, 4))
         else:
             assert p["mb"] in (1, 2) and p["nb"] in (1, 2) and p["wn"] in (1, 2)
             assert p["wk"] in (1, 2, 4, 8, 16) and p["wn"] * p["wk"] <= 16
@@ -178,7 +178,7 @@ def test_explicit_plan_rejections():
            dict(mb=1, nb=4, wn=1, wk=16, splits=1, amode=4),     # stream mode: nb <= 2 at 16 waves
            dict(mb=1, nb=4, wn=1, wk=4, splits=1, amode=0),      # nb = 4 only in the stream mode
            dict(mb=1, nb=1, wn=1, wk=1, splits=1, amode=5),      # shared mode: no such wave split
-           dict(mb=1, nb=1, wn=4, wk=4, splits=2, amode=5),      # shared mode: 56 K steps > 32 per split
+           dict(mb=1, nb=1, wn=4, wk=4, splits=2, amode=5),      # shared mode: 56 K steps > 24 per split
            dict(mb=1, nb=1, wn=4, wk=4, splits=4, amode=5, finish=1),   # shared mode: no last-arrival finish
            dict(mb=1, nb=1, wn=1, wk=4, splits=4, amode=0, finish=2),   # no such split-K finish
            dict(mb=1, nb=1, wn=1, wk=4, splits=0, amode=1),
@@ -437,7 +437,7 @@ def test_noalloc_validates_before_any_hip_call():
 
 
 @pytest.mark.parametrize("src,kname,count", [("mx4_stream.s", "gemm_stream_kernel", 42),
-                                              ("mx4_shared.s", "gemm_shared_kernel", 16)])
+                                              ("mx4_shared.s", "gemm_shared_kernel", 19)])
 def test_mode_kernels_preload_arguments_and_never_spill(src, kname, count):
     """The K-looped stream-mode kernels and the quantiser-wave shared-mode
     kernels take the GEMM kernels' 72-byte scalar argument segment with its
