@@ -199,7 +199,7 @@ def stream_floor(torch, hw, st, B):
     mtiles = -(-((st.M + 31) // 32) // p["mb"])
     splits = p["splits"]
     wgs = ntiles * splits   # each weight byte once: the M tiles of an N tile share it
-    waves = p["wn"] * p["wk"]
+    waves = p["wn"] + p["wk"] if p["amode"] == 5 else p["wn"] * p["wk"]   # the shared mode: MFMA + quantiser waves
     chunk = -(-nbytes // wgs)
     chunk = -(-chunk // 16) * 16
     out = torch.empty(wgs * waves, dtype=torch.int32, device="cuda:0")
@@ -335,7 +335,7 @@ def stream_floor_profile(torch, hw, st, calls):
     nbytes = st.Ps[0].numel()
     ntiles = -(-((st.N + 31) // 32) // (p["nb"] * p["wn"]))
     wgs = ntiles * p["splits"]
-    waves = p["wn"] * p["wk"]
+    waves = p["wn"] + p["wk"] if p["amode"] == 5 else p["wn"] * p["wk"]   # the shared mode: MFMA + quantiser waves
     chunk = -(-(-(-nbytes // wgs)) // 16) * 16
     out = torch.empty(wgs * waves, dtype=torch.int32, device="cuda:0")
     s = torch.cuda.Stream()
