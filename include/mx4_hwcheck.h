@@ -5,10 +5,10 @@
  * same device wrappers as the GEMM and quantisation kernels, so a test can
  * compare the instructions' results with a host model element by element.
  *
- * All pointers are device pointers; each call enqueues one launch on
- * `stream` (a hipStream_t, NULL for the default stream) and returns 0, or -1
- * for a bad size or null pointer, -2 for a misaligned pointer, -4 when the
- * launch failed.  Nothing is allocated.
+ * Except in mxhw_xcd_map (host only), all pointers are device pointers; each
+ * call enqueues one launch on `stream` (a hipStream_t, NULL for the default
+ * stream) and returns 0, or -1 for a bad size or null pointer, -2 for a
+ * misaligned pointer, -4 when the launch failed.  Nothing is allocated.
  */
 #ifndef MX4_HWCHECK_H
 #define MX4_HWCHECK_H
@@ -48,6 +48,15 @@ int mxhw_mfma_fp4(const void* a_dev, const void* b_dev, const void* sa_dev, cons
  * (L2). */
 int mxhw_stream_read(const void* buf_dev, unsigned bytes, int wgs, int waves, int lpl,
                      unsigned chunk, unsigned stride, unsigned rot, void* out_dev, void* stream);
+
+/* Host only, no GPU call: the placement of the shared-mode GEMM's tiles on
+ * the 8 XCDs, by the library's own code.  For a one-split grid of mtiles x
+ * ntiles workgroups (at most 2^20) of `cols` weight columns over K,
+ * *map_out receives the placement code the kernel gets, and mt_out[lin] and
+ * nt_out[lin] (host arrays of mtiles * ntiles ints) the M and N tile of the
+ * workgroup with linear id lin = bx + ntiles * by.  Returns 0, or -1 for a
+ * bad size or null pointer. */
+int mxhw_xcd_map(int mtiles, int ntiles, int splits, int K, int cols, int* map_out, int* mt_out, int* nt_out);
 
 #ifdef __cplusplus
 }

@@ -791,15 +791,21 @@ bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
     if (!fn) return false;
     // the shared mode's workgroup is wn MFMA waves plus wk quantiser waves
     const int waves = plan.amode == kAmShared ? plan.wn + plan.wk : plan.wn * plan.wk;
+    // the shared kernels take their tile placement in bits 8 and up of the
+    // steps-per-split argument (at most 24 steps)
+    const int steps_arg =
+        plan.amode == kAmShared
+            ? p.steps_per_split | (shared_xcd_map(p.mtiles, p.ntiles, p.splits, p.K, 32 * plan.nb * plan.wn) << 8)
+            : p.steps_per_split;
     *out = GemmLaunch{fn, (unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits, (unsigned)(64 * waves),
-                      gemm_lds_bytes(plan, p.steps_per_split), plan.amode == kAmPrequant};
+                      gemm_lds_bytes(plan, p.steps_per_split), plan.amode == kAmPrequant, steps_arg};
     return true;
 }
 
 hipError_t launch_gemm(const GemmLaunch& gl, const GemmParams& p, hipStream_t s) {
     const void* a_src = gl.prequant ? (const void*)p.aop : (const void*)p.A;
     return launch_kernel(gl.fn, dim3(gl.gx, gl.gy, gl.gz), dim3(gl.block), gl.lds, s, a_src, p.bp, p.C, p.partial,
-                         p.lda, p.ldc, p.M, p.N, p.K, p.steps_per_split, p.counters, p.splits, p.mtiles);
+                         p.lda, p.ldc, p.M, p.N, p.K, gl.steps_arg, p.counters, p.splits, p.mtiles);
 }
 
 hipError_t launch_reduce(const GemmParams& p, hipStream_t s) {

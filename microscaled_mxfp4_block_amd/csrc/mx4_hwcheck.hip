@@ -19,6 +19,7 @@
 // GEMM's time can be set against what merely streaming its bytes costs with
 // the same grid.
 #include "mx4_device.h"
+#include "mx4_internal.h"
 #include "../../include/mx4_hwcheck.h"
 
 namespace mx4 {
@@ -139,6 +140,20 @@ int mxhw_mfma_fp4(const void* a_dev, const void* b_dev, const void* sa_dev, cons
     hipLaunchKernelGGL(mx4::hw_mfma_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, (const uint8_t*)a_dev,
                        (const uint8_t*)b_dev, (const uint32_t*)sa_dev, (const uint32_t*)sb_dev, (float*)out_dev);
     return hipGetLastError() == hipSuccess ? 0 : -4;
+}
+
+int mxhw_xcd_map(int mtiles, int ntiles, int splits, int K, int cols, int* map_out, int* mt_out, int* nt_out) {
+    if (mtiles < 1 || ntiles < 1 || (long long)mtiles * ntiles > (1 << 20) || splits < 1 || K < 1 || cols < 1 ||
+        !map_out || !mt_out || !nt_out)
+        return -1;
+    const int map = mx4::shared_xcd_map(mtiles, ntiles, splits, K, cols);
+    *map_out = map;
+    for (int by = 0; by < mtiles; ++by)
+        for (int bx = 0; bx < ntiles; ++bx) {
+            const int lin = bx + ntiles * by;
+            mx4::shared_tile_of(bx, by, ntiles, map, mt_out[lin], nt_out[lin]);
+        }
+    return 0;
 }
 
 }  // extern "C"

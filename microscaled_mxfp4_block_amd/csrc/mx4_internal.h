@@ -110,6 +110,7 @@ struct GemmLaunch {
     unsigned gx, gy, gz, block;
     size_t lds;
     bool prequant;   // the activation source is the pre-quantised operand
+    int steps_arg;   // the kernel's steps-per-split argument (with the shared mode's placement code)
 };
 bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out);
 // The K-looped kernels of the stream mode (mx4_stream.hip): one M block and
@@ -124,6 +125,62 @@ size_t stream_lds_bytes(const Plan& plan);
 // K steps per split (16 with nb = 2); no last-arrival finish.
 GemmKernelFn find_shared_kernel(const Plan& plan, int steps_per_split);
 size_t shared_lds_bytes(const Plan& plan, int steps_per_split);
+
+// Placement of the shared kernel's tiles on the 8 XCDs.  The dispatcher
+// hands the workgroups of a grid, in x-major order, to XCD (linear id mod 8),
+// and each XCD's L2 fetches every activation row block and weight column
+// block its workgroups touch.  A one-split grid of mtiles x ntiles
+// workgroups (`cols` weight columns each) is laid out so that the workgroups
+// of one XCD take a rectangle of a M tiles x b N tiles (a b = tiles / 8),
+// the rectangle that costs the fewest fetched bytes: a * 64 K of bf16
+// activation plus b * cols (K / 2 + K / 32) of packed weight.  a and
+// mtiles / a are powers of two (the kernel decodes with shifts).
+// shared_xcd_map returns the placement code: 0 when no rectangle fits (the
+// dispatcher's order), else 1 + la + 16 lmg with a = 2^la M tiles per XCD
+// and 2^lmg groups of M tiles.  It reaches the kernel in bits 8 and up of
+// its steps-per-split argument (a shared-mode split has at most 24 steps),
+// which is among the preloaded arguments: the first loads' addresses wait
+// on no argument-segment read.
+inline int shared_xcd_map(int mtiles, int ntiles, int splits, int K, int cols) {
+    if (splits != 1 || mtiles < 1 || ntiles < 1 || ((long long)mtiles * ntiles) % 8 != 0) return 0;
+    const double a_bytes = 64.0 * K;
+    const double b_bytes = cols * (K / 2.0 + K / 32.0);
+    int best = 0;
+    double best_cost = 0.0;
+    for (int lmg = 0; lmg <= 3; ++lmg) {
+        const int mg = 1 << lmg, ng = 8 >> lmg;   // M groups x N groups = 8 XCDs
+        if (mtiles % mg != 0 || ntiles % ng != 0) continue;
+        const int a = mtiles / mg, b = ntiles / ng;
+        if ((a & (a - 1)) != 0) continue;
+        int la = 0;
+        while ((1 << la) < a) ++la;
+        const double cost = a * a_bytes + b * b_bytes;
+        if (best == 0 || cost < best_cost) {
+            best = 1 + la + 16 * lmg;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+// Tile (mt, nt) of workgroup (bx, by) of an ntiles-wide grid under
+// placement code xcd_map:
+// the workgroups with linear id lin = bx + ntiles by, x = lin mod 8 and
+// j = lin / 8 take M tile (x mod 2^lmg) 2^la + (j mod 2^la) and N tile
+// (x / 2^lmg) b + j / 2^la, b = ntiles / 2^(3 - lmg) N tiles per XCD.
+__host__ __device__ inline void shared_tile_of(int bx, int by, int ntiles, int xcd_map, int& mt, int& nt) {
+    if (xcd_map == 0) {
+        mt = by;
+        nt = bx;
+        return;
+    }
+    const int la = (xcd_map - 1) & 15, lmg = (xcd_map - 1) >> 4;
+    const int lin = bx + ntiles * by;
+    const int x = lin & 7, j = lin >> 3;
+    const int b = ntiles >> (3 - lmg);
+    mt = ((x & ((1 << lmg) - 1)) << la) + (j & ((1 << la) - 1));
+    nt = (x >> lmg) * b + (j >> la);
+}
 hipError_t launch_gemm(const GemmLaunch& gl, const GemmParams& p, hipStream_t s);
 hipError_t launch_reduce(const GemmParams& p, hipStream_t s);
 

@@ -28,7 +28,17 @@
 //     gfx950 fp4 convert) and writes the MFMA fragment and scale byte into
 //     LDS, once for all the MFMA waves; then they join the barrier.
 // The two kinds of loads are issued by different waves, so neither waits
-// for the other's (a wave's vector-memory counter runs in issue order).
+// for the other's (a wave's vector-memory counter runs in issue order).  The
+// barrier between the two issues orders them and nothing else: it carries no
+// memory fence, which would make every quantiser wave wait for its whole
+// slice to land (buffer loads to LDS count as LDS writes) before any weight
+// load could go out.  Each quantiser wave then waits for its own steps one at
+// a time, and the slice barrier waits only for the quantisers' LDS writes, so
+// the MFMA waves' weight loads stay in flight across it.
+// Workgroups are grouped onto the XCDs (shared_xcd_map): the workgroups the
+// dispatcher sends to one XCD (linear id mod 8) take a rectangle of a M tiles
+// x b N tiles, chosen so that the activation rows and weight columns that
+// one XCD's L2 must fetch are fewest.
 // Rows past M read zeros through the buffer bound (zero codes, scale byte
 // 0); steps past the split read zeros; a group past K (K % 64 == 32) is
 // zeroed explicitly.  The epilogue stages each MFMA wave's bf16 tile in LDS
@@ -52,13 +62,38 @@ __host__ __device__ constexpr size_t shared_stage_bytes(int nb, int wn) {
     return (size_t)kRowBlock * (nb * wn * kRowBlock + 8) * 2;
 }
 
+// s_waitcnt for at most 4 n outstanding vector-memory operations (n a
+// constant after unrolling: the switch folds to one instruction).
+__device__ __forceinline__ void wait_steps_left(int n) {
+    switch (n) {
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<4>(); break;
+        case 2: wait_vmcnt<8>(); break;
+        case 3: wait_vmcnt<12>(); break;
+        case 4: wait_vmcnt<16>(); break;
+        case 5: wait_vmcnt<20>(); break;
+        case 6: wait_vmcnt<24>(); break;
+        case 7: wait_vmcnt<28>(); break;
+        case 8: wait_vmcnt<32>(); break;
+        case 9: wait_vmcnt<36>(); break;
+        case 10: wait_vmcnt<40>(); break;
+        case 11: wait_vmcnt<44>(); break;
+        default: wait_vmcnt<0>(); break;
+    }
+}
+
+// steps_arg: the steps per K split (at most 24) in bits 0..7, and above them
+// the code that places the workgroups' tiles on the XCDs (shared_xcd_map,
+// shared_tile_of; 0: tile (blockIdx.y, blockIdx.x)).
 template <int NB, int WN, int QW, int KR>
 __global__ void __launch_bounds__(64 * (WN + QW))
 gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_buf, int lda, int ldc, int M,
-                   int N, int K, int steps_per_split, uint32_t* counters, int splits, int mtiles) {
+                   int N, int K, int steps_arg, uint32_t* counters, int splits, int mtiles) {
     (void)counters;
     (void)splits;
     (void)mtiles;
+    const int steps_per_split = steps_arg & 0xFF;
+    const int xcd_map = steps_arg >> 8;
     constexpr uint32_t kOutOfRange = 0x80000000u;
     const OperandGeom gb = operand_geom(N, K);
     const int KS = gb.KS, KW = gb.KW, RBn = gb.RB;
@@ -72,8 +107,8 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = tid & 63;
 
-    const int nt = blockIdx.x;
-    const int mt = blockIdx.y;
+    int mt, nt;
+    shared_tile_of((int)blockIdx.x, (int)blockIdx.y, (RBn + WN * NB - 1) / (WN * NB), xcd_map, mt, nt);
     const int split = blockIdx.z;
     const int tb = split * steps_per_split;
     const int te = min(tb + steps_per_split, KS);
@@ -99,6 +134,7 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
     // segment, 16-byte column j of row r at slot j ^ ((r >> 1) & 7)).
     constexpr int KL = KR / QW;                      // steps per quantiser wave
     static_assert(KR % QW == 0, "whole steps per quantiser wave");
+    static_assert(KL <= 12, "wait_steps_left covers 12 steps per quantiser wave");
     const int qw = wave - WN;
     if (!mfma_wave) {
         // ---- the activation slice: rows 32 mt .. 32 mt + 31, steps tb .. te - 1
@@ -121,7 +157,7 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
         }
         asm volatile("" ::: "memory");
     }
-    __syncthreads();   // the activation loads are issued
+    __builtin_amdgcn_s_barrier();   // the activation loads are issued (no fence: see the top)
     if (mfma_wave) {
         // ---- the weight: every fragment and scale word of the split in flight
         // at once (steps past the split read zeros)
@@ -149,15 +185,16 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
         }
     }
     if (!mfma_wave) {
-        // every tile of this wave has landed (its only vector-memory operations
-        // are those loads); lane L quantises row L % 32, group L / 32 of each
-        // of its steps in registers and writes the MFMA fragment (16 bytes)
-        // and scale byte; steps past the split quantise zeros: zero codes,
-        // scale byte 0.
-        wait_vmcnt<0>();
-        asm volatile("" ::: "memory");
+        // step k of this wave has landed once at most the 4 loads of each of
+        // its KL - 1 - k later steps are outstanding (its only vector-memory
+        // operations are those loads, and they complete in issue order);
+        // lane L quantises row L % 32, group L / 32 of the step in registers
+        // and writes the MFMA fragment (16 bytes) and scale byte; steps past
+        // the split quantise zeros: zero codes, scale byte 0.
 #pragma unroll
         for (int k = 0; k < KL; ++k) {
+            wait_steps_left(KL - 1 - k);
+            asm volatile("" ::: "memory");
             const int s = qw + QW * k;
             const uint8_t* tile = raw + (size_t)s * kRawTile;
             u32x4 x[4];
@@ -169,7 +206,10 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
             asc[((s >> 2) * 64 + L) * 4 + (s & 3)] = (uint8_t)byte;   // byte s % 4 of the lane's word
         }
     }
-    __syncthreads();   // the quantised slice is in LDS
+    // The quantised slice is in LDS: each wave's LDS writes have completed
+    // before the barrier.  No vector-memory wait: the MFMA waves' weight
+    // loads stay in flight, and each MFMA waits for its own fragment.
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (mfma_wave) {
         uint32_t aw = 0;
 #pragma unroll

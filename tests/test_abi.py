@@ -7,6 +7,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 import torch
 
@@ -411,7 +412,7 @@ def test_hwcheck_library_exports_its_header():
     include/mx4_hwcheck.h declares, and libmx4.so exports none of them."""
     hdr = open(os.path.join(ROOT, "include", "mx4_hwcheck.h")).read()
     names = sorted(set(re.findall(r"^\s*int\s+(mxhw_\w+)\s*\(", hdr, re.M)))
-    assert len(names) == 4
+    assert len(names) == 5
     hwlib = os.path.join(ROOT, "microscaled_mxfp4_block_amd", "libmx4hw.so")
     out = subprocess.run(["nm", "-D", "--defined-only", hwlib], stdout=subprocess.PIPE, text=True, check=True).stdout
     exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
@@ -419,6 +420,61 @@ def test_hwcheck_library_exports_its_header():
     main = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], stdout=subprocess.PIPE, text=True,
                           check=True).stdout
     assert "mxhw_" not in main
+
+
+def xcd_fetch_cost(mt, nt, K, cols):
+    """Bytes the 8 XCDs' L2s fetch when workgroup lin runs on XCD lin % 8:
+    per XCD, its distinct M tiles' bf16 activation rows (32 x K x 2 bytes)
+    and its distinct N tiles' packed weight (cols x (K/2 + K/32))."""
+    lin = np.arange(mt.size)
+    cost = 0.0
+    for x in range(8):
+        sel = lin % 8 == x
+        cost += np.unique(mt[sel]).size * 64.0 * K + np.unique(nt[sel]).size * cols * (K / 2 + K / 32)
+    return cost
+
+
+def test_shared_xcd_map_places_every_tile_once_and_fetches_no_more():
+    """The shared-mode GEMM's placement of tiles on the XCDs (library code,
+    through libmx4hw.so's host-only hook): every (M tile, N tile) goes to
+    exactly one workgroup for every grid, the dispatcher's order is kept
+    where no rectangle fits, the chosen placement never makes the XCDs fetch
+    more than the dispatcher's order would, and 256 x 3072 x 1536 (8 x 32
+    tiles of 96 columns) gets 4 M tiles x 8 N tiles per XCD."""
+    hwlib = os.path.join(ROOT, "microscaled_mxfp4_block_amd", "libmx4hw.so")
+    hw = ctypes.CDLL(hwlib)
+    I, P = ctypes.c_int, ctypes.c_void_p
+    hw.mxhw_xcd_map.argtypes = [I, I, I, I, I, P, P, P]
+
+    def place(mtiles, ntiles, splits, K, cols):
+        T = mtiles * ntiles
+        mt, nt, mp = (ctypes.c_int * T)(), (ctypes.c_int * T)(), ctypes.c_int(-1)
+        assert hw.mxhw_xcd_map(mtiles, ntiles, splits, K, cols, ctypes.byref(mp), mt, nt) == 0
+        return mp.value, np.frombuffer(mt, np.int32).copy(), np.frombuffer(nt, np.int32).copy()
+
+    remapped = 0
+    for mtiles in (1, 2, 3, 4, 5, 6, 8, 12, 16, 32):
+        for ntiles in range(1, 66):
+            for K, cols in ((1536, 96), (512, 128), (7168, 64)):
+                mp, mt, nt = place(mtiles, ntiles, 1, K, cols)
+                T = mtiles * ntiles
+                assert mt.min() >= 0 and mt.max() < mtiles and nt.min() >= 0 and nt.max() < ntiles
+                assert np.unique(mt.astype(np.int64) * ntiles + nt).size == T, (mtiles, ntiles, mp)
+                lin = np.arange(T)
+                d_mt, d_nt = lin // ntiles, lin % ntiles
+                if mp == 0:
+                    assert np.array_equal(mt, d_mt) and np.array_equal(nt, d_nt)
+                else:
+                    remapped += 1
+                    assert T % 8 == 0
+                    assert xcd_fetch_cost(mt, nt, K, cols) <= xcd_fetch_cost(d_mt, d_nt, K, cols) + 1e-6
+    assert remapped > 100
+    mp, mt, nt = place(8, 32, 1, 1536, 96)
+    for x in range(8):
+        sel = np.arange(256) % 8 == x
+        assert np.unique(mt[sel]).size == 4 and np.unique(nt[sel]).size == 8
+    assert place(8, 32, 2, 1536, 96)[0] == 0       # K splits keep the dispatcher's order
+    assert hw.mxhw_xcd_map(0, 32, 1, 1536, 96, None, None, None) == -1
 
 
 def test_noalloc_validates_before_any_hip_call():
