@@ -349,6 +349,41 @@ def test_lds_dma_tiles_are_read_only_after_their_loads_land():
     assert checked > 50
 
 
+def test_shared_kernels_keep_weight_loads_in_flight_across_barriers():
+    """In every shared-mode kernel: the barrier between the quantiser waves'
+    loads to LDS and the MFMA waves' weight loads waits for no vector memory
+    (no vmcnt wait between the last load to LDS and it); the first LDS read
+    of the quantisers comes after a vmcnt wait that covers their first step
+    and no more (4 (KL - 1) loads left outstanding, KL = KR / QW steps per
+    wave); and the slice barrier after the quantisation
+    waits only for LDS (it is preceded by `s_waitcnt lgkmcnt(0)` alone), so
+    the weight loads stay in flight across it."""
+    build = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "_build")
+    path = os.path.join(build, "mx4_shared.s")
+    if not os.path.exists(path):
+        pytest.skip("no device assembly under _build (run the package build first)")
+    text = open(path).read()
+    checked = 0
+    for m in re.finditer(r"^(_ZN3mx418gemm_shared_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E\S*):.*?^\.Lfunc_end",
+                         text, re.S | re.M):
+        name = m.group(1)
+        QW, KR = int(m.group(4)), int(m.group(5))
+        KL = KR // QW
+        body = [ln for ln in m.group(0).splitlines() if not ln.strip().startswith(";")]
+        dma = [k for k, ln in enumerate(body) if re.match(r"^\s*buffer_load_dwordx4\b", ln) and ln.rstrip().endswith(" lds")]
+        bars = [k for k, ln in enumerate(body) if ln.strip() == "s_barrier"]
+        assert len(dma) == 4 * KL and bars, name
+        b1 = next(k for k in bars if k > dma[-1])
+        assert not any("vmcnt" in ln for ln in body[dma[-1]:b1]), (name, "vmcnt wait before the first barrier")
+        r1 = next(k for k in range(b1, len(body)) if body[k].strip().startswith("ds_read"))
+        waits = [int(w.group(1)) for ln in body[b1:r1] for w in [re.search(r"vmcnt\((\d+)\)", ln)] if w]
+        assert waits and waits[-1] == 4 * (KL - 1), (name, waits)   # the first step only
+        b2 = next(k for k in bars if k > r1)
+        assert body[b2 - 1].strip() == "s_waitcnt lgkmcnt(0)", (name, body[b2 - 1])
+        checked += 1
+    assert checked == 19, checked
+
+
 def test_shapes_past_the_addressing_limit_are_refused():
     """rows * K * 2 >= 2^31 for an operand (32-bit buffer offsets) is refused
     before any launch; just below it is accepted."""
