@@ -549,8 +549,9 @@ GRID_BATCH = [1, 2, 4, 8, 16, 32, 64, 128, 256]
 def regret_candidates(B, M, N, K):
     """Plans timed against the library's own for one grid shape: the
     register-quantising mode over wave and split counts and two N widths,
-    the pre-quantising mode over its tile shapes, the LDS mode; only those
-    the planner accepts."""
+    the pre-quantising mode over its tile shapes, the LDS mode, the shared
+    mode over its MFMA and quantiser waves and splits; only those the
+    planner accepts."""
     cands = []
     for nb in (1, 2):
         for wk in (2, 4, 8):
@@ -562,8 +563,9 @@ def regret_candidates(B, M, N, K):
     for sp in (1, 2, 4):
         cands.append(dict(mb=1, nb=1, wn=1, wk=8, splits=sp, amode=0, finish=0))
     for wn in (3, 4):
-        for sp in (1, 2, 4, 8):
-            cands.append(dict(mb=1, nb=1, wn=wn, wk=4, splits=sp, amode=5, finish=0))
+        for wk in (4, 8):
+            for sp in (1, 2, 4, 7, 8, 14):
+                cands.append(dict(mb=1, nb=1, wn=wn, wk=wk, splits=sp, amode=5, finish=0))
     out = []
     for p in cands:
         try:
@@ -574,10 +576,12 @@ def regret_candidates(B, M, N, K):
     return out
 
 
-def plan_regret(torch, B, inputs, only=None):
+def plan_regret(torch, B, inputs, only=None, out=None):
     """Graph-replay GPU time per call of the library's plan and of the
     candidate plans for every grid shape (weights rotating over copies
-    >= 256 MiB); writes profiles/plan_regret.md and .json."""
+    >= 256 MiB).  With `out`, every candidate's time goes to that JSON file
+    (a part, for --regret-merge); else the summary goes to
+    profiles/plan_regret.*."""
     dev = "cuda:0"
     results = []
     pairs = GRID_DIM_PAIRS if only is None else [GRID_DIM_PAIRS[i] for i in only]
@@ -607,22 +611,34 @@ def plan_regret(torch, B, inputs, only=None):
             best_us, best = min(rows, key=lambda r: r[0])
             results.append({"M": M, "N": N, "K": K, "plan": lib_plan, "us": round(lib_us, 3), "best_plan": best,
                             "best_us": round(best_us, 3), "regret": round(lib_us / best_us, 3),
-                            "candidates": len(rows)})
+                            "candidates": len(rows), "all": [[round(u, 3), p] for u, p in rows]})
             print("regret %4d x %4d x %4d  plan %.3f us  best %.3f us  x%.3f  %s" % (
                 M, N, K, lib_us, best_us, lib_us / best_us, best), file=sys.stderr, flush=True)
             del A0, C0
         del Ps, P0
         torch.cuda.empty_cache()
+    if out:
+        with open(out, "w") as f:
+            json.dump({"shapes": results}, f)
+    else:
+        regret_summary(results, "`python3 bench.py --plan-regret`")
+
+
+def regret_summary(results, command):
+    """profiles/plan_regret.md and .json from the timed shapes (without the
+    per-candidate times)."""
     regrets = [r["regret"] for r in results]
     geo = float(np.exp(np.mean(np.log(regrets)))) if regrets else float("nan")
     lines = ["# Planner regret on the pages' shape grid", "",
-             "`python3 bench.py --plan-regret`: for each of the %d shapes (19 (N, K) weight shapes of the "
+             "%s: for each of the %d shapes (19 (N, K) weight shapes of the "
              "kernelindex.com amd-mxfp4-mm pages' synthesized config CSV, submission 754569, times M = 1 .. 256), "
-             "the HIP-graph-replay GPU time per call of the plan mx_gemm picks (the measured table for the five "
+             "the HIP-graph-replay GPU time per call of the plan mx_gemm picks (the measured table for the "
              "workloads, the model elsewhere) against the fastest of up to %d candidate plans (register-quantising "
-             "mode over waves, splits and N widths; pre-quantising mode over its tiles; LDS mode; quantiser-wave shared mode), weights rotating "
-             "over copies of >= 256 MiB. Regret = plan time / best time; geometric mean %.3f, worst %.3f." % (
-                 len(results), max((r["candidates"] for r in results), default=0), geo, max(regrets, default=0)),
+             "mode over waves, splits and N widths; pre-quantising mode over its tiles; LDS mode; quantiser-wave "
+             "shared mode over its waves and splits), weights rotating over copies of >= 256 MiB. "
+             "Regret = plan time / best time; geometric mean %.3f, worst %.3f." % (
+                 command, len(results), max((r["candidates"] for r in results), default=0), geo,
+                 max(regrets, default=0)),
              "", "| M | N | K | plan (mb nb wn wk splits amode) | us | best plan | best us | regret |",
              "|---|---|---|---|---|---|---|---|"]
 
@@ -634,28 +650,9 @@ def plan_regret(torch, B, inputs, only=None):
     with open(os.path.join(ROOT, "profiles", "plan_regret.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(os.path.join(ROOT, "profiles", "plan_regret.json"), "w") as f:
-        json.dump({"geomean_regret": geo, "shapes": results}, f, indent=0)
+        json.dump({"geomean_regret": geo, "shapes": [{k: v for k, v in r.items() if k != "all"} for r in results]},
+                  f, indent=0)
         f.write("\n")
-    print("\n".join(lines[:4]))
-
-
-def stats_markdown(stats_csv, command):
-    """profiles/bench_kernel_stats.md: the rocprofv3 --stats summary of the
-    mx4 kernels of one bench.py run under the tracer."""
-    import csv
-    with open(stats_csv) as f:
-        rows = [r for r in csv.DictReader(f) if "mx4::" in r["Name"]]
-    lines = ["# Kernel statistics of bench.py under rocprofv3", "",
-             "`%s` (the bench command of the bench line, fewer steps), `*_kernel_stats.csv` rows of the mx4 "
-             "kernels. Under the tracer consecutive dispatches start about 9 us apart, so each traced duration is "
-             "that of a kernel starting on an idle GPU; the bench line's GPU time per call is the untraced HIP-graph "
-             "replay." % command, "",
-             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
-    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
-        lines.append("| `%s` | %s | %.3f | %.3f | %.3f |" % (_short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
-                                                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
-    with open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w") as f:
-        f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
@@ -675,11 +672,26 @@ def main():
     ap.add_argument("--plan-regret", nargs="?", const="all", default=None, metavar="PAIRS",
                     help="time the library's plan against candidate plans on the pages' shape grid (PAIRS: "
                          "comma-separated indices of the (N, K) pairs, default all) and write profiles/plan_regret.*")
+    ap.add_argument("--regret-out", default=None, metavar="JSON",
+                    help="with --plan-regret: write every candidate's time to JSON (a part for --regret-merge) "
+                         "instead of profiles/plan_regret.*")
+    ap.add_argument("--regret-merge", nargs="+", metavar="JSON",
+                    help="no GPU: profiles/plan_regret.* from --regret-out parts (in grid order)")
     ap.add_argument("--stats-md", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="no GPU: profiles/bench_kernel_stats.md from a rocprofv3 --stats kernel_stats.csv")
     args = ap.parse_args()
     if args.stats_md:
         stats_markdown(*args.stats_md)
+        return
+    if args.regret_merge:
+        results = []
+        for path in args.regret_merge:
+            with open(path) as f:
+                results += json.load(f)["shapes"]
+        order = {nk: i for i, nk in enumerate(GRID_DIM_PAIRS)}
+        results.sort(key=lambda r: (order[(r["N"], r["K"])], r["M"]))
+        regret_summary(results, "`python3 bench.py --plan-regret PAIRS --regret-out PART` over parts of the grid, "
+                                "then `python3 bench.py --regret-merge PART...`")
         return
     if args.summarize:
         summarize_profiles(*args.summarize, args.summarize_calls)
@@ -699,7 +711,7 @@ def main():
         return
     if args.plan_regret:
         only = None if args.plan_regret == "all" else [int(i) for i in args.plan_regret.split(",")]
-        plan_regret(torch, B, inputs, only)
+        plan_regret(torch, B, inputs, only, args.regret_out)
         return
 
     per_workload = {}

@@ -62,23 +62,84 @@ __host__ __device__ constexpr size_t shared_stage_bytes(int nb, int wn) {
     return (size_t)kRowBlock * (nb * wn * kRowBlock + 8) * 2;
 }
 
-// s_waitcnt for at most 4 n outstanding vector-memory operations (n a
-// constant after unrolling: the switch folds to one instruction).
-__device__ __forceinline__ void wait_steps_left(int n) {
-    switch (n) {
+// s_waitcnt for at most RQ m outstanding vector-memory operations (RQ loads
+// per step, m later steps; m is a constant after unrolling, so the switch
+// folds to one instruction).
+template <int RQ>
+__device__ __forceinline__ void wait_steps_left(int m) {
+    switch (m) {
         case 0: wait_vmcnt<0>(); break;
-        case 1: wait_vmcnt<4>(); break;
-        case 2: wait_vmcnt<8>(); break;
-        case 3: wait_vmcnt<12>(); break;
-        case 4: wait_vmcnt<16>(); break;
-        case 5: wait_vmcnt<20>(); break;
-        case 6: wait_vmcnt<24>(); break;
-        case 7: wait_vmcnt<28>(); break;
-        case 8: wait_vmcnt<32>(); break;
-        case 9: wait_vmcnt<36>(); break;
-        case 10: wait_vmcnt<40>(); break;
-        case 11: wait_vmcnt<44>(); break;
+        case 1: wait_vmcnt<RQ>(); break;
+        case 2: wait_vmcnt<2 * RQ>(); break;
+        case 3: wait_vmcnt<3 * RQ>(); break;
+        case 4: wait_vmcnt<4 * RQ>(); break;
+        case 5: wait_vmcnt<5 * RQ>(); break;
+        case 6: wait_vmcnt<6 * RQ>(); break;
+        case 7: wait_vmcnt<7 * RQ>(); break;
+        case 8: wait_vmcnt<8 * RQ>(); break;
+        case 9: wait_vmcnt<9 * RQ>(); break;
+        case 10: wait_vmcnt<10 * RQ>(); break;
+        case 11: wait_vmcnt<11 * RQ>(); break;
         default: wait_vmcnt<0>(); break;
+    }
+}
+
+// A quantiser wave's share of the activation slice, rows 32 mt ..
+// 32 mt + 8 RQ - 1 (RQ of the four 8-row chunks: those holding rows below
+// M), split steps tb + s for s = qw, qw + QW, ... (KL of them): each step's
+// 32 x 64 bf16 tile goes straight into LDS (gfx950 buffer loads to LDS, RQ
+// loads of 1 KiB, 8 lanes per 128-byte row segment, 16-byte column j of row
+// r at slot j ^ ((r >> 1) & 7)).  Steps past the split and a group past K
+// (K % 64 == 32) read zeros; rows past M read zeros through the buffer
+// bound.
+template <int KL, int QW, int RQ>
+__device__ __forceinline__ void shared_issue_activation(const Rsrc& ra, uint8_t* raw, int mt, int tb, int T, int G,
+                                                        int lda, int qw, int L) {
+    constexpr uint32_t kOutOfRange = 0x80000000u;
+#pragma unroll
+    for (int k = 0; k < KL; ++k) {
+        const int s = qw + QW * k;
+#pragma unroll
+        for (int c4 = 0; c4 < RQ; ++c4) {
+            const int c = c4 * 64 + L;
+            const int r = c >> 3;
+            const int j = (c & 7) ^ ((r >> 1) & 7);
+            const bool live = s < T && 2 * (tb + s) + (j >> 2) < G;
+            const uint32_t off = (uint32_t)(mt * kRowBlock + r) * (uint32_t)lda * 2u + (uint32_t)(tb + s) * 128u +
+                                 (uint32_t)j * 16u;
+            bload16_lds(ra, raw + (size_t)s * kRawTile + c4 * 1024, live ? off : kOutOfRange);
+        }
+    }
+    asm volatile("" ::: "memory");
+}
+
+// The same wave's quantisation: step k has landed once at most the RQ loads
+// of each of its KL - 1 - k later steps are outstanding (its only
+// vector-memory operations are those loads, and they complete in issue
+// order); lane L quantises row L % 32, group L / 32 of the step in registers
+// and writes the MFMA fragment (16 bytes) and the scale byte into byte s % 4
+// of its word.  Steps past the split quantise zeros (zero codes, scale byte
+// 0), and so do the rows of chunks not loaded.
+template <int KL, int QW, int RQ>
+__device__ __forceinline__ void shared_quantise(const uint8_t* raw, uint8_t* aop, uint8_t* asc, int qw, int L) {
+    const bool row_loaded = RQ == 4 || (L & 31) < 8 * RQ;
+#pragma unroll
+    for (int k = 0; k < KL; ++k) {
+        wait_steps_left<RQ>(KL - 1 - k);
+        asm volatile("" ::: "memory");
+        const int s = qw + QW * k;
+        const uint8_t* tile = raw + (size_t)s * kRawTile;
+        u32x4 x[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) x[c] = *(const u32x4*)(tile + raw_slot(L & 31, 4 * (L >> 5) + c));
+        u32x4 codes;
+        uint32_t byte = quant_group32(x, codes);
+        if (!row_loaded) {
+            codes = u32x4{0u, 0u, 0u, 0u};
+            byte = 0u;
+        }
+        *(u32x4*)(aop + 16 * (s * 64 + L)) = codes;
+        asc[((s >> 2) * 64 + L) * 4 + (s & 3)] = (uint8_t)byte;
     }
 }
 
@@ -127,35 +188,26 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
     // The activation loads go out before the weight's: a CU returns the loads
     // of its waves roughly in the order it takes them, and the activation
     // (L2-resident) must arrive early for the quantisers, while the weight
-    // (HBM) is consumed last.
-    // Quantiser wave w (0 .. QW - 1) takes the K steps w, w + QW, ... of the
-    // split: each step's 32 x 64 bf16 tile goes straight into LDS (gfx950
-    // buffer loads to LDS, four 1 KiB loads, 8 lanes per 128-byte row
-    // segment, 16-byte column j of row r at slot j ^ ((r >> 1) & 7)).
+    // (HBM) is consumed last.  Quantiser wave qw (0 .. QW - 1) takes the K
+    // steps qw, qw + QW, ... of the split.
     constexpr int KL = KR / QW;                      // steps per quantiser wave
     static_assert(KR % QW == 0, "whole steps per quantiser wave");
     static_assert(KL <= 12, "wait_steps_left covers 12 steps per quantiser wave");
     const int qw = wave - WN;
+    // The 8-row chunks of this M tile that hold rows below M: 1, 2 or all
+    // four (three load all four; the fourth reads zeros through the buffer
+    // bound).  The code for each count is straight-line: a branch between
+    // the loads would break up their issue.
+    const int rows_here = M - mt * kRowBlock;
+    const int rq = rows_here > 16 ? 4 : rows_here > 8 ? 2 : 1;
     if (!mfma_wave) {
-        // ---- the activation slice: rows 32 mt .. 32 mt + 31, steps tb .. te - 1
         const Rsrc ra = make_rsrc(A, (uint32_t)M * (uint32_t)lda * 2u);
-#pragma unroll
-        for (int k = 0; k < KL; ++k) {
-            const int s = qw + QW * k;
-#pragma unroll
-            for (int c4 = 0; c4 < 4; ++c4) {
-                const int c = c4 * 64 + L;
-                const int r = c >> 3;
-                const int j = (c & 7) ^ ((r >> 1) & 7);
-                // steps past the split and a group past K (K % 64 == 32) read
-                // zeros; rows past M read zeros through the buffer bound
-                const bool live = s < T && 2 * (tb + s) + (j >> 2) < G;
-                const uint32_t off = (uint32_t)(mt * kRowBlock + r) * (uint32_t)lda * 2u +
-                                     (uint32_t)(tb + s) * 128u + (uint32_t)j * 16u;
-                bload16_lds(ra, raw + (size_t)s * kRawTile + c4 * 1024, live ? off : kOutOfRange);
-            }
-        }
-        asm volatile("" ::: "memory");
+        if (rq == 4)
+            shared_issue_activation<KL, QW, 4>(ra, raw, mt, tb, T, G, lda, qw, L);
+        else if (rq == 2)
+            shared_issue_activation<KL, QW, 2>(ra, raw, mt, tb, T, G, lda, qw, L);
+        else
+            shared_issue_activation<KL, QW, 1>(ra, raw, mt, tb, T, G, lda, qw, L);
     }
     __builtin_amdgcn_s_barrier();   // the activation loads are issued (no fence: see the top)
     if (mfma_wave) {
@@ -185,26 +237,12 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
         }
     }
     if (!mfma_wave) {
-        // step k of this wave has landed once at most the 4 loads of each of
-        // its KL - 1 - k later steps are outstanding (its only vector-memory
-        // operations are those loads, and they complete in issue order);
-        // lane L quantises row L % 32, group L / 32 of the step in registers
-        // and writes the MFMA fragment (16 bytes) and scale byte; steps past
-        // the split quantise zeros: zero codes, scale byte 0.
-#pragma unroll
-        for (int k = 0; k < KL; ++k) {
-            wait_steps_left(KL - 1 - k);
-            asm volatile("" ::: "memory");
-            const int s = qw + QW * k;
-            const uint8_t* tile = raw + (size_t)s * kRawTile;
-            u32x4 x[4];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) x[c] = *(const u32x4*)(tile + raw_slot(L & 31, 4 * (L >> 5) + c));
-            u32x4 codes;
-            const uint32_t byte = quant_group32(x, codes);
-            *(u32x4*)(aop + 16 * (s * 64 + L)) = codes;
-            asc[((s >> 2) * 64 + L) * 4 + (s & 3)] = (uint8_t)byte;   // byte s % 4 of the lane's word
-        }
+        if (rq == 4)
+            shared_quantise<KL, QW, 4>(raw, aop, asc, qw, L);
+        else if (rq == 2)
+            shared_quantise<KL, QW, 2>(raw, aop, asc, qw, L);
+        else
+            shared_quantise<KL, QW, 1>(raw, aop, asc, qw, L);
     }
     // The quantised slice is in LDS: each wave's LDS writes have completed
     // before the barrier.  No vector-memory wait: the MFMA waves' weight
