@@ -50,7 +50,7 @@ const TableEntry kTable[] = {
     {4, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
     {32, 4096, 512, {1, 1, 1, 4, 1, 2, 0}},
     {32, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
-    {16, 2112, 7168, {1, 2, 1, 4, 7, 2, 0}},
+    {16, 2112, 7168, {1, 1, 3, 4, 7, 5, 0}},
     {64, 7168, 2048, {1, 2, 1, 8, 1, 2, 0}},
     {256, 3072, 1536, {1, 1, 3, 8, 1, 5, 0}},
 };
@@ -124,7 +124,16 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 
 // Model for shapes without a table entry, fitted to the plan-regret sweep
 // over the pages' shape grid (19 (N, K) weight shapes x M = 1 .. 256, up to
-// 63 candidate plans each):
+// 69 candidate plans each):
+//   - deep K (more than 64 steps) with one or two 32-row blocks of M: the
+//     quantiser-wave mode with 4 quantiser waves and K split into pieces of
+//     at most 16 steps (7 splits at K = 7168), three MFMA waves when the N
+//     blocks divide by 3 and the grid stays within one workgroup per CU
+//     (such a workgroup holds about 81 KB of LDS), else four; except at
+//     N >= 7168, where one M block of at most 8 rows takes splits of 8 steps
+//     (three workgroups fit a CU), 9 .. 32 rows the register mode with 2
+//     splits, and two M blocks the pre-quantisation kernel with 2 splits;
+//     two M blocks at 2112 < N < 7168 go on below;
 //   - the activation is quantised once per workgroup by quantiser waves for
 //     three or four MFMA waves when M has at least eight 32-row blocks (or
 //     four, with K <= 512 or N >= 7168) and K is at most 24 steps;
@@ -136,14 +145,30 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 //   - otherwise each wave quantises its own fragments: two N blocks per wave
 //     from four M blocks on, from two at N >= 7168, and for deep K;
 //   - 8 waves along K (4 for K <= 512), and K split over workgroups only as
-//     far as the register budget needs, except that deep K (more than 64
-//     steps) with the register mode takes at least 4 splits for one M
-//     block and 2 for more: the N tiles alone leave most CUs idle.
+//     far as the register budget needs, except that deep K with the register
+//     mode takes at least 2 splits: the N tiles alone leave most CUs idle.
+// A deep-K plan that the layout refuses for a shape (a split count past the
+// partials' 32-bit range, say) falls through to the rules after it.
 Plan model_plan(int M, int N, int K) {
     const OperandGeom ga = mx4::operand_geom(M, K);
     const OperandGeom gb = mx4::operand_geom(N, K);
-    const int RBm = ga.RB, KS = gb.KS;
+    const int RBm = ga.RB, RBn = gb.RB, KS = gb.KS;
     const bool deep = KS > 64;
+    Layout l;
+    if (deep && (RBm == 1 || (RBm == 2 && (N <= 2112 || N >= 7168)))) {
+        Plan q{1, 1, 4, 4, 1, kAmShared, 0};
+        if (N >= 7168 && RBm == 2) {
+            q = Plan{2, 1, 1, 8, 2, kAmPrequant, 0};
+        } else if (N >= 7168 && M > 8) {
+            q = Plan{1, 2, 1, 8, 2, kAmDirect, 0};
+        } else if (N >= 7168) {
+            q.splits = (KS + 7) / 8;
+        } else {
+            q.splits = (KS + 15) / 16;
+            if (RBn % 3 == 0 && (long long)((RBn + 2) / 3) * RBm * q.splits <= 256) q.wn = 3;
+        }
+        if (plan_layout(q, M, N, K, &l) == MX_OK) return q;
+    }
     // quantiser waves for the whole workgroup: at least 8 M blocks, or 4
     // with a short K or a wide N, when the split's K fits their budget
     const bool shared = KS <= 24 && (RBm >= 8 || (RBm >= 4 && (KS <= 8 || N >= 7168)));
@@ -157,7 +182,7 @@ Plan model_plan(int M, int N, int K) {
         p.amode = kAmShared;
         p.mb = 1;
         p.nb = 1;
-        p.wn = gb.RB % 3 == 0 ? 3 : 4;
+        p.wn = RBn % 3 == 0 ? 3 : 4;
         p.wk = 8;
         return p;
     }
@@ -172,12 +197,8 @@ Plan model_plan(int M, int N, int K) {
         p.nb = (RBm >= 4 || (RBm >= 2 && N >= 7168) || deep) ? 2 : 1;
         p.wn = 1;
     }
-    Layout l;
     while (p.splits < KS && plan_layout(p, M, N, K, &l) != MX_OK) ++p.splits;
-    if (deep && !pre) {
-        const int want = RBm <= 1 ? 4 : 2;
-        if (p.splits < want && want <= KS) p.splits = want;
-    }
+    if (deep && !pre && p.splits < 2) p.splits = 2;
     return p;
 }
 

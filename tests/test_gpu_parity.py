@@ -373,7 +373,9 @@ def test_split_k_deterministic_and_consistent():
     c1 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=plan, workspace=ws))
     c2 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=plan, workspace=ws))
     np.testing.assert_array_equal(c1, c2)
-    other = dict(plan, splits=4, wk=4)
+    # another activation mode and split count: register quantisation, 4 splits
+    other = dict(mb=1, nb=2, wn=1, wk=4, splits=4, amode=2, finish=0)
+    assert other != plan
     c3 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=other))
     ref = oracle.gemm(inputs.bits(A), inputs.bits(Bm))
     assert_c_close(c1, ref, "split %d" % plan["splits"])
