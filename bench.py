@@ -656,6 +656,26 @@ def regret_summary(results, command):
     print("\n".join(lines))
 
 
+def stats_markdown(stats_csv, command):
+    """profiles/bench_kernel_stats.md: the rocprofv3 --stats summary of the
+    mx4 kernels of one bench.py run under the tracer."""
+    import csv
+    with open(stats_csv) as f:
+        rows = [r for r in csv.DictReader(f) if "mx4::" in r["Name"]]
+    lines = ["# Kernel statistics of bench.py under rocprofv3", "",
+             "`%s` (the bench command of the bench line, fewer steps), `*_kernel_stats.csv` rows of the mx4 "
+             "kernels. Under the tracer consecutive dispatches start about 9 us apart, so each traced duration is "
+             "that of a kernel starting on an idle GPU; the bench line's GPU time per call is the untraced HIP-graph "
+             "replay." % command, "",
+             "| kernel | calls | average us | min us | max us |", "|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append("| `%s` | %s | %.3f | %.3f | %.3f |" % (_short(r["Name"]), r["Calls"], float(r["AverageNs"]) / 1e3,
+                                                         float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+    with open(os.path.join(ROOT, "profiles", "bench_kernel_stats.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)

@@ -417,6 +417,30 @@ def test_bench_algorithmic_bytes_of_the_workloads():
     assert sorted(expected.values()) == sorted([810496, 1409024, 8339456, 8978432, 4866048])
 
 
+def test_bench_names_every_function_it_calls():
+    """Every plain name that bench.py calls resolves to a module-level
+    definition, an import or a builtin: the offline subcommands
+    (--summarize, --stats-md, --regret-merge) run without a GPU and are
+    otherwise exercised only when profiles are rewritten."""
+    import ast
+    import builtins
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    tree = ast.parse(open(os.path.join(root, "bench.py")).read())
+    defined = set(dir(builtins))
+    for node in ast.walk(tree):
+        if isinstance(node, (ast.FunctionDef, ast.ClassDef)):
+            defined.add(node.name)
+        elif isinstance(node, (ast.Import, ast.ImportFrom)):
+            defined.update((a.asname or a.name).split(".")[0] for a in node.names)
+        elif isinstance(node, ast.Name) and isinstance(node.ctx, ast.Store):
+            defined.add(node.id)
+        elif isinstance(node, ast.arg):
+            defined.add(node.arg)
+    called = {n.func.id for n in ast.walk(tree) if isinstance(n, ast.Call) and isinstance(n.func, ast.Name)}
+    assert called - defined == set(), sorted(called - defined)
+    assert {"stats_markdown", "regret_summary", "summarize_profiles", "plan_regret"} <= defined
+
+
 def test_split_k_partials_complete_before_arrival():
     """In every GEMM kernel, the last-arrival split-K finish counts a
     workgroup's arrival (the agent-scope atomic add on the tile counter) only
