@@ -39,28 +39,28 @@
 // dispatcher sends to one XCD (linear id mod 8) take a rectangle of a M tiles
 // x b N tiles, chosen so that the activation rows and weight columns that
 // one XCD's L2 must fetch are fewest.
-// Rows past M read zeros through the buffer bound (zero codes, scale byte
-// 0); steps past the split read zeros; a group past K (K % 64 == 32) is
-// zeroed explicitly.  The epilogue stages each MFMA wave's bf16 tile in LDS
-// and stores it in 16-byte row chunks; with K split over workgroups, fp32
-// partials go to the workspace and reduce_kernel sums them in split order.
+// Rows past M are not loaded or read zeros through the buffer bound (zero
+// codes, scale byte 0); steps past the split read zeros; a group past K
+// (K % 64 == 32) is zeroed explicitly.  After the slice barrier the
+// quantiser waves leave; each MFMA wave stages its own bf16 tile in the dead
+// raw-tile region and stores it in 16-byte row chunks, with no barrier (a
+// wave that finishes early stores early); with K split over workgroups,
+// fp32 partials go to the workspace and reduce_kernel sums them in split
+// order.
 #include "mx4_device.h"
 #include "mx4_internal.h"
 
 namespace mx4 {
 
 // LDS: the quantised activation slice, [KR][64 lanes][16 B] codes then the
-// scale bytes as [KR / 4][64 lanes] words (byte b: step 4 w + b); the staged
-// bf16 output tile aliases it after the MFMAs.
+// scale bytes as [KR / 4][64 lanes] words (byte b: step 4 w + b).
 __host__ __device__ constexpr size_t shared_aop_bytes(int kr) { return (size_t)kr * 64 * 17; }
-// then the raw bf16 tiles of the slice, one 4 KiB tile per K step
+// then the raw bf16 tiles of the slice, one 4 KiB tile per K step; after the
+// quantisation the MFMA waves stage their bf16 output tiles there
 constexpr int kRawTile = kRowBlock * 128;
 __host__ __device__ constexpr size_t shared_raw_offset(int kr) { return (shared_aop_bytes(kr) + 255) / 256 * 256; }
 __host__ __device__ constexpr size_t shared_all_bytes(int kr) { return shared_raw_offset(kr) + (size_t)kr * kRawTile; }
 __host__ __device__ constexpr int raw_slot(int r, int j) { return r * 128 + ((j ^ ((r >> 1) & 7)) << 4); }
-__host__ __device__ constexpr size_t shared_stage_bytes(int nb, int wn) {
-    return (size_t)kRowBlock * (nb * wn * kRowBlock + 8) * 2;
-}
 
 // s_waitcnt for at most RQ m outstanding vector-memory operations (RQ loads
 // per step, m later steps; m is a constant after unrolling, so the switch
@@ -248,7 +248,8 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
     // before the barrier.  No vector-memory wait: the MFMA waves' weight
     // loads stay in flight, and each MFMA waits for its own fragment.
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (mfma_wave) {
+    if (!mfma_wave) return;   // the quantisers are done; no barrier follows
+    {
         uint32_t aw = 0;
 #pragma unroll
         for (int s = 0; s < KR; ++s) {
@@ -260,51 +261,53 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
                 acc[j] = mfma_fp4_32x32x64(bfrag[s][j], af, acc[j], bscale[s / 4][j] >> sh, aw >> sh);
         }
     }
-    if (mfma_wave) {
 #pragma unroll
-        for (int j = 0; j < NB; ++j) mfma_result_fence(acc[j]);
-    }
-    __syncthreads();   // every MFMA wave is done with the slice: the stage may reuse it
+    for (int j = 0; j < NB; ++j) mfma_result_fence(acc[j]);
 
-    // ---- epilogue: lane L, element e of block j: m = 32 mt + L % 32,
-    // n = 32 (nb0 + j) + 8 (e / 4) + 4 (L / 32) + e % 4.
-    constexpr int TC = NB * WN * kRowBlock;
-    constexpr int SROW = TC + 8;
-    uint16_t* stage = (uint16_t*)lds;
+    // ---- epilogue, each MFMA wave on its own: lane L, element e of block j:
+    // m = 32 mt + L % 32, n = 32 (nb0 + j) + 8 (e / 4) + 4 (L / 32) + e % 4.
     const int m_lane = L & 31;
     const int n_lane = 4 * (L >> 5);
-    const bool part = partial_buf != nullptr;
-    const int ldp = RBn * kRowBlock;
-    if (mfma_wave) {
+    if (partial_buf != nullptr) {   // K split: fp32 partials, summed by reduce_kernel
+        const int ldp = RBn * kRowBlock;
 #pragma unroll
         for (int j = 0; j < NB; ++j)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const f32x4 v = {acc[j][4 * r], acc[j][4 * r + 1], acc[j][4 * r + 2], acc[j][4 * r + 3]};
-                if (part) {
-                    const int m = mt * kRowBlock + m_lane;
-                    const int nb = nb0 + j;
-                    if (m < M && nb < RBn)
-                        *(f32x4*)(partial_buf + ((size_t)split * M + m) * ldp + nb * kRowBlock + 8 * r + n_lane) = v;
-                } else {
-                    const int col = (wave * NB + j) * kRowBlock + 8 * r + n_lane;
-                    uint2 w;
-                    w.x = pack_bf16x2(v.x, v.y);
-                    w.y = pack_bf16x2(v.z, v.w);
-                    *(uint2*)(stage + m_lane * SROW + col) = w;
-                }
+                const int m = mt * kRowBlock + m_lane;
+                const int nb = nb0 + j;
+                if (m < M && nb < RBn)
+                    *(f32x4*)(partial_buf + ((size_t)split * M + m) * ldp + nb * kRowBlock + 8 * r + n_lane) = v;
             }
+        return;
     }
-    if (part) return;   // reduce_kernel sums the partials
-    __syncthreads();
+    // The wave's bf16 tile (32 rows x 32 NB columns) goes through its own
+    // stage in the raw-tile region, dead since the slice barrier, and leaves
+    // in 16-byte row chunks: no barrier, so each wave stores as soon as its
+    // MFMAs are done (a wave reads its own LDS writes in order).
+    constexpr int WC = NB * kRowBlock;
+    constexpr int WROW = WC + 8;   // bf16 per staged row (16-byte pad)
+    static_assert((size_t)WN * kRowBlock * WROW * 2 <= (size_t)KR * kRawTile, "stages fit the raw-tile region");
+    uint16_t* wst = (uint16_t*)(raw + (size_t)wave * kRowBlock * WROW * 2);
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            uint2 w;
+            w.x = pack_bf16x2(acc[j][4 * r], acc[j][4 * r + 1]);
+            w.y = pack_bf16x2(acc[j][4 * r + 2], acc[j][4 * r + 3]);
+            *(uint2*)(wst + m_lane * WROW + j * kRowBlock + 8 * r + n_lane) = w;
+        }
     const int m_base = mt * kRowBlock;
-    const int n_base = nt * WN * NB * kRowBlock;
+    const int n_base = nb0 * kRowBlock;
     const bool vec16 = ((uintptr_t)C % 16 == 0) && (ldc % 8 == 0);
-    for (int c = tid; c < kRowBlock * TC / 8; c += 64 * (WN + QW)) {
-        const int row = c / (TC / 8), c8 = c % (TC / 8);
+#pragma unroll
+    for (int c = L; c < kRowBlock * WC / 8; c += 64) {
+        const int row = c / (WC / 8), c8 = c % (WC / 8);
         const int m = m_base + row, n = n_base + 8 * c8;
         if (m >= M || n >= N) continue;
-        const u32x4 v = *(const u32x4*)(stage + row * SROW + 8 * c8);
+        const u32x4 v = *(const u32x4*)(wst + row * WROW + 8 * c8);
         uint16_t* dst = C + (size_t)m * ldc + n;
         if (vec16 && n + 7 < N) {
             __builtin_nontemporal_store(v, (u32x4*)dst);
@@ -356,9 +359,8 @@ GemmKernelFn find_shared_kernel(const Plan& plan, int steps_per_split) {
 }
 
 size_t shared_lds_bytes(const Plan& plan, int steps_per_split) {
-    const size_t a = shared_all_bytes(shared_kr_for(steps_per_split));
-    const size_t st = shared_stage_bytes(plan.nb, plan.wn);
-    return a > st ? a : st;
+    (void)plan;
+    return shared_all_bytes(shared_kr_for(steps_per_split));
 }
 
 }  // namespace mx4
