@@ -125,18 +125,19 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 // Model for shapes without a table entry, fitted to the plan-regret sweep
 // over the pages' shape grid (19 (N, K) weight shapes x M = 1 .. 256, up to
 // 69 candidate plans each):
-//   - deep K (more than 64 steps) with one or two 32-row blocks of M: the
-//     quantiser-wave mode with 4 quantiser waves and K split into pieces of
-//     at most 16 steps (7 splits at K = 7168), three MFMA waves when the N
-//     blocks divide by 3 and the grid stays within one workgroup per CU
-//     (such a workgroup holds about 81 KB of LDS), else four; except at
-//     N >= 7168, where one M block of at most 8 rows takes splits of 8 steps
-//     (three workgroups fit a CU), 9 .. 32 rows the register mode with 2
-//     splits, and two M blocks the pre-quantisation kernel with 2 splits;
-//     two M blocks at 2112 < N < 7168 go on below;
+//   - deep K (more than 64 steps) with one 32-row block of M, or up to four
+//     at N <= 2112: the quantiser-wave mode with 4 quantiser waves and K
+//     split into pieces of at most 16 steps (7 splits at K = 7168), three
+//     MFMA waves when the N blocks divide by 3 and the grid stays within one
+//     workgroup per CU (such a workgroup holds about 81 KB of LDS), else
+//     four; except at N >= 7168, where one M block of at most 8 rows takes
+//     splits of 8 steps (three workgroups fit a CU), 9 .. 32 rows the
+//     register mode with 2 splits, and two M blocks the pre-quantisation
+//     kernel with 2 splits; the rest of deep K goes on below;
 //   - the activation is quantised once per workgroup by quantiser waves for
 //     three or four MFMA waves when M has at least eight 32-row blocks (or
-//     four, with K <= 512 or N >= 7168) and K is at most 24 steps;
+//     four, with K <= 512 or N >= 7168; or two, with both) and K is at most
+//     24 steps;
 //   - else it is quantised in a first kernel when M has four or more 32-row
 //     blocks and K more than 8 steps, unless M is exactly four blocks with
 //     N < 7168 and K <= 2048: every wave of every N tile would otherwise
@@ -155,7 +156,7 @@ Plan model_plan(int M, int N, int K) {
     const int RBm = ga.RB, RBn = gb.RB, KS = gb.KS;
     const bool deep = KS > 64;
     Layout l;
-    if (deep && (RBm == 1 || (RBm == 2 && (N <= 2112 || N >= 7168)))) {
+    if (deep && (RBm == 1 || (RBm == 2 && N >= 7168) || (RBm <= 4 && N <= 2112))) {
         Plan q{1, 1, 4, 4, 1, kAmShared, 0};
         if (N >= 7168 && RBm == 2) {
             q = Plan{2, 1, 1, 8, 2, kAmPrequant, 0};
@@ -170,8 +171,10 @@ Plan model_plan(int M, int N, int K) {
         if (plan_layout(q, M, N, K, &l) == MX_OK) return q;
     }
     // quantiser waves for the whole workgroup: at least 8 M blocks, or 4
-    // with a short K or a wide N, when the split's K fits their budget
-    const bool shared = KS <= 24 && (RBm >= 8 || (RBm >= 4 && (KS <= 8 || N >= 7168)));
+    // with a short K or a wide N, or 2 with both, when the split's K fits
+    // their budget
+    const bool shared =
+        KS <= 24 && (RBm >= 8 || (RBm >= 4 && (KS <= 8 || N >= 7168)) || (RBm >= 2 && KS <= 8 && N >= 7168));
     const bool pre = !shared && RBm >= 4 && KS > 8 && (RBm > 4 || N >= 7168 || KS > 32);
     Plan p;
     p.finish = 0;
