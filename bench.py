@@ -117,7 +117,7 @@ class Setup:
 
     def launches(self):
         p = self.plan
-        return 1 + (p["amode"] == 1) + (1 if p["splits"] > 1 and not p["finish"] else 0)
+        return 1 + (p["amode"] in (1, 6)) + (1 if p["splits"] > 1 and not p["finish"] else 0)
 
 
 def eager_loop(torch, st, steps, warmup, a16w4=False):

@@ -136,7 +136,7 @@ int mx_gemm_workspace_bytes(int M, int N, int K, size_t* bytes_host);
  *              that overlap in time (other streams) need separate
  *              workspaces.
  * Launches per call: 1 (A quantised inside the GEMM), +1 for the quantisation
- * kernel when the plan's amode is MX_AMODE_PREQUANT, +1 for the split-K
+ * kernel when the plan's amode is MX_AMODE_PREQUANT or MX_AMODE_TILE, +1 for the split-K
  * reduction when splits > 1 and the plan's finish is MX_FINISH_KERNEL.
  * Either split-K finish sums the partials in split order: results do not
  * depend on timing. */
@@ -150,12 +150,15 @@ int mx_gemm(const void* A_dev, int M, int K, int lda,
  * A workgroup of wn x wk waves owns 32*mb rows of C and 32*nb*wn columns,
  * over K / splits of the reduction; its wk waves share that K range. */
 typedef struct mx_plan {
-    int mb;          /* 32-row blocks of M per wave (1 or 2) */
+    int mb;          /* 32-row blocks of M per wave (1 or 2); in
+                        MX_AMODE_TILE per workgroup */
     int nb;          /* 32-column blocks of N per wave (1 or 2; 1, 2 or 4 in
-                        MX_AMODE_STREAM) */
-    int wn;          /* waves along N per workgroup (1 or 2) */
+                        MX_AMODE_STREAM); in MX_AMODE_TILE per workgroup */
+    int wn;          /* waves along N per workgroup (1 or 2; up to 4 in
+                        MX_AMODE_SHARED and MX_AMODE_TILE) */
     int wk;          /* waves along K per workgroup (1, 2, 4, 8 or 16; wn*wk <= 16);
-                        in MX_AMODE_SHARED the quantiser waves */
+                        in MX_AMODE_SHARED the quantiser waves, in
+                        MX_AMODE_TILE the waves along M */
     int splits;      /* workgroups along K; > 1 adds a reduction kernel
                         unless finish is MX_FINISH_LAST_ARRIVAL */
     int amode;       /* where A is quantised: one of MX_AMODE_* */
@@ -177,7 +180,7 @@ enum {
                                K steps with the loads of several steps in
                                flight (any K per wave; mb = wn = 1,
                                nb in {1, 2, 4}) */
-    MX_AMODE_SHARED = 5     /* wk quantiser waves per workgroup quantise its
+    MX_AMODE_SHARED = 5,    /* wk quantiser waves per workgroup quantise its
                                32-row activation slice once into LDS for wn
                                MFMA waves of nb N blocks each, which hold the
                                weight of the whole K split in registers and
@@ -186,6 +189,13 @@ enum {
                                (1,4,4), (1,4,8), (2,2,2), (2,4,4)}; at most
                                24 K steps per split, 16 with nb = 2;
                                finish 0) */
+    MX_AMODE_TILE = 6       /* a first kernel quantises A into the workspace;
+                               the GEMM workgroup owns 32*mb x 32*nb of C over
+                               the whole of K and loops over K with both
+                               operands staged in LDS, wk waves along M and
+                               wn along N (the large-M, MFMA-bound regime;
+                               (mb, nb, wk, wn) in {(8,8,2,4), (4,8,2,2),
+                               (8,4,2,2)}; splits 1) */
 };
 
 /* Split-K finishes of a plan (no effect when splits == 1). */

@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # (source, extra flags, object name): the GEMM is compiled once per K-step budget
 SOURCES = [("mx4_api.cpp", [], "mx4_api"), ("mx4_quant.hip", [], "mx4_quant"),
            ("mx4_noalloc.hip", [], "mx4_noalloc"), ("mx4_stream.hip", [], "mx4_stream"),
-           ("mx4_shared.hip", [], "mx4_shared")] + [
+           ("mx4_shared.hip", [], "mx4_shared"), ("mx4_tile.hip", [], "mx4_tile")] + [
     ("mx4_gemm.hip", ["-DMX4_KR=%d" % kr], "mx4_gemm_kr%d" % kr) for kr in (1, 2, 3, 4, 8)]
 ARCH = "gfx950"
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,

@@ -20,8 +20,10 @@ using mx4::kAmLds;
 using mx4::kAmPrequant;
 using mx4::kAmShared;
 using mx4::kAmStream;
+using mx4::kAmTile;
 static_assert(kAmLds == MX_AMODE_LDS && kAmPrequant == MX_AMODE_PREQUANT && kAmDirect == MX_AMODE_DIRECT &&
-                  kAmBf16 == MX_AMODE_BF16 && kAmStream == MX_AMODE_STREAM && kAmShared == MX_AMODE_SHARED,
+                  kAmBf16 == MX_AMODE_BF16 && kAmStream == MX_AMODE_STREAM && kAmShared == MX_AMODE_SHARED &&
+                  kAmTile == MX_AMODE_TILE,
               "activation modes of the C ABI and the kernels differ");
 
 namespace {
@@ -86,7 +88,7 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     // each hold a whole split (its kernels' own budgets, checked when the
     // kernel is resolved); the other modes hold all of a wave's steps in
     // registers at once.
-    const bool stream = plan.amode == kAmStream || plan.amode == kAmShared;
+    const bool stream = plan.amode == kAmStream || plan.amode == kAmShared || plan.amode == kAmTile;
     if (plan.amode == kAmShared) {
         if (!mx4::find_shared_kernel(plan, l.steps_per_split)) return MX_EPLAN;
         if (plan.finish != 0 && l.splits > 1) return MX_EPLAN;   // partials go to reduce_kernel
@@ -106,12 +108,14 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     }
     if (mx4::gemm_lds_bytes(plan, l.steps_per_split) > mx4::kLdsBudget) return MX_EPLAN;
     l.mtiles = (ga.RB + plan.mb - 1) / plan.mb;
-    l.ntiles = (gb.RB + plan.nb * plan.wn - 1) / (plan.nb * plan.wn);
+    // the tile mode's nb counts the workgroup's N blocks, the others' a wave's
+    const int nblk = plan.amode == kAmTile ? plan.nb : plan.nb * plan.wn;
+    l.ntiles = (gb.RB + nblk - 1) / nblk;
     // grid (N tiles, M tiles, splits): y and z are 16-bit
     if (l.mtiles > 65535 || l.splits > 65535 || l.ntiles > (1 << 30)) return MX_EINVAL;
     if (plan.finish != 0 && plan.finish != 1) return MX_EPLAN;
     if (plan.finish == 1 && l.splits > 1 && (long long)l.mtiles * l.ntiles > mx4::kMaxCounters) return MX_EPLAN;
-    l.aop_bytes = plan.amode == kAmPrequant ? round_up(ga.total_bytes, 256) : 0;
+    l.aop_bytes = mx4::amode_prequantises(plan.amode) ? round_up(ga.total_bytes, 256) : 0;
     l.partial_bytes = l.splits > 1 ? round_up((size_t)l.splits * M * gb.RB * mx4::kRowBlock * sizeof(float), 256) : 0;
     if (l.partial_bytes >= (1ull << 31)) return MX_EPLAN;   // 32-bit buffer offsets
     l.counter_bytes = (l.aop_bytes + l.partial_bytes) > 0 ? mx4::kCounterBytes : 0;
@@ -148,14 +152,26 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 //   - 8 waves along K (4 for K <= 512), and K split over workgroups only as
 //     far as the register budget needs, except that deep K with the register
 //     mode takes at least 2 splits: the N tiles alone leave most CUs idle.
-// A deep-K plan that the layout refuses for a shape (a split count past the
-// partials' 32-bit range, say) falls through to the rules after it.
+//   - large MFMA work (M >= 384 and 2MNK >= 32 GFLOP; M >= 512, N >= 4096
+//     and 16 GFLOP; or M >= 1024, K >= 1024 and 12 GFLOP, from a sweep of
+//     M = 256 .. 2048 over seven weight shapes): the tile mode, a 256 x 256
+//     workgroup tile when that grid has at least 200 workgroups, else
+//     256 x 128 (more workgroups; with few, each waits on memory latency).
+// A deep-K or tile plan that the layout refuses for a shape (a split count
+// past the partials' 32-bit range, say) falls through to the rules after it.
 Plan model_plan(int M, int N, int K) {
     const OperandGeom ga = mx4::operand_geom(M, K);
     const OperandGeom gb = mx4::operand_geom(N, K);
     const int RBm = ga.RB, RBn = gb.RB, KS = gb.KS;
     const bool deep = KS > 64;
     Layout l;
+    const double flops = 2.0 * M * N * K;
+    if ((M >= 384 && flops >= 32e9) || (M >= 512 && N >= 4096 && flops >= 16e9) ||
+        (M >= 1024 && K >= 1024 && flops >= 12e9)) {
+        const long long wgs88 = (long long)((RBm + 7) / 8) * ((RBn + 7) / 8);
+        const Plan q = wgs88 >= 200 ? Plan{8, 8, 4, 2, 1, kAmTile, 0} : Plan{8, 4, 2, 2, 1, kAmTile, 0};
+        if (plan_layout(q, M, N, K, &l) == MX_OK) return q;
+    }
     if (deep && (RBm == 1 || (RBm == 2 && N >= 7168) || (RBm <= 4 && N <= 2112))) {
         Plan q{1, 1, 4, 4, 1, kAmShared, 0};
         if (N >= 7168 && RBm == 2) {
@@ -228,7 +244,7 @@ Plan choose_plan_a16w4(int M, int N, int K) {
     for (const TableEntry& e : kTableA16w4)
         if (e.M == M && e.N == N && e.K == K) return e.plan;
     Plan p = choose_plan(M, N, K);
-    if (p.amode == kAmShared || p.amode == kAmStream) {
+    if (p.amode == kAmShared || p.amode == kAmStream || p.amode == kAmTile) {
         // tilings of modes the bf16 kernels do not have: one wave along N,
         // waves along K as the register mode takes them
         const OperandGeom gk = mx4::operand_geom(N, K);
@@ -346,7 +362,7 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     hipStream_t s = (hipStream_t)stream;
     GemmParams p = e->p;
     p.A = (const uint16_t*)A;
-    p.aop = plan.amode == kAmPrequant ? wsb + lay.aop_offset : nullptr;
+    p.aop = mx4::amode_prequantises(plan.amode) ? wsb + lay.aop_offset : nullptr;
     p.bp = (const uint8_t*)packed;
     p.C = (uint16_t*)C;
     p.c_vec = (ldc % 4 == 0 && aligned(C, 8)) ? 1 : 0;
@@ -354,7 +370,7 @@ int gemm_impl(const void* A, int M, int K, int lda, const void* packed, int N, v
     p.counters = e->finish_in_gemm ? (uint32_t*)wsb : nullptr;
 
     int rc;
-    if (plan.amode == kAmPrequant) {
+    if (mx4::amode_prequantises(plan.amode)) {
         rc = hip_status(mx4::launch_pack((const uint16_t*)A, M, K, lda, wsb + lay.aop_offset, s));
         if (rc) return rc;
     }

@@ -786,6 +786,7 @@ static int row_chunks(const Plan& plan, const GemmParams& p) {
 size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
     if (plan.amode == kAmStream) return stream_lds_bytes(plan);
     if (plan.amode == kAmShared) return shared_lds_bytes(plan, steps_per_split);
+    if (plan.amode == kAmTile) return tile_lds_bytes(plan);
     const size_t a_op = plan.amode == kAmLds ? (size_t)plan.mb * steps_per_split * 64 * 17 : 0;
     size_t out = gemm_red_bytes(plan.wn, plan.wk, plan.mb, plan.nb) + gemm_stage_bytes(plan.wn, plan.mb, plan.nb);
     if (plan.amode == kAmDirect || plan.amode == kAmBf16) {   // tiles or slabs alias the epilogue's buffers
@@ -801,6 +802,7 @@ size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
 bool gemm_plan_supported(const Plan& plan) {
     if (plan.amode == kAmStream) return plan.splits >= 1 && find_stream_kernel(plan, 4) != nullptr;
     if (plan.amode == kAmShared) return plan.splits >= 1 && find_shared_kernel(plan, 8) != nullptr;
+    if (plan.amode == kAmTile) return plan.splits == 1 && find_tile_kernel(plan) != nullptr;
     return plan.splits >= 1 && find_kernel(plan, 1) != nullptr;
 }
 
@@ -808,18 +810,24 @@ bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
     const int per_wave = (p.steps_per_split + plan.wk - 1) / plan.wk;
     GemmFn fn = plan.amode == kAmStream   ? find_stream_kernel(plan, row_chunks(plan, p))
               : plan.amode == kAmShared ? find_shared_kernel(plan, p.steps_per_split)
+              : plan.amode == kAmTile   ? find_tile_kernel(plan)
                                         : find_kernel(plan, gemm_kr_for(per_wave), row_chunks(plan, p));
     if (!fn) return false;
     // the shared mode's workgroup is wn MFMA waves plus wk quantiser waves
     const int waves = plan.amode == kAmShared ? plan.wn + plan.wk : plan.wn * plan.wk;
     // the shared kernels take their tile placement in bits 8 and up of the
-    // steps-per-split argument (at most 24 steps)
+    // steps-per-split argument (at most 24 steps); the tile kernels, which
+    // walk all of K, take the placement code alone
+    const double kbytes = p.K / 2.0 + p.K / 32.0;   // packed bytes of one row over K
     const int steps_arg =
         plan.amode == kAmShared
-            ? p.steps_per_split | (shared_xcd_map(p.mtiles, p.ntiles, p.splits, p.K, 32 * plan.nb * plan.wn) << 8)
+            ? p.steps_per_split |
+                  (shared_xcd_map(p.mtiles, p.ntiles, p.splits, 64.0 * p.K, 32.0 * plan.nb * plan.wn * kbytes) << 8)
+        : plan.amode == kAmTile
+            ? shared_xcd_map(p.mtiles, p.ntiles, 1, 32.0 * plan.mb * kbytes, 32.0 * plan.nb * kbytes)
             : p.steps_per_split;
     *out = GemmLaunch{fn, (unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits, (unsigned)(64 * waves),
-                      gemm_lds_bytes(plan, p.steps_per_split), plan.amode == kAmPrequant, steps_arg};
+                      gemm_lds_bytes(plan, p.steps_per_split), amode_prequantises(plan.amode), steps_arg};
     return true;
 }
 

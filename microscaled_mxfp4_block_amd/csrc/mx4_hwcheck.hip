@@ -146,7 +146,7 @@ int mxhw_xcd_map(int mtiles, int ntiles, int splits, int K, int cols, int* map_o
     if (mtiles < 1 || ntiles < 1 || (long long)mtiles * ntiles > (1 << 20) || splits < 1 || K < 1 || cols < 1 ||
         !map_out || !mt_out || !nt_out)
         return -1;
-    const int map = mx4::shared_xcd_map(mtiles, ntiles, splits, K, cols);
+    const int map = mx4::shared_xcd_map(mtiles, ntiles, splits, 64.0 * K, cols * (K / 2.0 + K / 32.0));
     *map_out = map;
     for (int by = 0; by < mtiles; ++by)
         for (int bx = 0; bx < ntiles; ++bx) {

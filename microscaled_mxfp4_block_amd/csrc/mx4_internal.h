@@ -87,6 +87,9 @@ constexpr int kAmDirect = 2;     // by each wave, in registers
 constexpr int kAmBf16 = 3;       // not at all: bf16 A x dequantised B (the a16wfp4 product)
 constexpr int kAmStream = 4;     // by each wave, in registers, in a K loop (gemm_stream_kernel)
 constexpr int kAmShared = 5;     // by quantiser waves into LDS, for MFMA waves (gemm_shared_kernel)
+constexpr int kAmTile = 6;       // by pack_kernel, into the workspace; K-looped LDS-tiled GEMM (gemm_tile_kernel)
+// the modes whose GEMM reads A pre-quantised by pack_kernel
+constexpr bool amode_prequantises(int amode) { return amode == kAmPrequant || amode == kAmTile; }
 
 bool gemm_plan_supported(const Plan& p);
 int gemm_kr_for(int steps_per_wave);   // K-step budget KR of the kernel for that many steps (0: none)
@@ -125,26 +128,32 @@ size_t stream_lds_bytes(const Plan& plan);
 // K steps per split (16 with nb = 2); no last-arrival finish.
 GemmKernelFn find_shared_kernel(const Plan& plan, int steps_per_split);
 size_t shared_lds_bytes(const Plan& plan, int steps_per_split);
+// The K-looped tiled kernels of the tile mode (mx4_tile.hip): a workgroup
+// tile of plan.mb x plan.nb blocks over the whole of K, plan.wk waves along
+// M and plan.wn along N, (mb, nb, wk, wn) in {(8, 8, 2, 4), (4, 8, 2, 2),
+// (8, 4, 2, 2)}; splits 1.
+GemmKernelFn find_tile_kernel(const Plan& plan);
+size_t tile_lds_bytes(const Plan& plan);
 
 // Placement of the shared kernel's tiles on the 8 XCDs.  The dispatcher
 // hands the workgroups of a grid, in x-major order, to XCD (linear id mod 8),
 // and each XCD's L2 fetches every activation row block and weight column
 // block its workgroups touch.  A one-split grid of mtiles x ntiles
-// workgroups (`cols` weight columns each) is laid out so that the workgroups
-// of one XCD take a rectangle of a M tiles x b N tiles (a b = tiles / 8),
-// the rectangle that costs the fewest fetched bytes: a * 64 K of bf16
-// activation plus b * cols (K / 2 + K / 32) of packed weight.  a and
-// mtiles / a are powers of two (the kernel decodes with shifts).
+// workgroups is laid out so that the workgroups of one XCD take a rectangle
+// of a M tiles x b N tiles (a b = tiles / 8), the rectangle that costs the
+// fewest fetched bytes: a * a_tile_bytes of activation plus b * b_tile_bytes
+// of weight (the shared mode: 32 bf16 rows, 64 K bytes, and `cols` packed
+// weight columns, cols (K / 2 + K / 32) bytes; the tile mode: packed
+// operands on both sides).  a and mtiles / a are powers of two (the kernel
+// decodes with shifts).
 // shared_xcd_map returns the placement code: 0 when no rectangle fits (the
 // dispatcher's order), else 1 + la + 16 lmg with a = 2^la M tiles per XCD
 // and 2^lmg groups of M tiles.  It reaches the kernel in bits 8 and up of
 // its steps-per-split argument (a shared-mode split has at most 24 steps),
 // which is among the preloaded arguments: the first loads' addresses wait
 // on no argument-segment read.
-inline int shared_xcd_map(int mtiles, int ntiles, int splits, int K, int cols) {
+inline int shared_xcd_map(int mtiles, int ntiles, int splits, double a_bytes, double b_bytes) {
     if (splits != 1 || mtiles < 1 || ntiles < 1 || ((long long)mtiles * ntiles) % 8 != 0) return 0;
-    const double a_bytes = 64.0 * K;
-    const double b_bytes = cols * (K / 2.0 + K / 32.0);
     int best = 0;
     double best_cost = 0.0;
     for (int lmg = 0; lmg <= 3; ++lmg) {

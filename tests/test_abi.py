@@ -185,7 +185,10 @@ def test_explicit_plan_rejections():
            dict(mb=1, nb=1, wn=1, wk=4, splits=0, amode=1),
            dict(mb=1, nb=1, wn=1, wk=4, splits=1000, amode=1),   # more splits than K steps
            dict(mb=1, nb=1, wn=1, wk=8, splits=1, amode=1),      # 14 K steps per wave > register budget
-           dict(mb=2, nb=1, wn=1, wk=16, splits=1, amode=0)]     # activation slice over the 160 KiB LDS
+           dict(mb=2, nb=1, wn=1, wk=16, splits=1, amode=0),     # activation slice over the 160 KiB LDS
+           dict(mb=8, nb=8, wn=4, wk=2, splits=2, amode=6),      # tile mode: one split
+           dict(mb=8, nb=8, wn=2, wk=4, splits=1, amode=6),      # tile mode: no such wave split
+           dict(mb=2, nb=1, wn=1, wk=8, splits=1, amode=6)]      # tile mode: no such tile
     for p in bad:
         with pytest.raises(B.MxError) as e:
             B.mx_gemm_workspace_bytes(16, 2112, 7168, p)
@@ -557,10 +560,12 @@ def test_noalloc_validates_before_any_hip_call():
 
 
 @pytest.mark.parametrize("src,kname,count", [("mx4_stream.s", "gemm_stream_kernel", 42),
-                                              ("mx4_shared.s", "gemm_shared_kernel", 19)])
+                                              ("mx4_shared.s", "gemm_shared_kernel", 19),
+                                              ("mx4_tile.s", "gemm_tile_kernel", 3)])
 def test_mode_kernels_preload_arguments_and_never_spill(src, kname, count):
-    """The K-looped stream-mode kernels and the quantiser-wave shared-mode
-    kernels take the GEMM kernels' 72-byte scalar argument segment with its
+    """The K-looped stream-mode kernels, the quantiser-wave shared-mode
+    kernels and the LDS-tiled tile-mode kernels take the GEMM kernels'
+    72-byte scalar argument segment with its
     14 leading SGPRs preloaded, and none spills VGPRs or uses scratch
     memory."""
     path = os.path.join(ROOT, "_build", src)

@@ -271,7 +271,34 @@ PLANS = [
     dict(mb=1, nb=1, wn=4, wk=4, splits=1, amode=5),
     dict(mb=1, nb=2, wn=2, wk=2, splits=3, amode=5),
     dict(mb=1, nb=2, wn=4, wk=4, splits=2, amode=5),
+    dict(mb=8, nb=8, wn=4, wk=2, splits=1, amode=6),
+    dict(mb=4, nb=8, wn=2, wk=2, splits=1, amode=6),
+    dict(mb=8, nb=4, wn=2, wk=2, splits=1, amode=6),
 ]
+
+LARGE_M_SHAPES = [(1024, 4096, 4096), (2048, 7168, 2048), (384, 7168, 7168), (777, 4100, 4160)]
+
+
+@pytest.mark.parametrize("shape", LARGE_M_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_large_m_takes_the_tile_mode(shape):
+    """Large-M shapes run the K-looped tile mode by the library's own plan;
+    sampled rows (the first, the last and 14 random ones) by sampled columns
+    (the first 4, the last 4 and 60 random ones) of C against the oracle's
+    product of exactly those rows of A and columns of B."""
+    M, N, K = shape
+    plan = B.mx_gemm_plan(M, N, K)
+    assert plan["amode"] == B.MX_AMODE_TILE, plan
+    say("large M", shape, plan_id(plan))
+    gen = torch.Generator("cpu").manual_seed(M + N + K)
+    A = inputs.bf16_randn(M, K, gen)
+    Bm = inputs.bf16_randn(N, K, gen)
+    C = gpu_bits(B.mx_gemm(to_dev(A), B.mx_pack_weight(to_dev(Bm)), N))
+    rng = np.random.default_rng(M + N)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 14)]))
+    cols = np.unique(np.concatenate([np.arange(4), np.arange(N - 4, N), rng.integers(0, N, 60)]))
+    ref = oracle.gemm(np.ascontiguousarray(inputs.bits(A)[rows]), np.ascontiguousarray(inputs.bits(Bm)[cols]))
+    assert_c_close(C[np.ix_(rows, cols)], ref, "%s %s" % (shape, plan_id(plan)))
+
 
 # The a16wfp4 product (amode 3) against its own oracle.
 PLANS_A16W4 = [

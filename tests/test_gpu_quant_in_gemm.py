@@ -138,7 +138,7 @@ def test_workload_plan_quantises_a_bit_exactly(w, kind):
 # quantisation with 1, 2 and 4 loaded row chunks, LDS-DMA tiles and the
 # padded slab, the workgroup LDS quantiser, the pre-quantisation kernel,
 # K splits with either finish, 16-wave workgroups, the K-looped stream mode,
-# the quantiser-wave shared mode.
+# the quantiser-wave shared mode, the LDS-tiled tile mode.
 PLANS = [
     dict(mb=1, nb=1, wn=1, wk=1, splits=1, amode=2),
     dict(mb=1, nb=1, wn=1, wk=4, splits=1, amode=2),
@@ -158,6 +158,8 @@ PLANS = [
     dict(mb=1, nb=2, wn=1, wk=8, splits=2, amode=4, finish=1),
     dict(mb=1, nb=1, wn=4, wk=4, splits=1, amode=5),
     dict(mb=1, nb=2, wn=2, wk=2, splits=3, amode=5),
+    dict(mb=8, nb=8, wn=4, wk=2, splits=1, amode=6),
+    dict(mb=8, nb=4, wn=2, wk=2, splits=1, amode=6),
 ]
 
 SHAPES = [(5, 352), (13, 1088), (40, 2048), (70, 1536)]   # (M, K); N = K
