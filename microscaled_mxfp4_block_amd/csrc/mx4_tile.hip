@@ -28,6 +28,8 @@
 // The epilogue stages each wave's bf16 tiles in the (then dead) ring and
 // stores them in 16-byte row chunks.
 #include "mx4_device.h"
+#include <type_traits>
+
 #include "mx4_internal.h"
 
 namespace mx4 {
@@ -35,14 +37,52 @@ namespace mx4 {
 constexpr int kTileOpBytes = 1024;   // one packed operand tile: 64 lanes x 16 B
 constexpr int kTileWordBytes = 256;  // one packed scale word group: 64 lanes x 4 B
 
-__host__ __device__ constexpr size_t tile_stage_bytes(int mb, int nb) {
-    return (size_t)(mb + nb) * (kTileOpBytes + kTileWordBytes);
+// Scale word groups (4 steps each) the ring holds with S tile stages.  The
+// words of group h + W are issued with the tiles of step 4 (h + W), at step
+// 4 (h + W) - S, after that step's barrier; group h's words were last read
+// from LDS at step 4 h - 1, so W slots suffice once 4 W >= S.
+__host__ __device__ constexpr int tile_word_slots(int s) { return (s + 3) / 4; }
+
+// LDS of a kernel with S tile stages: S stages of the step's MB + NB operand
+// tiles, then tile_word_slots(S) groups of their scale words.
+__host__ __device__ constexpr size_t tile_lds_bytes_for(int mb, int nb, int s) {
+    return (size_t)(mb + nb) * (s * kTileOpBytes + tile_word_slots(s) * kTileWordBytes);
 }
 
 // 4-byte buffer load straight into LDS: lane L's dword lands at lds_base + 4 L.
 __device__ __forceinline__ void bload4_lds(Rsrc r, uint8_t* lds_base, uint32_t voff) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 4, (int)voff, 0, 0,
                                              0);
+}
+
+// One block-scaled fp4 MFMA whose scales are byte SEL of each scale register
+// (the instruction's op_sel), so the K step's byte needs no shift.
+template <int SEL>
+__device__ __forceinline__ f32x16 mfma_fp4_sel(const u32x4& a, const u32x4& b, f32x16 acc, uint32_t scale_a,
+                                               uint32_t scale_b) {
+    i32x8 va = {(int)a.x, (int)a.y, (int)a.z, (int)a.w, 0, 0, 0, 0};
+    i32x8 vb = {(int)b.x, (int)b.y, (int)b.z, (int)b.w, 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, 4, 4, SEL, (int)scale_a, SEL, (int)scale_b);
+}
+
+// Loads of a wave issued after the tiles of step t + 1 while step t is in
+// flight: the tiles of steps t + 2 .. t + S - 1 and the word groups whose
+// first step is among them (LPW of each).
+__host__ __device__ constexpr int tile_wait_count(int lpw, int s, int u) {
+    int groups = 0;
+    for (int x = u + 2; x <= u + s - 1; ++x) groups += (x % 4 == 0);
+    return lpw * (s - 2) + lpw * groups;
+}
+
+// Scheduling order of one K step after its barrier: the buffer loads, then
+// N LDS reads each followed by one MFMA (the rest of the MFMAs follow).
+template <int N>
+__device__ __forceinline__ void order_reads_between_mfmas() {
+    if constexpr (N > 0) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        order_reads_between_mfmas<N - 1>();
+    }
 }
 
 template <int MB, int NB, int WM, int WN, int S>
@@ -57,14 +97,17 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
     constexpr int TM = MB / WM, TN = NB / WN, NW = WM * WN;
     constexpr int OPS = MB + NB;   // operand blocks per step
     static_assert(MB % WM == 0 && NB % WN == 0 && OPS % NW == 0, "whole blocks per wave");
-    constexpr int LPW = OPS / NW;  // blocks each wave loads per step (a tile and a word each)
-    constexpr int STAGE = (int)tile_stage_bytes(MB, NB);
+    constexpr int LPW = OPS / NW;  // blocks each wave loads per step
+    constexpr int WS = tile_word_slots(S);
+    constexpr int TSTAGE = OPS * kTileOpBytes;
+    constexpr int WGROUP = OPS * kTileWordBytes;
     constexpr uint32_t kOutOfRange = 0x80000000u;
-    static_assert(2 * LPW * (S - 1) < 64, "vmcnt range");
+    static_assert(tile_wait_count(LPW, S, 1) < 64 && LPW * (S - 1) + LPW * ((S - 1) / 4) < 64, "vmcnt range");
 
     const OperandGeom ga = operand_geom(M, K), gb = operand_geom(N, K);
     const int KS = gb.KS, KW = gb.KW;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    uint8_t* words = lds + (size_t)S * TSTAGE;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int L = tid & 63;
@@ -74,27 +117,48 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
     int mt, nt;
     shared_tile_of((int)blockIdx.x, (int)blockIdx.y, (gb.RB + NB - 1) / NB, steps_arg, mt, nt);
     const int rbm0 = mt * MB, rbn0 = nt * NB;
-    const Rsrc ra = make_rsrc(a_src, (uint32_t)ga.total_bytes);
-    const Rsrc rbr = make_rsrc(bp, (uint32_t)gb.total_bytes);
-
-    // The loads of step t into the stage at `st`: wave w takes blocks
-    // q = w LPW .. w LPW + LPW - 1 of the step, q < MB being A block rbm0 + q
-    // and the rest B block rbn0 + q - MB: the 1 KiB tile (rb, t) and the
-    // scale word group (rb, t / 4).  Blocks past the operand and steps past K
-    // read zeros.
-    auto issue = [&](int t, uint8_t* st) {
+    // Wave w loads blocks q = w LPW .. w LPW + LPW - 1 of a step, q < MB
+    // being A block rbm0 + q and the rest B block rbn0 + q - MB: the 1 KiB
+    // tile (rb, t) of step t into tile stage t % S and, for the first step of
+    // each 4-step group h, the scale word group (rb, h) into word slot
+    // h % WS, issued just before that step's tiles.  Blocks past
+    // the operand and steps past K read zeros.  Each block's resource and
+    // offsets are values set up once here.
+    Rsrc rsrc[LPW];
+    bool rb_live[LPW];
+    uint32_t tile_base[LPW], word_base[LPW];
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+        const int q = wave * LPW + i;
+        int rb, rb_end;
+        uint32_t word_region;
+        if (q < MB) {
+            rb = rbm0 + q;
+            rb_end = ga.RB;
+            word_region = (uint32_t)ga.code_bytes;
+            rsrc[i] = make_rsrc(a_src, (uint32_t)ga.total_bytes);
+        } else {
+            rb = rbn0 + (q - MB);
+            rb_end = gb.RB;
+            word_region = (uint32_t)gb.code_bytes;
+            rsrc[i] = make_rsrc(bp, (uint32_t)gb.total_bytes);
+        }
+        rb_live[i] = rb < rb_end;
+        tile_base[i] = ((uint32_t)(rb * KS) * 64u + (uint32_t)L) * 16u;
+        word_base[i] = word_region + ((uint32_t)(rb * KW) * 64u + (uint32_t)L) * 4u;
+    }
+    auto issue = [&](int t, int ws) {
+        if ((t & 3) == 0) {
+#pragma unroll
+            for (int i = 0; i < LPW; ++i) {
+                const uint32_t woff = rb_live[i] && t < KS ? word_base[i] + (uint32_t)(t >> 2) * 256u : kOutOfRange;
+                bload4_lds(rsrc[i], words + (size_t)ws * WGROUP + (wave * LPW + i) * kTileWordBytes, woff);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
-            const int q = wave * LPW + i;
-            const bool is_a = q < MB;
-            const int rb = is_a ? rbm0 + q : rbn0 + (q - MB);
-            const bool live = t < KS && rb < (is_a ? ga.RB : gb.RB);
-            const uint32_t code_bytes = (uint32_t)(is_a ? ga.code_bytes : gb.code_bytes);
-            const uint32_t toff = live ? ((uint32_t)(rb * KS + t) * 64u + (uint32_t)L) * 16u : kOutOfRange;
-            const uint32_t woff =
-                live ? code_bytes + ((uint32_t)(rb * KW + (t >> 2)) * 64u + (uint32_t)L) * 4u : kOutOfRange;
-            bload16_lds(is_a ? ra : rbr, st + q * kTileOpBytes, toff);
-            bload4_lds(is_a ? ra : rbr, st + OPS * kTileOpBytes + q * kTileWordBytes, woff);
+            const uint32_t toff = rb_live[i] && t < KS ? tile_base[i] + (uint32_t)t * 1024u : kOutOfRange;
+            bload16_lds(rsrc[i], lds + (size_t)(t % S) * TSTAGE + (wave * LPW + i) * kTileOpBytes, toff);
         }
     };
 
@@ -106,55 +170,89 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-    // this wave's fragments of one step: TM A tiles and TN B tiles (16 bytes
-    // a lane) and their scale words
+    // a wave's fragments of one step (TM A and TN B tiles, 16 bytes a lane)
+    // and the scale words of its 4-step group
     struct Frags {
         u32x4 a[TM], b[TN];
         uint32_t as[TM], bs[TN];
     };
-    auto read_frags = [&](const uint8_t* st, Frags& f) {
+    auto read_tiles = [&](int t, Frags& f) {
+        const uint8_t* st = lds + (size_t)(t % S) * TSTAGE;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-            f.a[i] = *(const u32x4*)(st + (wm * TM + i) * kTileOpBytes + 16 * L);
-            f.as[i] = *(const uint32_t*)(st + OPS * kTileOpBytes + (wm * TM + i) * kTileWordBytes + 4 * L);
-        }
+        for (int i = 0; i < TM; ++i) f.a[i] = *(const u32x4*)(st + (wm * TM + i) * kTileOpBytes + 16 * L);
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-            f.b[j] = *(const u32x4*)(st + (MB + wn * TN + j) * kTileOpBytes + 16 * L);
-            f.bs[j] = *(const uint32_t*)(st + OPS * kTileOpBytes + (MB + wn * TN + j) * kTileWordBytes + 4 * L);
-        }
+        for (int j = 0; j < TN; ++j) f.b[j] = *(const u32x4*)(st + (MB + wn * TN + j) * kTileOpBytes + 16 * L);
+    };
+    auto read_words = [&](int ws, Frags& f) {
+        const uint8_t* wg = words + (size_t)ws * WGROUP;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) f.as[i] = *(const uint32_t*)(wg + (wm * TM + i) * kTileWordBytes + 4 * L);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) f.bs[j] = *(const uint32_t*)(wg + (MB + wn * TN + j) * kTileWordBytes + 4 * L);
     };
 
-    // The ring holds S steps in flight.  Step t's fragments are read into
-    // registers one step ahead, so a wave's LDS reads of step t + 1 overlap
-    // its MFMAs of step t; the barrier before them tells every wave that the
-    // loads of step t + 1 have landed everywhere and that every wave has
-    // read step t (its LDS reads completed), whose stage then takes step
-    // t + S.
+    // The ring holds S steps in flight; word slot of group h: h % WS
+    // (tile_word_slots says why WS slots suffice).  Step t's fragments are read into registers
+    // one step ahead, so a wave's LDS reads of step t + 1 overlap its MFMAs of
+    // step t; the barrier before them tells every wave that the loads of
+    // step t + 1 have landed everywhere and that every wave has read step t
+    // (its LDS reads completed), whose stage then takes step t + S.
+    int ws_issue = 0;   // word slot of the next group to issue
 #pragma unroll
-    for (int t = 0; t < S; ++t) issue(t, lds + (size_t)t * STAGE);
-    wait_vmcnt<2 * LPW * (S - 1)>();   // step 0 has landed for this wave
+    for (int t = 0; t < S; ++t) {
+        issue(t, ws_issue);
+        if ((t & 3) == 0) ws_issue = ws_issue == WS - 1 ? 0 : ws_issue + 1;
+    }
+    wait_vmcnt<LPW * (S - 1) + LPW * ((S - 1) / 4)>();   // step 0 and its words have landed
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     Frags cur, nxt;
-    read_frags(lds, cur);
-    int st_t = 0;   // stage of step t
-    for (int t = 0; t < KS; ++t) {
-        const int st_n = st_t == S - 1 ? 0 : st_t + 1;   // stage of step t + 1
-        // step t + 1 has landed for this wave once at most the loads of
-        // steps t + 2 .. t + S - 1 are outstanding (a wave's loads complete
-        // in issue order)
-        wait_vmcnt<2 * LPW * (S - 2)>();
+    read_tiles(0, cur);
+    read_words(0, cur);
+    int ws_read = 0;    // word slot of the group being read
+    const int groups = (KS + 3) / 4;
+    // one K step at position U of its 4-step group (U fixes the wait count,
+    // the scale byte and whether the next group's words are read)
+    auto step = [&](int t, auto uc) {
+        constexpr int U = decltype(uc)::value;
+        // step t + 1 (and its words) has landed for this wave once at most
+        // the loads issued after its tiles are outstanding (a wave's loads
+        // complete in issue order)
+        // (scheduling fences keep each step's MFMAs between its barrier and
+        // the next, on fragments already in registers)
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<tile_wait_count(LPW, S, U)>();
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        issue(t + S, lds + (size_t)st_t * STAGE);
-        read_frags(lds + (size_t)st_n * STAGE, nxt);
-        const int sh = 8 * (t & 3);   // byte of step t in the scale words
+        __builtin_amdgcn_sched_barrier(0);
+        issue(t + S, ws_issue);
+        if constexpr (((U + S) & 3) == 0) ws_issue = ws_issue == WS - 1 ? 0 : ws_issue + 1;
+        read_tiles(t + 1, nxt);
+        if constexpr (U == 3) {
+            ws_read = ws_read == WS - 1 ? 0 : ws_read + 1;
+            read_words(ws_read, nxt);
+        } else {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) nxt.as[i] = cur.as[i];
+#pragma unroll
+            for (int j = 0; j < TN; ++j) nxt.bs[j] = cur.bs[j];
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j)
-                acc[i][j] = mfma_fp4_32x32x64(cur.b[j], cur.a[i], acc[i][j], cur.bs[j] >> sh, cur.as[i] >> sh);
+                acc[i][j] = mfma_fp4_sel<U>(cur.b[j], cur.a[i], acc[i][j], cur.bs[j], cur.as[i]);
+        // the loads go out first; the reads of step t + 1 then run under
+        // this step's MFMAs
+        __builtin_amdgcn_sched_group_barrier(0x020, 2 * LPW, 0);
+        order_reads_between_mfmas<(TM + TN < TM * TN ? TM + TN : TM * TN)>();
+        __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);
         cur = nxt;
-        st_t = st_n;
+    };
+    for (int g = 0; g < groups; ++g) {
+        step(4 * g + 0, std::integral_constant<int, 0>{});
+        step(4 * g + 1, std::integral_constant<int, 1>{});
+        step(4 * g + 2, std::integral_constant<int, 2>{});
+        step(4 * g + 3, std::integral_constant<int, 3>{});
     }
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -170,7 +268,7 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     constexpr int WC = TN * kRowBlock;   // columns of a wave's row of blocks
     constexpr int WROW = WC + 8;          // bf16 per staged row (16-byte pad)
-    static_assert((size_t)NW * kRowBlock * WROW * 2 <= (size_t)S * STAGE, "stages fit the ring");
+    static_assert((size_t)NW * kRowBlock * WROW * 2 <= (size_t)S * TSTAGE, "stages fit the ring");
     uint16_t* wst = (uint16_t*)(lds + (size_t)wave * kRowBlock * WROW * 2);
     const int m_lane = L & 31;
     const int n_lane = 4 * (L >> 5);
@@ -189,8 +287,10 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
             }
         // the wave reads back its own LDS writes (in order within a wave)
         const int m_base = (rbm0 + wm * TM + i) * kRowBlock;
+        static_assert(kRowBlock * WC / 8 % 64 == 0, "whole 16-byte chunks per lane");
 #pragma unroll
-        for (int c = L; c < kRowBlock * WC / 8; c += 64) {
+        for (int k = 0; k < kRowBlock * WC / 8 / 64; ++k) {
+            const int c = L + 64 * k;
             const int row = c / (WC / 8), c8 = c % (WC / 8);
             const int m = m_base + row, n = n_base + 8 * c8;
             const u32x4 v = *(const u32x4*)(wst + row * WROW + 8 * c8);
@@ -216,7 +316,7 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
 // 32-column blocks of the workgroup tile, wk the waves along M and wn the
 // waves along N (splits 1).
 
-constexpr int kTileStages = 6;
+constexpr int kTileStages = 8;
 
 GemmKernelFn find_tile_kernel(const Plan& plan) {
     if (plan.mb == 8 && plan.nb == 8 && plan.wk == 2 && plan.wn == 4)
@@ -228,6 +328,6 @@ GemmKernelFn find_tile_kernel(const Plan& plan) {
     return nullptr;
 }
 
-size_t tile_lds_bytes(const Plan& plan) { return (size_t)kTileStages * tile_stage_bytes(plan.mb, plan.nb); }
+size_t tile_lds_bytes(const Plan& plan) { return tile_lds_bytes_for(plan.mb, plan.nb, kTileStages); }
 
 }  // namespace mx4
