@@ -18,7 +18,9 @@ stream, which covers every launch of a call (two at 256x3072x1536: the
 activation quantiser and the GEMM).  Beside them: the oracle timed on the
 host cores (cpu_baseline), what a near-empty kernel and a kernel that only
 streams the same weight bytes with the GEMM's own grid cost (reference
-floors), and the same figures for the other workloads (per_workload).
+floors), the same figures for the other workloads (per_workload), and the
+GPU time and fp4 MFMA rate of four large-M shapes, where the contraction
+bounds the call (large_m).
 """
 from __future__ import annotations
 
@@ -389,6 +391,19 @@ def _dispatches(rows, counter_names=()):
     return [per[k] for k in order]
 
 
+def _calibration(disp, counter):
+    """The counter's reading on the calibration copy: the largest among the
+    dispatches that run before the first library kernel."""
+    pre = []
+    for d in disp:
+        if d["name"].startswith("mx4::"):
+            break
+        pre.append(d.get(counter, 0.0))
+    if not pre or max(pre) <= 0:
+        raise SystemExit("no calibration dispatch before the first mx4 kernel")
+    return max(pre)
+
+
 def _segments(disp):
     """The mx4 dispatches of a --profile run split per workload: each
     segment is the weight pack, the calls' launches, then the
@@ -429,8 +444,8 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, calls):
         if len(v) != nw:
             raise SystemExit("%s: %d workload segments, expected %d" % (k, len(v), nw))
     copy_bytes = 256 << 20
-    cal_f = max(d.get("FETCH_SIZE", 0.0) for d in fetch)
-    cal_w = max(d.get("WRITE_SIZE", 0.0) for d in write)
+    cal_f = _calibration(fetch, "FETCH_SIZE")
+    cal_w = _calibration(write, "WRITE_SIZE")
     f_scale, w_scale = copy_bytes / (cal_f * 1024), copy_bytes / (cal_w * 1024)
     cmd = "rocprofv3 %s -f csv -d %s -o %s -- python3 bench.py --profile %d"
     lines = ["# GEMM kernels on MI355X: rocprofv3 kernel trace and counters", "",
@@ -529,6 +544,220 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, calls):
     with open(os.path.join(out, "gemm_kernels_trace.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(os.path.join(out, "gemm_traffic.json"), "w") as f:
+        json.dump(record, f, indent=1)
+        f.write("\n")
+    print("\n".join(lines))
+
+
+# ---------------------------------------------------------------------------
+# Large M: shapes where the contraction, not the weight stream, bounds the
+# call (the tile mode's regime).  One set of buffers per shape, called back to
+# back (at these sizes a call does far more MFMA work than it moves bytes).
+
+LARGE_M_SHAPES = [(1024, 4096, 4096), (2048, 7168, 2048), (4096, 4096, 4096), (8192, 8192, 8192)]
+
+
+def _large_name(M, N, K):
+    return "%dx%dx%d" % (M, N, K)
+
+
+def large_setup(torch, B, inputs, M, N, K):
+    """Device inputs (seeded N(0,1) bf16), packed weight, output and
+    workspace of one large-M shape, and the mx_gemm argument tuple."""
+    A, Bm = inputs.shape_inputs(M, N, K, seed=1000)
+    dev = "cuda:0"
+    Ad = A.to(dev)
+    del A
+    P = B.mx_pack_weight(Bm.to(dev))
+    del Bm
+    plan = B.mx_gemm_plan(M, N, K)
+    wsb = B.mx_gemm_workspace_bytes(M, N, K)
+    ws = torch.zeros(max(wsb, 256), dtype=torch.uint8, device=dev)
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    args = (Ad.data_ptr(), M, K, K, P.data_ptr(), N, C.data_ptr(), N, ws.data_ptr(), ws.numel())
+    torch.cuda.synchronize()
+    return {"keep": (Ad, P, ws, C), "args": args, "plan": plan,
+            "launches": 1 + (plan["amode"] in (1, 6)) + (1 if plan["splits"] > 1 and not plan["finish"] else 0)}
+
+
+def load_large_profile():
+    """profiles/large_m_traffic.json, only if taken on the current kernel sources."""
+    try:
+        with open(os.path.join(ROOT, "profiles", "large_m_traffic.json")) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return rec if rec.get("kernel_source_hash") == kernel_source_hash() else None
+
+
+def measure_large_m(torch, B, inputs):
+    """GPU time per mx_gemm call (graph replay of 20 back-to-back calls) and
+    the fp4 MFMA rate for each large-M shape; the traced per-kernel figures
+    of the committed profile beside it when current."""
+    fn = B.ext().gemm
+    prof = load_large_profile()
+    out = {}
+    for (M, N, K) in LARGE_M_SHAPES:
+        st = large_setup(torch, B, inputs, M, N, K)
+        args = st["args"]
+
+        def call(i, stream):
+            if fn(*args, stream):
+                raise RuntimeError("mx_gemm failed under capture")
+        us = graph_time(torch, call, 20)
+        flops = 2.0 * M * N * K
+        name = _large_name(M, N, K)
+        rec = {"plan": st["plan"], "launches_per_call": st["launches"], "gpu_us_per_call": round(us, 3),
+               "tflops": round(flops / us / 1e6, 1), "fp4_mfma_frac": round(flops / us / 1e6 / FP4_PEAK_TFLOPS, 4)}
+        if prof is not None and name in prof.get("shapes", {}):
+            rec["traced"] = prof["shapes"][name]
+        out[name] = rec
+        print(json.dumps({"large_m " + name: rec}), file=sys.stderr, flush=True)
+        del st
+        torch.cuda.empty_cache()
+    return out
+
+
+def profile_large_m(torch, B, inputs, hw, calls):
+    """No timing.  The 256 MiB calibration copy, then per large-M shape: the
+    weight pack, CALLS mx_gemm calls captured in a HIP graph and replayed
+    once, and one near-empty reference dispatch that ends the shape's
+    segment.  For running under rocprofv3."""
+    n = 256 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    buf = torch.zeros(256, dtype=torch.uint8, device="cuda:0")
+    mark = torch.empty(64, dtype=torch.int32, device="cuda:0")
+    fn = B.ext().gemm
+    for (M, N, K) in LARGE_M_SHAPES:
+        st = large_setup(torch, B, inputs, M, N, K)
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            handle = torch.cuda.current_stream().cuda_stream
+            for _ in range(calls):
+                if fn(*st["args"], handle):
+                    raise RuntimeError("mx_gemm failed under capture")
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        del g
+        if hw.mxhw_stream_read(buf.data_ptr(), 16, 1, 1, 1, 16, 0, 0, mark.data_ptr(),
+                               torch.cuda.current_stream().cuda_stream):
+            raise RuntimeError("mxhw_stream_read failed")
+        torch.cuda.synchronize()
+        print("profiled %s plan %s: %d calls" % (_large_name(M, N, K), st["plan"], calls), flush=True)
+        del st
+        torch.cuda.empty_cache()
+
+
+def summarize_large_m(trace_dir, fetch_dir, write_dir, mfma_dir, calls, out_dir=None):
+    """profiles/large_m_trace.md and profiles/large_m_traffic.json from the
+    rocprofv3 output of four `bench.py --profile-large-m CALLS` runs (trace,
+    FETCH_SIZE, WRITE_SIZE, fp4 MFMA counters), per kernel of a call: traced
+    duration, the fp4 MFMA rate of the GEMM kernel against the dense peak,
+    and its counted HBM bytes against the bytes it must move."""
+    trace = _dispatches(_csv(trace_dir, "kernel_trace.csv"))
+    fetch = _dispatches(_csv(fetch_dir, "counter_collection.csv"), ("FETCH_SIZE",))
+    write = _dispatches(_csv(write_dir, "counter_collection.csv"), ("WRITE_SIZE",))
+    mfma = _dispatches(_csv(mfma_dir, "counter_collection.csv"), MFMA_COUNTERS)
+    segs = {k: _segments(v) for k, v in (("trace", trace), ("fetch", fetch), ("write", write), ("mfma", mfma))}
+    for k, v in segs.items():
+        if len(v) != len(LARGE_M_SHAPES):
+            raise SystemExit("%s: %d shape segments, expected %d" % (k, len(v), len(LARGE_M_SHAPES)))
+    copy_bytes = 256 << 20
+    cal_f = _calibration(fetch, "FETCH_SIZE")
+    cal_w = _calibration(write, "WRITE_SIZE")
+    f_scale, w_scale = copy_bytes / (cal_f * 1024), copy_bytes / (cal_w * 1024)
+    cmd = "rocprofv3 %s -f csv -d %s -o %s -- python3 bench.py --profile-large-m %d"
+    lines = ["# Large-M GEMM kernels on MI355X: rocprofv3 kernel trace and counters", "",
+             "Kernel durations (end minus start timestamp of each dispatch): `%s`" % (
+                 cmd % ("--kernel-trace --stats", trace_dir, "trace", calls)), "",
+             "Counters, one run each: `%s`, `%s`, `%s`" % (
+                 cmd % ("--pmc FETCH_SIZE", fetch_dir, "fetch", calls),
+                 cmd % ("--pmc WRITE_SIZE", write_dir, "write", calls),
+                 cmd % ("--pmc " + " ".join(MFMA_COUNTERS), mfma_dir, "mfma", calls)), "",
+             "`--profile-large-m %d` runs the 256 MiB calibration copy (FETCH_SIZE reads %.0f KiB and WRITE_SIZE "
+             "%.0f KiB on it, so they are scaled by %.3f and %.3f to bytes), then per shape: the weight pack (left "
+             "out below) and %d back-to-back mx_gemm calls on one set of seeded N(0,1) bf16 buffers, captured in a "
+             "HIP graph and replayed once. Bytes to move: the kernel's inputs and outputs once (pre-quantiser: A "
+             "bf16 in, packed A out; GEMM: packed A and packed B in, C bf16 out)." % (
+                 calls, cal_f, cal_w, f_scale, w_scale, calls), "",
+             "| shape M x N x K | kernel | grid (threads) | dispatches | avg us | min us | fp4 TFLOP/s (avg) | "
+             "of 10.1 PFLOP/s | FETCH bytes | WRITE bytes | bytes to move | counted / to move |",
+             "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    record = {"kernel_source_hash": kernel_source_hash(),
+              "source": "profiles/large_m_trace.md (python3 bench.py --profile-large-m %d under rocprofv3)" % calls,
+              "shapes": {}}
+    mrows = []
+    for si, (M, N, K) in enumerate(LARGE_M_SHAPES):
+        def groups(seg):
+            g, order = {}, []
+            for d in seg[1:]:   # the weight pack left out
+                if d["name"].startswith("mx4::hw_stream_kernel"):
+                    continue
+                key = (d["name"], d["grid"])
+                if key not in g:
+                    g[key] = []
+                    order.append(key)
+                g[key].append(d)
+            return g, order
+        tg, order = groups(segs["trace"][si])
+        fg, _ = groups(segs["fetch"][si])
+        wg, _ = groups(segs["write"][si])
+        mg, _ = groups(segs["mfma"][si])
+
+        def med(gr, key, cname):
+            vals = [d.get(cname) for d in gr.get(key, []) if d.get(cname) is not None]
+            return statistics.median(vals) if vals else None
+        flops = 2.0 * M * N * K
+        packed = lambda rows: rows * K // 2 + rows * K // 32
+        srec = {"kernels": {}}
+        call_us = 0.0
+        for key in order:
+            ds = [d["us"] for d in tg[key]]
+            avg = statistics.mean(ds)
+            call_us += avg
+            fb, wb = med(fg, key, "FETCH_SIZE"), med(wg, key, "WRITE_SIZE")
+            fb = None if fb is None else fb * 1024 * f_scale
+            wb = None if wb is None else wb * 1024 * w_scale
+            gemm = key[0].startswith("mx4::gemm")
+            move = packed(M) + packed(N) + 2 * M * N if gemm else 2 * M * K + packed(M)
+            tf = flops / avg / 1e6 if gemm else None
+            lines.append("| %s | `%s` | %d | %d | %.2f | %.2f | %s | %s | %s | %s | %d | %s |" % (
+                _large_name(M, N, K), key[0], key[1], len(ds), avg, min(ds),
+                "%.0f" % tf if tf else "-", "%.3f" % (tf / FP4_PEAK_TFLOPS) if tf else "-",
+                "%.0f" % fb if fb is not None else "-", "%.0f" % wb if wb is not None else "-", move,
+                "%.2f" % ((fb + wb) / move) if fb is not None and wb is not None else "-"))
+            srec["kernels"][key[0]] = {"avg_us": round(avg, 3), "bytes_to_move": move,
+                                       "hbm_bytes": None if fb is None or wb is None else round(fb + wb)}
+            if gemm:
+                srec["gemm_kernel"] = key[0]
+                srec["gemm_tflops_traced"] = round(tf, 1)
+                srec["gemm_fp4_frac_traced"] = round(tf / FP4_PEAK_TFLOPS, 4)
+                mrows.append((M, N, K, key[0], avg, med(mg, key, "SQ_INSTS_VALU_MFMA_MOPS_F6F4"),
+                              med(mg, key, "SQ_VALU_MFMA_BUSY_CYCLES")))
+        srec["traced_us_per_call"] = round(call_us, 3)
+        record["shapes"][_large_name(M, N, K)] = srec
+    lines += ["", "## fp4 MFMA counters of the GEMM kernel", "",
+              "Medians over the dispatches, summed over all XCDs. MOPS x 512 is the counter's flop count; MFMA busy "
+              "= SQ_VALU_MFMA_BUSY_CYCLES / (traced duration x 2.4 GHz x 1024 SIMDs).", "",
+              "| shape | kernel | traced us | MOPS x 512 | 2MNK | ratio | MFMA busy |", "|---|---|---|---|---|---|---|"]
+    for M, N, K, kname, us, mops, busy in mrows:
+        flops = 2.0 * M * N * K
+        lines.append("| %s | `%s` | %.2f | %s | %.4g | %s | %s |" % (
+            _large_name(M, N, K), kname, us, "%.4g" % (mops * 512) if mops is not None else "-", flops,
+            "%.3f" % (mops * 512 / flops) if mops is not None else "-",
+            "%.1f %%" % (100 * busy / (us * 2400.0 * 1024)) if busy is not None else "-"))
+    out = out_dir or os.path.join(ROOT, "profiles")
+    with open(os.path.join(out, "large_m_trace.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(os.path.join(out, "large_m_traffic.json"), "w") as f:
         json.dump(record, f, indent=1)
         f.write("\n")
     print("\n".join(lines))
@@ -689,6 +918,12 @@ def main():
     ap.add_argument("--summarize", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "MFMA_DIR"),
                     help="no GPU: summarise the rocprofv3 output of --profile runs into profiles/")
     ap.add_argument("--summarize-calls", type=int, default=100, help="the --profile CALLS being summarised")
+    ap.add_argument("--no-large-m", action="store_true", help="skip the large-M (MFMA-bound) shapes")
+    ap.add_argument("--profile-large-m", type=int, default=0, metavar="CALLS",
+                    help="no timing: the calibration copy, then per large-M shape CALLS mx_gemm calls, for "
+                         "running under rocprofv3")
+    ap.add_argument("--summarize-large-m", nargs=4, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "MFMA_DIR"),
+                    help="no GPU: summarise the rocprofv3 output of --profile-large-m runs into profiles/")
     ap.add_argument("--plan-regret", nargs="?", const="all", default=None, metavar="PAIRS",
                     help="time the library's plan against candidate plans on the pages' shape grid (PAIRS: "
                          "comma-separated indices of the (N, K) pairs, default all) and write profiles/plan_regret.*")
@@ -716,6 +951,9 @@ def main():
     if args.summarize:
         summarize_profiles(*args.summarize, args.summarize_calls)
         return
+    if args.summarize_large_m:
+        summarize_large_m(*args.summarize_large_m, args.summarize_calls)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode (run with --gpus 1)",
               file=sys.stderr)
@@ -728,6 +966,9 @@ def main():
 
     if args.profile:
         profile_run(torch, B, inputs, hw, args.profile)
+        return
+    if args.profile_large_m:
+        profile_large_m(torch, B, inputs, hw, args.profile_large_m)
         return
     if args.plan_regret:
         only = None if args.plan_regret == "all" else [int(i) for i in args.plan_regret.split(",")]
@@ -797,6 +1038,12 @@ def main():
         },
         "per_workload": per_workload,
     }
+    if not args.no_large_m and not args.only_headline:
+        line["large_m"] = {
+            "note": "MFMA-bound shapes (tile mode): GPU us per mx_gemm call in HIP graph replay of 20 back-to-back "
+                    "calls on one set of buffers, all launches of a call; fp4 rate against the 10.1 PFLOP/s dense "
+                    "peak; 'traced' = the committed rocprofv3 figures per kernel when taken on the current sources",
+            "shapes": measure_large_m(torch, B, inputs)}
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(HEADLINE, inputs)
     print(json.dumps(line), flush=True)

@@ -134,6 +134,8 @@ size_t shared_lds_bytes(const Plan& plan, int steps_per_split);
 // (8, 4, 2, 2)}; splits 1.
 GemmKernelFn find_tile_kernel(const Plan& plan);
 size_t tile_lds_bytes(const Plan& plan);
+// Tile-mode workgroups one XCD runs at once: its 32 CUs hold one each (LDS).
+constexpr int kTileWgsPerXcd = 32;
 
 // Placement of the shared kernel's tiles on the 8 XCDs.  The dispatcher
 // hands the workgroups of a grid, in x-major order, to XCD (linear id mod 8),
@@ -152,7 +154,11 @@ size_t tile_lds_bytes(const Plan& plan);
 // its steps-per-split argument (a shared-mode split has at most 24 steps),
 // which is among the preloaded arguments: the first loads' addresses wait
 // on no argument-segment read.
-inline int shared_xcd_map(int mtiles, int ntiles, int splits, double a_bytes, double b_bytes) {
+// With conc > 0, an XCD runs at most conc workgroups at once, in rounds of
+// conc consecutive ones: its rectangle is then scored by the fetches of its
+// rounds, each round covering min(a, conc) M tiles x ceil(conc / a) N tiles
+// (the decode below walks M fastest).
+inline int shared_xcd_map(int mtiles, int ntiles, int splits, double a_bytes, double b_bytes, int conc = 0) {
     if (splits != 1 || mtiles < 1 || ntiles < 1 || ((long long)mtiles * ntiles) % 8 != 0) return 0;
     int best = 0;
     double best_cost = 0.0;
@@ -163,7 +169,12 @@ inline int shared_xcd_map(int mtiles, int ntiles, int splits, double a_bytes, do
         if ((a & (a - 1)) != 0) continue;
         int la = 0;
         while ((1 << la) < a) ++la;
-        const double cost = a * a_bytes + b * b_bytes;
+        double cost = a * a_bytes + b * b_bytes;
+        if (conc > 0 && (long long)a * b > conc) {
+            const double rounds = (double)a * b / conc;
+            const int ra = a < conc ? a : conc, rb = (conc + a - 1) / a;
+            cost = rounds * (ra * a_bytes + rb * b_bytes);
+        }
         if (best == 0 || cost < best_cost) {
             best = 1 + la + 16 * lmg;
             best_cost = cost;

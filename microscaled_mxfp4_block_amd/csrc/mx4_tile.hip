@@ -65,13 +65,22 @@ __device__ __forceinline__ f32x16 mfma_fp4_sel(const u32x4& a, const u32x4& b, f
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(va, vb, acc, 4, 4, SEL, (int)scale_a, SEL, (int)scale_b);
 }
 
-// Loads of a wave issued after the tiles of step t + 1 while step t is in
-// flight: the tiles of steps t + 2 .. t + S - 1 and the word groups whose
-// first step is among them (LPW of each).
-__host__ __device__ constexpr int tile_wait_count(int lpw, int s, int u) {
+// The workgroup syncs once every G steps, at the barrier before step t
+// (t a multiple of G, t = u mod 4).  Loads of a wave that may still be
+// outstanding there once the tiles and words of every step up to t + G have
+// landed: the tiles of steps t + G + 1 .. t + S - G (issued at earlier
+// barriers) and the word groups whose first step is among them.
+__host__ __device__ constexpr int tile_wait_count(int lpw, int s, int g, int u) {
     int groups = 0;
-    for (int x = u + 2; x <= u + s - 1; ++x) groups += (x % 4 == 0);
-    return lpw * (s - 2) + lpw * groups;
+    for (int x = u + g + 1; x <= u + s - g; ++x) groups += (x % 4 == 0);
+    return lpw * (s - 2 * g) + lpw * groups;
+}
+
+// The same before the first barrier: steps 0 .. S - G issued, step 0 landed.
+__host__ __device__ constexpr int tile_prologue_wait(int lpw, int s, int g) {
+    int groups = 0;
+    for (int x = 1; x <= s - g; ++x) groups += (x % 4 == 0);
+    return lpw * (s - g) + lpw * groups;
 }
 
 // Scheduling order of one K step after its barrier: the buffer loads, then
@@ -85,7 +94,7 @@ __device__ __forceinline__ void order_reads_between_mfmas() {
     }
 }
 
-template <int MB, int NB, int WM, int WN, int S>
+template <int MB, int NB, int WM, int WN, int S, int G>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_buf, int lda, int ldc, int M,
                  int N, int K, int steps_arg, uint32_t* counters, int splits, int mtiles) {
@@ -102,7 +111,8 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
     constexpr int TSTAGE = OPS * kTileOpBytes;
     constexpr int WGROUP = OPS * kTileWordBytes;
     constexpr uint32_t kOutOfRange = 0x80000000u;
-    static_assert(tile_wait_count(LPW, S, 1) < 64 && LPW * (S - 1) + LPW * ((S - 1) / 4) < 64, "vmcnt range");
+    static_assert(G >= 1 && 4 % G == 0 && S >= 2 * G, "syncs on a 4-step boundary, two sync intervals in the ring");
+    static_assert(tile_prologue_wait(LPW, S, G) < 64, "vmcnt range");
 
     const OperandGeom ga = operand_geom(M, K), gb = operand_geom(N, K);
     const int KS = gb.KS, KW = gb.KW;
@@ -191,40 +201,46 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
         for (int j = 0; j < TN; ++j) f.bs[j] = *(const uint32_t*)(wg + (MB + wn * TN + j) * kTileWordBytes + 4 * L);
     };
 
-    // The ring holds S steps in flight; word slot of group h: h % WS
-    // (tile_word_slots says why WS slots suffice).  Step t's fragments are read into registers
-    // one step ahead, so a wave's LDS reads of step t + 1 overlap its MFMAs of
-    // step t; the barrier before them tells every wave that the loads of
-    // step t + 1 have landed everywhere and that every wave has read step t
-    // (its LDS reads completed), whose stage then takes step t + S.
+    // The ring holds S steps; word slot of group h: h % WS (tile_word_slots
+    // says why WS slots suffice).  Step t's fragments are read into
+    // registers one step ahead, so a wave's LDS reads of step t + 1 overlap
+    // its MFMAs of step t.  The workgroup syncs every G steps: the barrier
+    // before step t (t a multiple of G) tells every wave that the loads of
+    // steps up to t + G have landed everywhere and that every wave has read
+    // the steps up to t (its LDS reads completed), whose stages then take
+    // steps t + S - G + 1 .. t + S.  The prologue issues steps 0 .. S - G.
     int ws_issue = 0;   // word slot of the next group to issue
 #pragma unroll
-    for (int t = 0; t < S; ++t) {
+    for (int t = 0; t <= S - G; ++t) {
         issue(t, ws_issue);
         if ((t & 3) == 0) ws_issue = ws_issue == WS - 1 ? 0 : ws_issue + 1;
     }
-    wait_vmcnt<LPW * (S - 1) + LPW * ((S - 1) / 4)>();   // step 0 and its words have landed
+    wait_vmcnt<tile_prologue_wait(LPW, S, G)>();   // step 0 and its words have landed
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     Frags cur, nxt;
     read_tiles(0, cur);
     read_words(0, cur);
     int ws_read = 0;    // word slot of the group being read
     const int groups = (KS + 3) / 4;
-    // one K step at position U of its 4-step group (U fixes the wait count,
-    // the scale byte and whether the next group's words are read)
+    // one K step at position U of its 4-step group (U fixes the sync, the
+    // wait count, the scale byte and whether the next group's words are read)
     auto step = [&](int t, auto uc) {
         constexpr int U = decltype(uc)::value;
-        // step t + 1 (and its words) has landed for this wave once at most
-        // the loads issued after its tiles are outstanding (a wave's loads
-        // complete in issue order)
-        // (scheduling fences keep each step's MFMAs between its barrier and
-        // the next, on fragments already in registers)
+        // (scheduling fences keep each step's MFMAs inside the step, on
+        // fragments already in registers)
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<tile_wait_count(LPW, S, U)>();
-        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-        __builtin_amdgcn_sched_barrier(0);
-        issue(t + S, ws_issue);
-        if constexpr (((U + S) & 3) == 0) ws_issue = ws_issue == WS - 1 ? 0 : ws_issue + 1;
+        if constexpr (U % G == 0) {
+            // a wave's loads complete in issue order: at most the loads
+            // issued after step t + G's tiles are outstanding
+            wait_vmcnt<tile_wait_count(LPW, S, G, U)>();
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < G; ++j) {
+                issue(t + S - G + 1 + j, ws_issue);
+                if (((U + S - G + 1 + j) & 3) == 0) ws_issue = ws_issue == WS - 1 ? 0 : ws_issue + 1;
+            }
+        }
         read_tiles(t + 1, nxt);
         if constexpr (U == 3) {
             ws_read = ws_read == WS - 1 ? 0 : ws_read + 1;
@@ -242,7 +258,7 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
                 acc[i][j] = mfma_fp4_sel<U>(cur.b[j], cur.a[i], acc[i][j], cur.bs[j], cur.as[i]);
         // the loads go out first; the reads of step t + 1 then run under
         // this step's MFMAs
-        __builtin_amdgcn_sched_group_barrier(0x020, 2 * LPW, 0);
+        if constexpr (U % G == 0) __builtin_amdgcn_sched_group_barrier(0x020, 2 * LPW * G, 0);
         order_reads_between_mfmas<(TM + TN < TM * TN ? TM + TN : TM * TN)>();
         __builtin_amdgcn_sched_group_barrier(0x008, TM * TN, 0);
         __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TM + TN), 0);
@@ -317,14 +333,15 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
 // waves along N (splits 1).
 
 constexpr int kTileStages = 8;
+constexpr int kTileSync = 2;   // K steps per workgroup barrier
 
 GemmKernelFn find_tile_kernel(const Plan& plan) {
     if (plan.mb == 8 && plan.nb == 8 && plan.wk == 2 && plan.wn == 4)
-        return gemm_tile_kernel<8, 8, 2, 4, kTileStages>;
+        return gemm_tile_kernel<8, 8, 2, 4, kTileStages, kTileSync>;
     if (plan.mb == 4 && plan.nb == 8 && plan.wk == 2 && plan.wn == 2)
-        return gemm_tile_kernel<4, 8, 2, 2, kTileStages>;
+        return gemm_tile_kernel<4, 8, 2, 2, kTileStages, kTileSync>;
     if (plan.mb == 8 && plan.nb == 4 && plan.wk == 2 && plan.wn == 2)
-        return gemm_tile_kernel<8, 4, 2, 2, kTileStages>;
+        return gemm_tile_kernel<8, 4, 2, 2, kTileStages, kTileSync>;
     return nullptr;
 }
 

@@ -392,6 +392,49 @@ def test_shared_kernels_keep_weight_loads_in_flight_across_barriers():
     assert checked == 19, checked
 
 
+def test_tile_kernels_keep_their_ring_of_loads_in_flight():
+    """In every tile-mode kernel (MB x NB blocks, WM x WN waves, S ring
+    stages, one barrier per G K steps; LPW = (MB + NB) / (WM WN) blocks
+    loaded per wave and step, plus one scale word load per block every 4
+    steps): before the first barrier the kernel waits only for step 0, with
+    the tiles of steps 1 .. S - G and their word groups still in flight, and
+    each barrier of the K loop waits only for the steps up to t + G, leaving
+    steps t + G + 1 .. t + S - G in flight: for the loop position u = t mod 4,
+    LPW (S - 2G) tile loads plus LPW per word group starting in that range.
+    Every barrier waits for the wave's own LDS reads first, and only the
+    epilogue waits for every load."""
+    build = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "_build")
+    path = os.path.join(build, "mx4_tile.s")
+    if not os.path.exists(path):
+        pytest.skip("no device assembly under _build (run the package build first)")
+    text = open(path).read()
+
+    def starts(lo, hi):   # word groups (first step a multiple of 4) among steps lo .. hi
+        return sum(1 for x in range(lo, hi + 1) if x % 4 == 0)
+    checked = 0
+    pat = r"^(_ZN3mx416gemm_tile_kernelILi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)E\S*):.*?^\.Lfunc_end"
+    for m in re.finditer(pat, text, re.S | re.M):
+        name = m.group(1)
+        MB, NB, WM, WN, S, G = (int(m.group(k)) for k in range(2, 8))
+        lpw = (MB + NB) // (WM * WN)
+        body = [ln.strip() for ln in m.group(0).splitlines() if not ln.strip().startswith(";")]
+        bars = [k for k, ln in enumerate(body) if ln == "s_barrier"]
+        assert len(bars) >= 3, name
+        for k in bars:
+            assert body[k - 1] == "s_waitcnt lgkmcnt(0)", (name, body[k - 1])
+        waits = [(k, int(w.group(1))) for k, ln in enumerate(body) for w in [re.search(r"vmcnt\((\d+)\)", ln)] if w]
+        first = [v for k, v in waits if k < bars[0]]
+        assert first == [lpw * (S - G) + lpw * starts(1, S - G)], (name, first)
+        inner = [(k, v) for k, v in waits if bars[0] < k < bars[-1]]
+        assert inner and inner[-1][1] == 0, name            # the epilogue's wait for every load
+        loop = {v for k, v in inner[:-1]}
+        expected = {lpw * (S - 2 * G) + lpw * starts(u + G + 1, u + S - G) for u in range(0, 4, G)}
+        assert loop == expected, (name, sorted(loop), sorted(expected))
+        assert not [v for k, v in waits if k > bars[-1]], name
+        checked += 1
+    assert checked == 3, checked
+
+
 def test_shapes_past_the_addressing_limit_are_refused():
     """rows * K * 2 >= 2^31 for an operand (32-bit buffer offsets) is refused
     before any launch; just below it is accepted."""
@@ -618,3 +661,80 @@ def test_library_plans_are_accepted_for_random_shapes():
     for M, N, K in shapes:
         assert B.mx_gemm_workspace_bytes(M, N, K) >= 0
         assert B.mx_gemm_a16w4_workspace_bytes(M, N, K) >= 0
+
+
+def test_bench_large_m_summary_from_synthetic_rocprof_output(tmp_path):
+    """bench.py --summarize-large-m on hand-made rocprofv3 CSVs: the
+    calibration copy sets the counter scales (FETCH_SIZE reads half the
+    copied bytes, WRITE_SIZE all of them), each shape's segment drops its
+    weight pack and ends at the reference dispatch, and the GEMM kernel's
+    fp4 rate and byte ratio follow from the traced durations by hand."""
+    import csv
+    import importlib.util
+    import json as _json
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    spec = importlib.util.spec_from_file_location("mx4_bench_lm", os.path.join(root, "bench.py"))
+    bench = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(bench)
+    shapes = bench.LARGE_M_SHAPES
+    calls = 3
+    copy_kib = (256 << 20) // 1024
+
+    def dispatches():
+        d = [("copy_kernel", 1, 50.0, {"FETCH_SIZE": copy_kib // 2, "WRITE_SIZE": copy_kib})]
+        for si, (M, N, K) in enumerate(shapes):
+            d.append(("mx4::pack_kernel(a)", 999, 7.0, {"FETCH_SIZE": 1, "WRITE_SIZE": 1}))
+            for c in range(calls):
+                d.append(("mx4::pack_kernel(b)", 4096, 2.0 + si, {"FETCH_SIZE": 100, "WRITE_SIZE": 50}))
+                # (the last shape's GEMM counts more than the calibration copy:
+                # the calibration is the copy before the first library kernel)
+                big = si == len(shapes) - 1
+                d.append(("mx4::gemm_tile_kernel<8>(x)", 512, 10.0 * (si + 1) + c, {
+                    "FETCH_SIZE": 4 * copy_kib if big else 1000, "WRITE_SIZE": 4 * copy_kib if big else 2000, "SQ_INSTS_VALU_MFMA_MOPS_F6F4": 2.0 * M * N * K / 512,
+                    "SQ_VALU_MFMA_BUSY_CYCLES": 1.0e6}))
+            d.append(("mx4::hw_stream_kernel(z)", 64, 1.0, {}))
+        return d
+
+    def write(sub, fname, counters):
+        os.makedirs(tmp_path / sub)
+        rows = []
+        for i, (name, grid, us, cv) in enumerate(dispatches()):
+            base = {"Dispatch_Id": i + 1, "Kernel_Name": name, "Grid_Size": grid,
+                    "Start_Timestamp": 10 ** 6 * (i + 1), "End_Timestamp": 10 ** 6 * (i + 1) + int(us * 1000)}
+            picked = [c for c in counters if c in cv]
+            rows += [dict(base, Counter_Name=c, Counter_Value=cv[c]) for c in picked] if counters else [base]
+            if counters and not picked:
+                rows.append(dict(base, Counter_Name="GRBM_COUNT", Counter_Value=0))
+        with open(tmp_path / sub / fname, "w", newline="") as f:
+            w = csv.DictWriter(f, fieldnames=list(rows[0].keys()) if not counters else
+                               ["Dispatch_Id", "Kernel_Name", "Grid_Size", "Start_Timestamp", "End_Timestamp",
+                                "Counter_Name", "Counter_Value"])
+            w.writeheader()
+            w.writerows(rows)
+    write("t", "x_kernel_trace.csv", ())
+    write("f", "x_counter_collection.csv", ("FETCH_SIZE",))
+    write("w", "x_counter_collection.csv", ("WRITE_SIZE",))
+    write("m", "x_counter_collection.csv", bench.MFMA_COUNTERS)
+    out = tmp_path / "out"
+    os.makedirs(out)
+    bench.summarize_large_m(str(tmp_path / "t"), str(tmp_path / "f"), str(tmp_path / "w"), str(tmp_path / "m"),
+                            calls, out_dir=str(out))
+    rec = _json.load(open(out / "large_m_traffic.json"))
+    assert list(rec["shapes"]) == ["%dx%dx%d" % s for s in shapes]
+    for si, (M, N, K) in enumerate(shapes):
+        r = rec["shapes"]["%dx%dx%d" % (M, N, K)]
+        g = r["kernels"]["mx4::gemm_tile_kernel<8>"]
+        avg = 10.0 * (si + 1) + 1.0                     # mean of 10(si+1) + {0, 1, 2}
+        assert g["avg_us"] == round(avg, 3)
+        assert set(r["kernels"]) == {"mx4::gemm_tile_kernel<8>", "mx4::pack_kernel"}   # weight pack dropped
+        assert r["kernels"]["mx4::pack_kernel"]["avg_us"] == 2.0 + si
+        assert r["gemm_tflops_traced"] == round(2.0 * M * N * K / avg / 1e6, 1)
+        # counters: FETCH scaled x2, WRITE x1 (the calibration copy)
+        if si == len(shapes) - 1:
+            assert g["hbm_bytes"] == 4 * copy_kib * 1024 * 2 + 4 * copy_kib * 1024
+        else:
+            assert g["hbm_bytes"] == 1000 * 1024 * 2 + 2000 * 1024
+        assert g["bytes_to_move"] == (M * K // 2 + M * K // 32) + (N * K // 2 + N * K // 32) + 2 * M * N
+        assert r["traced_us_per_call"] == round(avg + 2.0 + si, 3)
+    md = open(out / "large_m_trace.md").read()
+    assert md.count("| 1.000 |") == len(shapes)     # MOPS x 512 / 2MNK
