@@ -773,6 +773,9 @@ GRID_DIM_PAIRS = [
     (2880, 2048), (2880, 7168),
 ]
 GRID_BATCH = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+# Past the grid: large M over six of its weight shapes (the planner's tile-mode rule).
+LARGE_REGRET_PAIRS = [(4096, 512), (3072, 1536), (7168, 2048), (2880, 2048), (2112, 7168), (7168, 7168)]
+LARGE_REGRET_M = [256, 384, 512, 768, 1024, 2048]
 
 
 def regret_candidates(B, M, N, K):
@@ -795,6 +798,9 @@ def regret_candidates(B, M, N, K):
         for wk in (4, 8):
             for sp in (1, 2, 4, 7, 8, 14):
                 cands.append(dict(mb=1, nb=1, wn=wn, wk=wk, splits=sp, amode=5, finish=0))
+    if M >= 256:   # the tile mode's 256-row tiles
+        for mb, nb, wk, wn in ((8, 8, 2, 4), (4, 8, 2, 2), (8, 4, 2, 2)):
+            cands.append(dict(mb=mb, nb=nb, wn=wn, wk=wk, splits=1, amode=6, finish=0))
     out = []
     for p in cands:
         try:
@@ -805,21 +811,25 @@ def regret_candidates(B, M, N, K):
     return out
 
 
-def plan_regret(torch, B, inputs, only=None, out=None):
+def plan_regret(torch, B, inputs, only=None, out=None, large=False):
     """Graph-replay GPU time per call of the library's plan and of the
     candidate plans for every grid shape (weights rotating over copies
     >= 256 MiB).  With `out`, every candidate's time goes to that JSON file
     (a part, for --regret-merge); else the summary goes to
-    profiles/plan_regret.*."""
+    profiles/plan_regret.*.  With `large`, the shapes are LARGE_REGRET_PAIRS x
+    LARGE_REGRET_M and the summary goes to profiles/plan_regret_large.*."""
     dev = "cuda:0"
     results = []
     pairs = GRID_DIM_PAIRS if only is None else [GRID_DIM_PAIRS[i] for i in only]
+    batches = GRID_BATCH
+    if large:
+        pairs, batches = LARGE_REGRET_PAIRS, LARGE_REGRET_M
     for (N, K) in pairs:
         gen = torch.Generator("cpu").manual_seed(5000 + N + K)
         P0 = B.mx_pack_weight(inputs.bf16_randn(N, K, gen).to(dev))
         copies = min(200, max(4, -(-(256 << 20) // P0.numel())))
         Ps = [P0] + [P0.clone() for _ in range(copies - 1)]
-        for M in GRID_BATCH:
+        for M in batches:
             A0 = inputs.bf16_randn(M, K, gen).to(dev)
             C0 = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             lib_plan = B.mx_gemm_plan(M, N, K)
@@ -849,15 +859,29 @@ def plan_regret(torch, B, inputs, only=None, out=None):
     if out:
         with open(out, "w") as f:
             json.dump({"shapes": results}, f)
-    else:
+    if large:
+        regret_summary(results, "`python3 bench.py --plan-regret-large`", large=True)
+    elif not out:
         regret_summary(results, "`python3 bench.py --plan-regret`")
 
 
-def regret_summary(results, command):
+def regret_summary(results, command, large=False):
     """profiles/plan_regret.md and .json from the timed shapes (without the
-    per-candidate times)."""
+    per-candidate times); with `large`, profiles/plan_regret_large.*."""
     regrets = [r["regret"] for r in results]
     geo = float(np.exp(np.mean(np.log(regrets)))) if regrets else float("nan")
+    if large:
+        lines = ["# Planner regret at large M", "",
+                 "%s: for each of the %d shapes (M = %s x six (N, K) weight shapes of the pages' grid; the grid "
+                 "itself stops at M = 256), the HIP-graph-replay GPU time per call of the plan mx_gemm picks "
+                 "against the fastest of up to %d candidate plans (those of the grid sweep plus the tile mode's "
+                 "three tiles), weights rotating over copies of >= 256 MiB. Regret = plan time / best time; "
+                 "geometric mean %.3f, worst %.3f." % (
+                     command, len(results), ", ".join(str(m) for m in LARGE_REGRET_M),
+                     max((r["candidates"] for r in results), default=0), geo, max(regrets, default=0)),
+                 "", "| M | N | K | plan (mb nb wn wk splits amode) | us | best plan | best us | regret |",
+                 "|---|---|---|---|---|---|---|---|"]
+        return _regret_tables(results, lines, geo, "plan_regret_large")
     lines = ["# Planner regret on the pages' shape grid", "",
              "%s: for each of the %d shapes (19 (N, K) weight shapes of the "
              "kernelindex.com amd-mxfp4-mm pages' synthesized config CSV, submission 754569, times M = 1 .. 256), "
@@ -871,14 +895,18 @@ def regret_summary(results, command):
              "", "| M | N | K | plan (mb nb wn wk splits amode) | us | best plan | best us | regret |",
              "|---|---|---|---|---|---|---|---|"]
 
+    return _regret_tables(results, lines, geo, "plan_regret")
+
+
+def _regret_tables(results, lines, geo, stem):
     def ps(p):
         return "%d %d %d %d %d %d" % (p["mb"], p["nb"], p["wn"], p["wk"], p["splits"], p["amode"])
     for r in results:
         lines.append("| %d | %d | %d | %s | %.3f | %s | %.3f | %.3f |" % (
             r["M"], r["N"], r["K"], ps(r["plan"]), r["us"], ps(r["best_plan"]), r["best_us"], r["regret"]))
-    with open(os.path.join(ROOT, "profiles", "plan_regret.md"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", stem + ".md"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    with open(os.path.join(ROOT, "profiles", "plan_regret.json"), "w") as f:
+    with open(os.path.join(ROOT, "profiles", stem + ".json"), "w") as f:
         json.dump({"geomean_regret": geo, "shapes": [{k: v for k, v in r.items() if k != "all"} for r in results]},
                   f, indent=0)
         f.write("\n")
@@ -927,6 +955,9 @@ def main():
     ap.add_argument("--plan-regret", nargs="?", const="all", default=None, metavar="PAIRS",
                     help="time the library's plan against candidate plans on the pages' shape grid (PAIRS: "
                          "comma-separated indices of the (N, K) pairs, default all) and write profiles/plan_regret.*")
+    ap.add_argument("--plan-regret-large", action="store_true",
+                    help="the same at M = 256 .. 2048 over six of the grid's weight shapes, tile plans among the "
+                         "candidates; writes profiles/plan_regret_large.*")
     ap.add_argument("--regret-out", default=None, metavar="JSON",
                     help="with --plan-regret: write every candidate's time to JSON (a part for --regret-merge) "
                          "instead of profiles/plan_regret.*")
@@ -973,6 +1004,9 @@ def main():
     if args.plan_regret:
         only = None if args.plan_regret == "all" else [int(i) for i in args.plan_regret.split(",")]
         plan_regret(torch, B, inputs, only, args.regret_out)
+        return
+    if args.plan_regret_large:
+        plan_regret(torch, B, inputs, out=args.regret_out, large=True)
         return
 
     per_workload = {}

@@ -128,7 +128,8 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 
 // Model for shapes without a table entry, fitted to the plan-regret sweep
 // over the pages' shape grid (19 (N, K) weight shapes x M = 1 .. 256, up to
-// 69 candidate plans each):
+// 69 candidate plans each) and to a sweep of M = 256 .. 2048 over six of its
+// weight shapes with the tile mode's plans among the candidates:
 //   - deep K (more than 64 steps) with one 32-row block of M, or up to four
 //     at N <= 2112: the quantiser-wave mode with 4 quantiser waves and K
 //     split into pieces of at most 16 steps (7 splits at K = 7168), three
@@ -141,22 +142,27 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 //   - the activation is quantised once per workgroup by quantiser waves for
 //     three or four MFMA waves when M has at least eight 32-row blocks (or
 //     four, with K <= 512 or N >= 7168; or two, with both) and K is at most
-//     24 steps;
+//     24 steps (eight quantiser waves, four for K <= 512 from 12 to 31 M
+//     blocks);
 //   - else it is quantised in a first kernel when M has four or more 32-row
 //     blocks and K more than 8 steps, unless M is exactly four blocks with
 //     N < 7168 and K <= 2048: every wave of every N tile would otherwise
 //     quantise it again, which costs more vector-ALU time than the launch;
-//     there, two M blocks per wave and two waves along N (one for deep K);
+//     there, two M blocks per wave and two waves along N (one for deep K,
+//     and from 12 M blocks below N = 7168);
 //   - otherwise each wave quantises its own fragments: two N blocks per wave
 //     from four M blocks on, from two at N >= 7168, and for deep K;
 //   - 8 waves along K (4 for K <= 512), and K split over workgroups only as
 //     far as the register budget needs, except that deep K with the register
 //     mode takes at least 2 splits: the N tiles alone leave most CUs idle.
-//   - large MFMA work (M >= 384 and 2MNK >= 32 GFLOP; M >= 512, N >= 4096
-//     and 16 GFLOP; or M >= 1024, K >= 1024 and 12 GFLOP, from a sweep of
-//     M = 256 .. 2048 over seven weight shapes): the tile mode, a 256 x 256
-//     workgroup tile when that grid has at least 200 workgroups, else
-//     256 x 128 (more workgroups; with few, each waits on memory latency).
+//   - large MFMA work takes the tile mode (from a sweep of M = 256 .. 2048
+//     over six weight shapes): with K >= 4096, from M = 384 at 2MNK >=
+//     12.5 GFLOP, or from M = 256 at N >= 7168 (a round of the tile grid
+//     walks all K steps, ~0.27 us each, so deep K needs the work to pay for
+//     them); with a shorter K, from M = 256 at 2MNK >= 5.5 GFLOP + 1.2 MFLOP
+//     per unit of K.  A 256 x 256 workgroup tile when that grid has at
+//     least 200 workgroups, else 256 x 128 (128 x 256 measured the same to
+//     within run-to-run noise).
 // A deep-K or tile plan that the layout refuses for a shape (a split count
 // past the partials' 32-bit range, say) falls through to the rules after it.
 Plan model_plan(int M, int N, int K) {
@@ -166,8 +172,9 @@ Plan model_plan(int M, int N, int K) {
     const bool deep = KS > 64;
     Layout l;
     const double flops = 2.0 * M * N * K;
-    if ((M >= 384 && flops >= 32e9) || (M >= 512 && N >= 4096 && flops >= 16e9) ||
-        (M >= 1024 && K >= 1024 && flops >= 12e9)) {
+    const bool tile = K >= 4096 ? (M >= 384 && flops >= 12.5e9) || (M >= 256 && N >= 7168)
+                                : M >= 256 && flops >= 5.5e9 + 1.2e6 * K;
+    if (tile) {
         const long long wgs88 = (long long)((RBm + 7) / 8) * ((RBn + 7) / 8);
         const Plan q = wgs88 >= 200 ? Plan{8, 8, 4, 2, 1, kAmTile, 0} : Plan{8, 4, 2, 2, 1, kAmTile, 0};
         if (plan_layout(q, M, N, K, &l) == MX_OK) return q;
@@ -197,19 +204,21 @@ Plan model_plan(int M, int N, int K) {
     p.splits = 1;
     p.wk = KS <= 8 ? pow2_floor(KS >= 8 ? 4 : (KS + 1) / 2) : 8;
     if (shared) {
-        // three MFMA waves when the N blocks divide by 3 (no ragged tile), else four
+        // three MFMA waves when the N blocks divide by 3 (no ragged tile),
+        // else four; four quantiser waves for a short K from 12 to 31 M blocks
         p.amode = kAmShared;
         p.mb = 1;
         p.nb = 1;
         p.wn = RBn % 3 == 0 ? 3 : 4;
-        p.wk = 8;
+        p.wk = KS <= 8 && RBm >= 12 && RBm < 32 ? 4 : 8;
         return p;
     }
     if (pre) {
+        // one N block per wave for deep K, and from 12 M blocks below N = 7168
         p.amode = kAmPrequant;
         p.mb = 2;
         p.nb = 1;
-        p.wn = deep ? 1 : 2;
+        p.wn = deep || (RBm >= 12 && N < 7168) ? 1 : 2;
     } else {
         p.amode = kAmDirect;
         p.mb = 1;
