@@ -49,14 +49,17 @@ int mxhw_mfma_fp4(const void* a_dev, const void* b_dev, const void* sa_dev, cons
 int mxhw_stream_read(const void* buf_dev, unsigned bytes, int wgs, int waves, int lpl,
                      unsigned chunk, unsigned stride, unsigned rot, void* out_dev, void* stream);
 
-/* Host only, no GPU call: the placement of the shared-mode GEMM's tiles on
- * the 8 XCDs, by the library's own code.  For a one-split grid of mtiles x
- * ntiles workgroups (at most 2^20) of `cols` weight columns over K,
+/* Host only, no GPU call: the placement of the GEMM's workgroup tiles on
+ * the 8 XCDs (shared and tile modes), by the library's own code.  For a
+ * one-split grid of mtiles x ntiles workgroups (at most 2^20) whose M tile
+ * costs an XCD's L2 a_tile_bytes of fetch and whose N tile b_tile_bytes,
+ * with at most `conc` workgroups of an XCD running at once (0: all of them),
  * *map_out receives the placement code the kernel gets, and mt_out[lin] and
  * nt_out[lin] (host arrays of mtiles * ntiles ints) the M and N tile of the
  * workgroup with linear id lin = bx + ntiles * by.  Returns 0, or -1 for a
- * bad size or null pointer. */
-int mxhw_xcd_map(int mtiles, int ntiles, int splits, int K, int cols, int* map_out, int* mt_out, int* nt_out);
+ * bad size, byte count or null pointer. */
+int mxhw_xcd_map(int mtiles, int ntiles, int splits, double a_tile_bytes, double b_tile_bytes, int conc,
+                 int* map_out, int* mt_out, int* nt_out);
 
 #ifdef __cplusplus
 }

@@ -142,11 +142,12 @@ int mxhw_mfma_fp4(const void* a_dev, const void* b_dev, const void* sa_dev, cons
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int mxhw_xcd_map(int mtiles, int ntiles, int splits, int K, int cols, int* map_out, int* mt_out, int* nt_out) {
-    if (mtiles < 1 || ntiles < 1 || (long long)mtiles * ntiles > (1 << 20) || splits < 1 || K < 1 || cols < 1 ||
-        !map_out || !mt_out || !nt_out)
+int mxhw_xcd_map(int mtiles, int ntiles, int splits, double a_tile_bytes, double b_tile_bytes, int conc,
+                 int* map_out, int* mt_out, int* nt_out) {
+    if (mtiles < 1 || ntiles < 1 || (long long)mtiles * ntiles > (1 << 20) || splits < 1 || !(a_tile_bytes > 0.0) ||
+        !(b_tile_bytes > 0.0) || conc < 0 || !map_out || !mt_out || !nt_out)
         return -1;
-    const int map = mx4::shared_xcd_map(mtiles, ntiles, splits, 64.0 * K, cols * (K / 2.0 + K / 32.0));
+    const int map = mx4::shared_xcd_map(mtiles, ntiles, splits, a_tile_bytes, b_tile_bytes, conc);
     *map_out = map;
     for (int by = 0; by < mtiles; ++by)
         for (int bx = 0; bx < ntiles; ++bx) {

@@ -545,28 +545,19 @@ def xcd_fetch_cost(mt, nt, K, cols):
 
 
 def test_shared_xcd_map_places_every_tile_once_and_fetches_no_more():
-    """The shared-mode GEMM's placement of tiles on the XCDs (library code,
-    through libmx4hw.so's host-only hook): every (M tile, N tile) goes to
-    exactly one workgroup for every grid, the dispatcher's order is kept
-    where no rectangle fits, the chosen placement never makes the XCDs fetch
-    more than the dispatcher's order would, and 256 x 3072 x 1536 (8 x 32
-    tiles of 96 columns) gets 4 M tiles x 8 N tiles per XCD."""
-    hwlib = os.path.join(ROOT, "microscaled_mxfp4_block_amd", "libmx4hw.so")
-    hw = ctypes.CDLL(hwlib)
-    I, P = ctypes.c_int, ctypes.c_void_p
-    hw.mxhw_xcd_map.argtypes = [I, I, I, I, I, P, P, P]
-
-    def place(mtiles, ntiles, splits, K, cols):
-        T = mtiles * ntiles
-        mt, nt, mp = (ctypes.c_int * T)(), (ctypes.c_int * T)(), ctypes.c_int(-1)
-        assert hw.mxhw_xcd_map(mtiles, ntiles, splits, K, cols, ctypes.byref(mp), mt, nt) == 0
-        return mp.value, np.frombuffer(mt, np.int32).copy(), np.frombuffer(nt, np.int32).copy()
-
+    """The GEMM's placement of tiles on the XCDs (library code, through
+    libmx4hw.so's host-only hook), as the shared mode uses it (all
+    workgroups resident at once): every (M tile, N tile) goes to exactly one
+    workgroup for every grid, the dispatcher's order is kept where no
+    rectangle fits, the chosen placement never makes the XCDs fetch more
+    than the dispatcher's order would, and 256 x 3072 x 1536 (8 x 32 tiles of
+    96 columns) gets 4 M tiles x 8 N tiles per XCD."""
+    place = xcd_placer()
     remapped = 0
     for mtiles in (1, 2, 3, 4, 5, 6, 8, 12, 16, 32):
         for ntiles in range(1, 66):
             for K, cols in ((1536, 96), (512, 128), (7168, 64)):
-                mp, mt, nt = place(mtiles, ntiles, 1, K, cols)
+                mp, mt, nt = place(mtiles, ntiles, 1, 64.0 * K, cols * (K / 2 + K / 32), 0)
                 T = mtiles * ntiles
                 assert mt.min() >= 0 and mt.max() < mtiles and nt.min() >= 0 and nt.max() < ntiles
                 assert np.unique(mt.astype(np.int64) * ntiles + nt).size == T, (mtiles, ntiles, mp)
@@ -579,12 +570,75 @@ def test_shared_xcd_map_places_every_tile_once_and_fetches_no_more():
                     assert T % 8 == 0
                     assert xcd_fetch_cost(mt, nt, K, cols) <= xcd_fetch_cost(d_mt, d_nt, K, cols) + 1e-6
     assert remapped > 100
-    mp, mt, nt = place(8, 32, 1, 1536, 96)
+    mp, mt, nt = place(8, 32, 1, 64.0 * 1536, 96 * (1536 / 2 + 1536 / 32), 0)
     for x in range(8):
         sel = np.arange(256) % 8 == x
         assert np.unique(mt[sel]).size == 4 and np.unique(nt[sel]).size == 8
-    assert place(8, 32, 2, 1536, 96)[0] == 0       # K splits keep the dispatcher's order
-    assert hw.mxhw_xcd_map(0, 32, 1, 1536, 96, None, None, None) == -1
+    assert place(8, 32, 2, 64.0 * 1536, 96 * 816.0, 0)[0] == 0       # K splits keep the dispatcher's order
+    assert B_hw().mxhw_xcd_map(0, 32, 1, 1.0, 1.0, 0, None, None, None) == -1
+
+
+def B_hw():
+    hw = ctypes.CDLL(os.path.join(ROOT, "microscaled_mxfp4_block_amd", "libmx4hw.so"))
+    I, P, D = ctypes.c_int, ctypes.c_void_p, ctypes.c_double
+    hw.mxhw_xcd_map.argtypes = [I, I, I, D, D, I, P, P, P]
+    return hw
+
+
+def xcd_placer():
+    hw = B_hw()
+
+    def place(mtiles, ntiles, splits, a_bytes, b_bytes, conc):
+        T = mtiles * ntiles
+        mt, nt, mp = (ctypes.c_int * T)(), (ctypes.c_int * T)(), ctypes.c_int(-1)
+        assert hw.mxhw_xcd_map(mtiles, ntiles, splits, a_bytes, b_bytes, conc, ctypes.byref(mp), mt, nt) == 0
+        return mp.value, np.frombuffer(mt, np.int32).copy(), np.frombuffer(nt, np.int32).copy()
+    return place
+
+
+def round_fetch_cost(mt, nt, a_bytes, b_bytes, conc):
+    """Bytes the XCDs' L2s fetch when each XCD runs its workgroups (linear id
+    x mod 8) in dispatch order, conc at a time: per round, its distinct M
+    tiles times a_bytes plus its distinct N tiles times b_bytes."""
+    lin = np.arange(mt.size)
+    cost = 0.0
+    for x in range(8):
+        idx = lin[lin % 8 == x]
+        for r in range(0, idx.size, conc):
+            sel = idx[r:r + conc]
+            cost += np.unique(mt[sel]).size * a_bytes + np.unique(nt[sel]).size * b_bytes
+    return cost
+
+
+def test_tile_xcd_map_scores_rounds_when_an_xcd_runs_its_tiles_in_turn():
+    """The tile mode's placement (at most 32 workgroups of an XCD at once):
+    every tile goes to exactly one workgroup, and where the grid runs in
+    several rounds per XCD the chosen rectangle fetches, round by round as
+    the dispatcher runs them, no more than the rectangle chosen for an
+    all-resident grid; at 8192^3 (32 x 32 tiles of 256 x 256, equal bytes)
+    each XCD takes 8 M tiles x 16 N tiles, so each round covers 8 x 4."""
+    place = xcd_placer()
+    checked = 0
+    for mtiles in (4, 8, 16, 32, 64):
+        for ntiles in (8, 16, 24, 28, 32, 56, 64):
+            for a_bytes, b_bytes in ((1.0, 1.0), (2.0, 1.0), (1.0, 2.0)):
+                mp, mt, nt = place(mtiles, ntiles, 1, a_bytes, b_bytes, 32)
+                T = mtiles * ntiles
+                assert np.unique(mt.astype(np.int64) * ntiles + nt).size == T, (mtiles, ntiles, mp)
+                if T <= 8 * 32:
+                    continue
+                mp0, mt0, nt0 = place(mtiles, ntiles, 1, a_bytes, b_bytes, 0)
+                assert round_fetch_cost(mt, nt, a_bytes, b_bytes, 32) <= \
+                    round_fetch_cost(mt0, nt0, a_bytes, b_bytes, 32) + 1e-9, (mtiles, ntiles, a_bytes, b_bytes)
+                checked += 1
+    assert checked > 30
+    mp, mt, nt = place(32, 32, 1, 1.0, 1.0, 32)
+    for x in range(8):
+        sel = np.arange(1024) % 8 == x
+        assert np.unique(mt[sel]).size == 8 and np.unique(nt[sel]).size == 16
+        first = np.arange(1024)[sel][:32]
+        assert np.unique(mt[first]).size == 8 and np.unique(nt[first]).size == 4
+    assert round_fetch_cost(mt, nt, 1.0, 1.0, 32) < round_fetch_cost(*place(32, 32, 1, 1.0, 1.0, 0)[1:], 1.0, 1.0, 32)
 
 
 def test_noalloc_validates_before_any_hip_call():

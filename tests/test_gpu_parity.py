@@ -276,7 +276,8 @@ PLANS = [
     dict(mb=8, nb=4, wn=2, wk=2, splits=1, amode=6),
 ]
 
-LARGE_M_SHAPES = [(1024, 4096, 4096), (2048, 7168, 2048), (384, 7168, 7168), (777, 4100, 4160)]
+# (8192 x 8192 x 512: a 32 x 32 grid of 256 x 256 tiles, four rounds per XCD, placed per round)
+LARGE_M_SHAPES = [(1024, 4096, 4096), (2048, 7168, 2048), (384, 7168, 7168), (777, 4100, 4160), (8192, 8192, 512)]
 
 
 @pytest.mark.parametrize("shape", LARGE_M_SHAPES, ids=lambda s: "x".join(map(str, s)))
