@@ -22,9 +22,10 @@
 // MFMAs from LDS and a wave's LDS reads overlap its MFMAs.  Every wave issues the
 // same number of loads per step (steps past K load from an offset past the
 // buffer and read zeros), so the wait for a step is a compile-time count.
-// One barrier per step, with no memory fence (a fence would wait for the
-// loads of the steps in flight), tells the waves that every wave's loads of
-// the step have landed and that the stage of the previous step is free.
+// One barrier every G steps, with no memory fence (a fence would wait for
+// the loads of the steps in flight), tells the waves that every wave's loads
+// of the next G steps have landed and that the stages of the steps already
+// read are free.
 // The epilogue stages each wave's bf16 tiles in the (then dead) ring and
 // stores them in 16-byte row chunks.
 #include "mx4_device.h"
@@ -38,9 +39,10 @@ constexpr int kTileOpBytes = 1024;   // one packed operand tile: 64 lanes x 16 B
 constexpr int kTileWordBytes = 256;  // one packed scale word group: 64 lanes x 4 B
 
 // Scale word groups (4 steps each) the ring holds with S tile stages.  The
-// words of group h + W are issued with the tiles of step 4 (h + W), at step
-// 4 (h + W) - S, after that step's barrier; group h's words were last read
-// from LDS at step 4 h - 1, so W slots suffice once 4 W >= S.
+// words of group h + W are issued with the tiles of step 4 (h + W), after the
+// barrier of step 4 (h + W) - S or a later one; group h's words were last
+// read from LDS at step 4 h - 1, before the barrier of step 4 h, so W slots
+// suffice once 4 W >= S.
 __host__ __device__ constexpr int tile_word_slots(int s) { return (s + 3) / 4; }
 
 // LDS of a kernel with S tile stages: S stages of the step's MB + NB operand
