@@ -550,6 +550,83 @@ def summarize_profiles(trace_dir, fetch_dir, write_dir, mfma_dir, calls):
 
 
 # ---------------------------------------------------------------------------
+# The other entry points on the path: the one-time weight pack, the standalone
+# activation quantiser and the weight import, each an HBM-bound kernel.
+
+SIDE_SHAPES = [(8192, 8192)]   # rows x K past the workloads, where the launch no longer dominates
+
+
+def measure_side_ops(torch, B, inputs):
+    """GPU time per call of mx_quant_act on each workload's A, and of
+    mx_pack_weight and mx_import_weight on each workload's B, with GB/s of
+    the bytes each call must move against 8 TB/s; the same on an
+    8192 x 8192 operand.  Cold: the calls rotate over copies of their
+    inputs and outputs (>= 512 MiB together), graph-replayed back to back."""
+    L = B.lib()
+    dev = "cuda:0"
+    out = {}
+
+    def rec(nbytes, us):
+        return {"gpu_us": round(us, 3), "bytes": nbytes, "gbps": round(nbytes / us / 1e3, 1),
+                "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+
+    def ncopies(per_set):
+        return min(MAX_COPIES, max(2, -(-COLD_BYTES // per_set)))
+    shapes = [(w.name, w.M, w.N, w.K, i) for i, w in enumerate(inputs.WORKLOADS)]
+    shapes += [("%dx%d" % (r, k), r, r, k, None) for r, k in SIDE_SHAPES]
+    for name, M, N, K, idx in shapes:
+        if idx is not None:
+            A0, B0 = inputs.workload_inputs(idx, 1000)
+        else:
+            A0, B0 = inputs.shape_inputs(M, N, K, seed=1000)
+        A0, B0 = A0.to(dev), B0.to(dev)
+        P0 = B.mx_pack_weight(B0)
+        bc0, bs0 = B.mx_unpack_weight(P0, N, K)
+        qa_bytes = 2 * M * K + M * K // 2 + M * K // 32
+        pk_bytes = 2 * N * K + P0.numel()
+        im_bytes = bc0.numel() + bs0.numel() + P0.numel()
+        res = {}
+        # activation quantiser: A copies in, natural codes and scales out
+        n = ncopies(qa_bytes)
+        As = [A0] + [A0.clone() for _ in range(n - 1)]
+        cs = [torch.empty((M, K // 2), dtype=torch.uint8, device=dev) for _ in range(n)]
+        ss = [torch.empty((M, K // 32), dtype=torch.uint8, device=dev) for _ in range(n)]
+
+        def quant(i, st):
+            k = i % n
+            if L.mx_quant_act(As[k].data_ptr(), M, K, K, cs[k].data_ptr(), ss[k].data_ptr(), st):
+                raise RuntimeError("mx_quant_act failed")
+        res["mx_quant_act"] = rec(qa_bytes, graph_time(torch, quant, max(n, 20)))
+        del As, cs, ss
+        # weight pack: B copies in, packed copies out
+        n = ncopies(pk_bytes)
+        Bs = [B0] + [B0.clone() for _ in range(n - 1)]
+        Ps = [torch.empty_like(P0) for _ in range(n)]
+
+        def pack(i, st):
+            k = i % n
+            if L.mx_pack_weight(Bs[k].data_ptr(), N, K, K, Ps[k].data_ptr(), Ps[k].numel(), st):
+                raise RuntimeError("mx_pack_weight failed")
+        res["mx_pack_weight"] = rec(pk_bytes, graph_time(torch, pack, max(n, 20)))
+        del Bs
+        # weight import: natural codes and scales in, packed out
+        n = min(n, ncopies(im_bytes))
+        bcs = [bc0] + [bc0.clone() for _ in range(n - 1)]
+        bss = [bs0] + [bs0.clone() for _ in range(n - 1)]
+
+        def imp(i, st):
+            k = i % n
+            if L.mx_import_weight(bcs[k].data_ptr(), bss[k].data_ptr(), N, K, Ps[k].data_ptr(), Ps[k].numel(), st):
+                raise RuntimeError("mx_import_weight failed")
+        res["mx_import_weight"] = rec(im_bytes, graph_time(torch, imp, max(n, 20)))
+        out[name] = res
+        print(json.dumps({"side_ops " + name: res}), file=sys.stderr, flush=True)
+        del bcs, bss, Ps, A0, B0, P0, bc0, bs0
+        torch.cuda.empty_cache()
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Large M: shapes where the contraction, not the weight stream, bounds the
 # call (the tile mode's regime).  One set of buffers per shape, called back to
 # back (at these sizes a call does far more MFMA work than it moves bytes).
@@ -1072,6 +1149,13 @@ def main():
         },
         "per_workload": per_workload,
     }
+    if not args.only_headline:
+        line["side_ops"] = {
+            "note": "the other entry points on the path, GPU us per call in HIP graph replay of back-to-back calls "
+                    "over rotating copies (>= 512 MiB, cold): mx_quant_act on A (bytes 2MK in + MK/2 + MK/32 out), "
+                    "mx_pack_weight on B (2NK in + the packed bytes out), mx_import_weight (natural codes and "
+                    "scales in + the packed bytes out); GB/s of those bytes against 8 TB/s",
+            "shapes": measure_side_ops(torch, B, inputs)}
     if not args.no_large_m and not args.only_headline:
         line["large_m"] = {
             "note": "MFMA-bound shapes (tile mode): GPU us per mx_gemm call in HIP graph replay of 20 back-to-back "
