@@ -984,9 +984,8 @@ def _regret_tables(results, lines, geo, stem):
     with open(os.path.join(ROOT, "profiles", stem + ".md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(os.path.join(ROOT, "profiles", stem + ".json"), "w") as f:
-        json.dump({"geomean_regret": geo, "shapes": [{k: v for k, v in r.items() if k != "all"} for r in results]},
-                  f, indent=0)
-        f.write("\n")
+        shapes = [json.dumps({k: v for k, v in r.items() if k != "all"}, separators=(",", ":")) for r in results]
+        f.write('{"geomean_regret": %s, "shapes": [\n%s\n]}\n' % (json.dumps(geo), ",\n".join(shapes)))
     print("\n".join(lines))
 
 
