@@ -893,8 +893,8 @@ def plan_regret(torch, B, inputs, only=None, out=None, large=False):
     candidate plans for every grid shape (weights rotating over copies
     >= 256 MiB).  With `out`, every candidate's time goes to that JSON file
     (a part, for --regret-merge); else the summary goes to
-    profiles/plan_regret.*.  With `large`, the shapes are LARGE_REGRET_PAIRS x
-    LARGE_REGRET_M and the summary goes to profiles/plan_regret_large.*."""
+    profiles/plan_regret.md.  With `large`, the shapes are LARGE_REGRET_PAIRS x
+    LARGE_REGRET_M and the summary goes to profiles/plan_regret_large.md."""
     dev = "cuda:0"
     results = []
     pairs = GRID_DIM_PAIRS if only is None else [GRID_DIM_PAIRS[i] for i in only]
@@ -943,8 +943,8 @@ def plan_regret(torch, B, inputs, only=None, out=None, large=False):
 
 
 def regret_summary(results, command, large=False):
-    """profiles/plan_regret.md and .json from the timed shapes (without the
-    per-candidate times); with `large`, profiles/plan_regret_large.*."""
+    """profiles/plan_regret.md from the timed shapes (without the
+    per-candidate times); with `large`, profiles/plan_regret_large.md."""
     regrets = [r["regret"] for r in results]
     geo = float(np.exp(np.mean(np.log(regrets)))) if regrets else float("nan")
     if large:
@@ -958,7 +958,7 @@ def regret_summary(results, command, large=False):
                      max((r["candidates"] for r in results), default=0), geo, max(regrets, default=0)),
                  "", "| M | N | K | plan (mb nb wn wk splits amode) | us | best plan | best us | regret |",
                  "|---|---|---|---|---|---|---|---|"]
-        return _regret_tables(results, lines, geo, "plan_regret_large")
+        return _regret_tables(results, lines, "plan_regret_large")
     lines = ["# Planner regret on the pages' shape grid", "",
              "%s: for each of the %d shapes (19 (N, K) weight shapes of the "
              "kernelindex.com amd-mxfp4-mm pages' synthesized config CSV, submission 754569, times M = 1 .. 256), "
@@ -972,10 +972,10 @@ def regret_summary(results, command, large=False):
              "", "| M | N | K | plan (mb nb wn wk splits amode) | us | best plan | best us | regret |",
              "|---|---|---|---|---|---|---|---|"]
 
-    return _regret_tables(results, lines, geo, "plan_regret")
+    return _regret_tables(results, lines, "plan_regret")
 
 
-def _regret_tables(results, lines, geo, stem):
+def _regret_tables(results, lines, stem):
     def ps(p):
         return "%d %d %d %d %d %d" % (p["mb"], p["nb"], p["wn"], p["wk"], p["splits"], p["amode"])
     for r in results:
@@ -983,9 +983,6 @@ def _regret_tables(results, lines, geo, stem):
             r["M"], r["N"], r["K"], ps(r["plan"]), r["us"], ps(r["best_plan"]), r["best_us"], r["regret"]))
     with open(os.path.join(ROOT, "profiles", stem + ".md"), "w") as f:
         f.write("\n".join(lines) + "\n")
-    with open(os.path.join(ROOT, "profiles", stem + ".json"), "w") as f:
-        shapes = [json.dumps({k: v for k, v in r.items() if k != "all"}, separators=(",", ":")) for r in results]
-        f.write('{"geomean_regret": %s, "shapes": [\n%s\n]}\n' % (json.dumps(geo), ",\n".join(shapes)))
     print("\n".join(lines))
 
 
@@ -1030,15 +1027,15 @@ def main():
                     help="no GPU: summarise the rocprofv3 output of --profile-large-m runs into profiles/")
     ap.add_argument("--plan-regret", nargs="?", const="all", default=None, metavar="PAIRS",
                     help="time the library's plan against candidate plans on the pages' shape grid (PAIRS: "
-                         "comma-separated indices of the (N, K) pairs, default all) and write profiles/plan_regret.*")
+                         "comma-separated indices of the (N, K) pairs, default all) and write profiles/plan_regret.md")
     ap.add_argument("--plan-regret-large", action="store_true",
                     help="the same at M = 256 .. 2048 over six of the grid's weight shapes, tile plans among the "
-                         "candidates; writes profiles/plan_regret_large.*")
+                         "candidates; writes profiles/plan_regret_large.md")
     ap.add_argument("--regret-out", default=None, metavar="JSON",
                     help="with --plan-regret: write every candidate's time to JSON (a part for --regret-merge) "
-                         "instead of profiles/plan_regret.*")
+                         "instead of profiles/plan_regret.md")
     ap.add_argument("--regret-merge", nargs="+", metavar="JSON",
-                    help="no GPU: profiles/plan_regret.* from --regret-out parts (in grid order)")
+                    help="no GPU: profiles/plan_regret.md from --regret-out parts (in grid order)")
     ap.add_argument("--stats-md", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="no GPU: profiles/bench_kernel_stats.md from a rocprofv3 --stats kernel_stats.csv")
     args = ap.parse_args()
