@@ -54,3 +54,25 @@ def test_noalloc_matches_mx_gemm_two_calls():
         assert tol_ok(g, oracle.gemm(inputs.bits(A), inputs.bits(Bm)))
         results.append(g)
     assert len(results) == 2
+
+
+# two large-M calls that the planner sends to the tile mode (the activation
+# pre-quantised into the scratch array), the second on a smaller input
+TILE_SEQUENCE = [(1024, 4096, 1024), (896, 4096, 1024)]
+
+
+def test_noalloc_tile_mode_matches_mx_gemm():
+    for M, N, K in TILE_SEQUENCE:
+        assert B.mx_gemm_plan(M, N, K)["amode"] == B.MX_AMODE_TILE
+        assert 0 < B.mx_gemm_workspace_bytes(M, N, K) <= B.MX_NOALLOC_SCRATCH_BYTES
+    for i, (M, N, K) in enumerate(TILE_SEQUENCE):
+        say("noalloc tile call", i, (M, N, K), B.mx_gemm_plan(M, N, K))
+        A, Bm = inputs.shape_inputs(M, N, K, seed=700 + i)
+        Ad, packed = A.to(DEV), B.mx_pack_weight(Bm.to(DEV))
+        C_ref = B.mx_gemm(Ad, packed, N)
+        C_na = torch.full((M, N), -3.0, dtype=torch.bfloat16, device=DEV)
+        B.mx_gemm_noalloc(Ad, packed, N, C=C_na)
+        torch.cuda.synchronize()
+        g, r = inputs.bits(C_na.cpu()), inputs.bits(C_ref.cpu())
+        assert np.array_equal(g, r), "tile call %d differs from mx_gemm" % i
+        assert tol_ok(g, oracle.gemm(inputs.bits(A), inputs.bits(Bm)))
