@@ -368,12 +368,28 @@ def test_gemm_writes_nothing_outside_c(shape, plan):
     assert_c_close(gpu_bits(C), ref(inputs.bits(A), inputs.bits(Bm)), "%s %s" % (shape, plan_id(plan)))
 
 
-def test_gemm_binade_spread_and_strides():
+# one plan of every activation mode (None: the library's own) for strided A
+# and C: lda = K + 24 elements, ldc = N + 5
+STRIDE_PLANS = [None,
+                dict(mb=1, nb=2, wn=1, wk=4, splits=1, amode=0),
+                dict(mb=2, nb=1, wn=2, wk=2, splits=2, amode=1),
+                dict(mb=1, nb=1, wn=1, wk=4, splits=1, amode=2),
+                dict(mb=1, nb=2, wn=1, wk=4, splits=1, amode=4),
+                dict(mb=1, nb=1, wn=3, wk=4, splits=1, amode=5),
+                dict(mb=8, nb=4, wn=2, wk=2, splits=1, amode=6),
+                dict(mb=4, nb=8, wn=2, wk=2, splits=1, amode=6)]
+
+
+@pytest.mark.parametrize("plan", STRIDE_PLANS, ids=lambda p: "auto" if p is None else plan_id(p))
+def test_gemm_binade_spread_and_strides(plan):
     M, N, K = 19, 75, 640
+    if plan is not None and not plan_runs(M, N, K, plan):
+        pytest.skip("plan outside the register / LDS budget for this shape")
     A = inputs.binade_spread(M, K, seed=21, lo=-10, hi=10)
     Bm = inputs.binade_spread(N, K, seed=22, lo=-10, hi=10)
-    C = run_gemm(A, Bm, lda_pad=24, ldc_pad=5)
-    assert_c_close(C, oracle.gemm(inputs.bits(A), inputs.bits(Bm)), "binades")
+    say("gemm strides", "auto" if plan is None else plan_id(plan))
+    C = run_gemm(A, Bm, plan=plan, lda_pad=24, ldc_pad=5)
+    assert_c_close(C, oracle.gemm(inputs.bits(A), inputs.bits(Bm)), "binades %s" % plan)
 
 
 def test_gemm_closed_form_all_ones():
