@@ -575,10 +575,11 @@ def test_shared_xcd_map_places_every_tile_once_and_fetches_no_more():
         sel = np.arange(256) % 8 == x
         assert np.unique(mt[sel]).size == 4 and np.unique(nt[sel]).size == 8
     assert place(8, 32, 2, 64.0 * 1536, 96 * 816.0, 0)[0] == 0       # K splits keep the dispatcher's order
-    assert B_hw().mxhw_xcd_map(0, 32, 1, 1.0, 1.0, 0, None, None, None) == -1
+    assert placement_hook().mxhw_xcd_map(0, 32, 1, 1.0, 1.0, 0, None, None, None) == -1
 
 
-def B_hw():
+def placement_hook():
+    """libmx4hw.so with the argument types of its host-only placement hook."""
     hw = ctypes.CDLL(os.path.join(ROOT, "microscaled_mxfp4_block_amd", "libmx4hw.so"))
     I, P, D = ctypes.c_int, ctypes.c_void_p, ctypes.c_double
     hw.mxhw_xcd_map.argtypes = [I, I, I, D, D, I, P, P, P]
@@ -586,7 +587,7 @@ def B_hw():
 
 
 def xcd_placer():
-    hw = B_hw()
+    hw = placement_hook()
 
     def place(mtiles, ntiles, splits, a_bytes, b_bytes, conc):
         T = mtiles * ntiles
