@@ -687,7 +687,16 @@ def measure_large_m(torch, B, inputs):
         rec = {"plan": st["plan"], "launches_per_call": st["launches"], "gpu_us_per_call": round(us, 3),
                "tflops": round(flops / us / 1e6, 1), "fp4_mfma_frac": round(flops / us / 1e6 / FP4_PEAK_TFLOPS, 4)}
         if prof is not None and name in prof.get("shapes", {}):
-            rec["traced"] = prof["shapes"][name]
+            t = prof["shapes"][name]
+            rec["traced"] = t
+            gk = t.get("gemm_kernel")
+            if gk:
+                # the tile GEMM kernel against the dense fp4 MFMA peak (traced
+                # duration), with its counted HBM bytes
+                rec["roofline"] = {"bound": "mfma", "kernel": gk, "achieved": t["gemm_tflops_traced"],
+                                   "peak": FP4_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": t["gemm_fp4_frac_traced"],
+                                   "traffic": t["kernels"][gk]["hbm_bytes"],
+                                   "kernel_us_traced": t["kernels"][gk]["avg_us"]}
         out[name] = rec
         print(json.dumps({"large_m " + name: rec}), file=sys.stderr, flush=True)
         del st
