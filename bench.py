@@ -1117,7 +1117,7 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "baseline_note": "BASELINE.json publishes no figure; the pages' 16.2 us end-to-end for this shape "
+        "baseline_note": "no published figure for this metric and workload; the pages' 16.2 us end-to-end for this shape "
                          "(CK route, MI355X) is context only",
         "dtype": "mxfp4",
         "data": "synthetic",
