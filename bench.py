@@ -1117,8 +1117,8 @@ def main():
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,
-        "baseline_note": "no published figure for this metric and workload; the pages' 16.2 us end-to-end for this shape "
-                         "(CK route, MI355X) is context only",
+        "baseline_note": "no published figure for this metric and workload; the pages' 16.2 us end-to-end for "
+                         "this shape (CK route, MI355X) is context only",
         "dtype": "mxfp4",
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K": w.K, "plan": rec["plan"],
