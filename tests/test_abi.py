@@ -373,7 +373,8 @@ def test_shared_kernels_keep_weight_loads_in_flight_across_barriers():
         QW, KR = int(m.group(4)), int(m.group(5))
         KL = KR // QW
         body = [ln for ln in m.group(0).splitlines() if not ln.strip().startswith(";")]
-        dma = [k for k, ln in enumerate(body) if re.match(r"^\s*buffer_load_dwordx4\b", ln) and ln.rstrip().endswith(" lds")]
+        dma = [k for k, ln in enumerate(body)
+               if re.match(r"^\s*buffer_load_dwordx4\b", ln) and ln.rstrip().endswith(" lds")]
         bars = [k for k, ln in enumerate(body) if ln.strip() == "s_barrier"]
         assert len(dma) == (4 + 2 + 1) * KL and bars, name   # the 4-, 2- and 1-chunk copies
         b1 = next(k for k in bars if k > dma[-1])
@@ -745,8 +746,8 @@ def test_bench_large_m_summary_from_synthetic_rocprof_output(tmp_path):
                 # the calibration is the copy before the first library kernel)
                 big = si == len(shapes) - 1
                 d.append(("mx4::gemm_tile_kernel<8>(x)", 512, 10.0 * (si + 1) + c, {
-                    "FETCH_SIZE": 4 * copy_kib if big else 1000, "WRITE_SIZE": 4 * copy_kib if big else 2000, "SQ_INSTS_VALU_MFMA_MOPS_F6F4": 2.0 * M * N * K / 512,
-                    "SQ_VALU_MFMA_BUSY_CYCLES": 1.0e6}))
+                    "FETCH_SIZE": 4 * copy_kib if big else 1000, "WRITE_SIZE": 4 * copy_kib if big else 2000,
+                    "SQ_INSTS_VALU_MFMA_MOPS_F6F4": 2.0 * M * N * K / 512, "SQ_VALU_MFMA_BUSY_CYCLES": 1.0e6}))
             d.append(("mx4::hw_stream_kernel(z)", 64, 1.0, {}))
         return d
 
