@@ -864,6 +864,11 @@ LARGE_REGRET_PAIRS = [(4096, 512), (3072, 1536), (7168, 2048), (2880, 2048), (21
 LARGE_REGRET_M = [256, 384, 512, 768, 1024, 2048]
 
 
+# The tile mode's workgroup tiles: (mb, nb, wk, wn) = M blocks, N blocks,
+# waves along M, waves along N.
+TILE_SHAPES = ((8, 8, 2, 4), (4, 8, 2, 2), (8, 4, 2, 2), (4, 4, 2, 2), (4, 4, 2, 4), (2, 2, 2, 2))
+
+
 def regret_candidates(B, M, N, K):
     """Plans timed against the library's own for one grid shape: the
     register-quantising mode over wave and split counts and two N widths,
@@ -884,9 +889,10 @@ def regret_candidates(B, M, N, K):
         for wk in (4, 8):
             for sp in (1, 2, 4, 7, 8, 14):
                 cands.append(dict(mb=1, nb=1, wn=wn, wk=wk, splits=sp, amode=5, finish=0))
-    if M >= 256:   # the tile mode's 256-row tiles
-        for mb, nb, wk, wn in ((8, 8, 2, 4), (4, 8, 2, 2), (8, 4, 2, 2)):
-            cands.append(dict(mb=mb, nb=nb, wn=wn, wk=wk, splits=1, amode=6, finish=0))
+    if M >= 32:   # the tile mode over its tiles (64 .. 256 rows)
+        for mb, nb, wk, wn in TILE_SHAPES:
+            if 32 * mb <= 2 * max(M, 32):
+                cands.append(dict(mb=mb, nb=nb, wn=wn, wk=wk, splits=1, amode=6, finish=0))
     out = []
     for p in cands:
         try:
@@ -960,8 +966,8 @@ def regret_summary(results, command, large=False):
         lines = ["# Planner regret at large M", "",
                  "%s: for each of the %d shapes (M = %s x six (N, K) weight shapes of the pages' grid; the grid "
                  "itself stops at M = 256), the HIP-graph-replay GPU time per call of the plan mx_gemm picks "
-                 "against the fastest of up to %d candidate plans (those of the grid sweep plus the tile mode's "
-                 "three tiles), weights rotating over copies of >= 256 MiB. Regret = plan time / best time; "
+                 "against the fastest of up to %d candidate plans (those of the grid sweep, the tile mode's "
+                 "tiles among them), weights rotating over copies of >= 256 MiB. Regret = plan time / best time; "
                  "geometric mean %.3f, worst %.3f." % (
                      command, len(results), ", ".join(str(m) for m in LARGE_REGRET_M),
                      max((r["candidates"] for r in results), default=0), geo, max(regrets, default=0)),
@@ -974,7 +980,8 @@ def regret_summary(results, command, large=False):
              "the HIP-graph-replay GPU time per call of the plan mx_gemm picks (the measured table for the "
              "workloads, the model elsewhere) against the fastest of up to %d candidate plans (register-quantising "
              "mode over waves, splits and N widths; pre-quantising mode over its tiles; LDS mode; quantiser-wave "
-             "shared mode over its waves and splits), weights rotating over copies of >= 256 MiB. "
+             "shared mode over its waves and splits; from M = 32 the tile mode over its tiles), weights rotating "
+             "over copies of >= 256 MiB. "
              "Regret = plan time / best time; geometric mean %.3f, worst %.3f." % (
                  command, len(results), max((r["candidates"] for r in results), default=0), geo,
                  max(regrets, default=0)),

@@ -30,7 +30,7 @@ MX_AMODE_DIRECT = 2
 MX_AMODE_BF16 = 3          # A not quantised: the a16wfp4 product
 MX_AMODE_STREAM = 4        # per-wave quantisation in a K loop
 MX_AMODE_SHARED = 5        # quantiser waves into LDS for MFMA waves
-MX_AMODE_TILE = 6          # pre-quantised A, K-looped LDS-tiled GEMM (large M)
+MX_AMODE_TILE = 6          # pre-quantised A, K-looped LDS-tiled GEMM (M from 64)
 # split-K finishes of a plan
 MX_FINISH_KERNEL = 0
 MX_FINISH_LAST_ARRIVAL = 1

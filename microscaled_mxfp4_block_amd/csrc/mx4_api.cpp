@@ -155,14 +155,16 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 //   - 8 waves along K (4 for K <= 512), and K split over workgroups only as
 //     far as the register budget needs, except that deep K with the register
 //     mode takes at least 2 splits: the N tiles alone leave most CUs idle.
-//   - large MFMA work takes the tile mode (from a sweep of M = 256 .. 2048
-//     over six weight shapes): with K >= 4096, from M = 384 at 2MNK >=
-//     12.5 GFLOP, or from M = 256 at N >= 7168 (a round of the tile grid
-//     walks all K steps, ~0.27 us each, so deep K needs the work to pay for
-//     them); with a shorter K, from M = 256 at 2MNK >= 5.5 GFLOP + 1.2 MFLOP
-//     per unit of K.  A 256 x 256 workgroup tile when that grid has at
-//     least 200 workgroups, else 256 x 128 (128 x 256 measured the same to
-//     within run-to-run noise).
+//   - the tile mode (activation quantised once, K-looped tiles of both
+//     operands), from the sweeps over the grid and M = 256 .. 2048 with its
+//     tiles among the candidates: from M = 64; with K >= 4096 from M = 256,
+//     or at 2MNK >= 5 GFLOP from M = 128 or at N >= 7168; with K from 2048
+//     from M = 256, or from M = 128 at N >= 7168; with a shorter K from
+//     M = 256 at 2MNK >= 3 GFLOP + 0.5 MFLOP per unit of K.  The tile: the
+//     largest of 256 x 256, 256 x 128, 128 x 128 and 64 x 64 whose grid has
+//     at least 128 workgroups (384 for K <= 512, where a workgroup's few K
+//     steps leave it latency-bound), the 128 x 128 tile with eight waves
+//     (four for K <= 512).
 // A deep-K or tile plan that the layout refuses for a shape (a split count
 // past the partials' 32-bit range, say) falls through to the rules after it.
 Plan model_plan(int M, int N, int K) {
@@ -172,12 +174,22 @@ Plan model_plan(int M, int N, int K) {
     const bool deep = KS > 64;
     Layout l;
     const double flops = 2.0 * M * N * K;
-    const bool tile = K >= 4096 ? (M >= 384 && flops >= 12.5e9) || (M >= 256 && N >= 7168)
-                                : M >= 256 && flops >= 5.5e9 + 1.2e6 * K;
+    const bool tile = M >= 64 && (K >= 4096   ? M >= 256 || (flops >= 5e9 && (M >= 128 || N >= 7168))
+                                  : K >= 2048 ? M >= 256 || (M >= 128 && N >= 7168)
+                                              : M >= 256 && flops >= 3e9 + 0.5e6 * K);
     if (tile) {
-        const long long wgs88 = (long long)((RBm + 7) / 8) * ((RBn + 7) / 8);
-        const Plan q = wgs88 >= 200 ? Plan{8, 8, 4, 2, 1, kAmTile, 0} : Plan{8, 4, 2, 2, 1, kAmTile, 0};
-        if (plan_layout(q, M, N, K, &l) == MX_OK) return q;
+        const bool short_k = K <= 512;
+        const long long min_wgs = short_k ? 384 : 128;
+        // {mb, nb, wn, wk}: wk waves along M, wn along N
+        const Plan tiles[4] = {{8, 8, 4, 2, 1, kAmTile, 0},
+                               {8, 4, 2, 2, 1, kAmTile, 0},
+                               {4, 4, short_k ? 2 : 4, 2, 1, kAmTile, 0},
+                               {2, 2, 2, 2, 1, kAmTile, 0}};
+        for (int i = 0; i < 4; ++i) {
+            const Plan& q = tiles[i];
+            const long long wgs = (long long)((RBm + q.mb - 1) / q.mb) * ((RBn + q.nb - 1) / q.nb);
+            if ((wgs >= min_wgs || i == 3) && plan_layout(q, M, N, K, &l) == MX_OK) return q;
+        }
     }
     if (deep && (RBm == 1 || (RBm == 2 && N >= 7168) || (RBm <= 4 && N <= 2112))) {
         Plan q{1, 1, 4, 4, 1, kAmShared, 0};

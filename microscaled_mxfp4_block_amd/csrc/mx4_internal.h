@@ -131,11 +131,18 @@ size_t shared_lds_bytes(const Plan& plan, int steps_per_split);
 // The K-looped tiled kernels of the tile mode (mx4_tile.hip): a workgroup
 // tile of plan.mb x plan.nb blocks over the whole of K, plan.wk waves along
 // M and plan.wn along N, (mb, nb, wk, wn) in {(8, 8, 2, 4), (4, 8, 2, 2),
-// (8, 4, 2, 2)}; splits 1.
+// (8, 4, 2, 2), (4, 4, 2, 2), (4, 4, 2, 4), (2, 2, 2, 2)}; splits 1.
 GemmKernelFn find_tile_kernel(const Plan& plan);
 size_t tile_lds_bytes(const Plan& plan);
-// Tile-mode workgroups one XCD runs at once: its 32 CUs hold one each (LDS).
-constexpr int kTileWgsPerXcd = 32;
+// Tile-mode workgroups one XCD runs at once: its 32 CUs each hold as many
+// as their 160 KiB of LDS and 32 wave slots allow (one 256 x 256 or
+// 256 x 128 tile, two 128 x 128, four 64 x 64).
+inline int tile_wgs_per_xcd(size_t lds_bytes, int waves) {
+    const int by_lds = (int)((160u * 1024u) / (lds_bytes > 0 ? lds_bytes : 1));
+    const int by_waves = 32 / (waves > 0 ? waves : 1);
+    const int per_cu = by_lds < by_waves ? by_lds : by_waves;
+    return 32 * (per_cu > 1 ? per_cu : 1);
+}
 
 // Placement of the shared kernel's tiles on the 8 XCDs.  The dispatcher
 // hands the workgroups of a grid, in x-major order, to XCD (linear id mod 8),

@@ -11,9 +11,13 @@
 // so both operands arrive as 1 KiB MFMA operand tiles and 256-byte scale
 // words.
 //
-// Where M is large the work is MFMA-bound, not weight-bound, and the kernel
-// is the classic tiled GEMM: a workgroup owns 32 MB rows x 32 NB columns of
-// C over the whole of K and walks K one 64-K step at a time.  Each step's
+// Once M reaches a few hundred rows the work is MFMA-bound, not weight-bound,
+// and the kernel is the classic tiled GEMM: a workgroup owns 32 MB rows x
+// 32 NB columns of C over the whole of K and walks K one 64-K step at a time
+// (tiles from 64 x 64 to 256 x 256: the small ones give a grid of enough
+// workgroups to fill the chip where M or N is short, so the same kernel also
+// serves M from 64 up where the weight is re-read from L2 a few times
+// instead of once).  Each step's
 // operand tiles (MB of A, NB of B) and their scale words go straight from
 // memory into a ring of S LDS stages (gfx950 buffer loads to LDS, issued S
 // steps ahead); its WM x WN waves each read the fragments of their TM x TN
@@ -344,6 +348,12 @@ GemmKernelFn find_tile_kernel(const Plan& plan) {
         return gemm_tile_kernel<4, 8, 2, 2, kTileStages, kTileSync>;
     if (plan.mb == 8 && plan.nb == 4 && plan.wk == 2 && plan.wn == 2)
         return gemm_tile_kernel<8, 4, 2, 2, kTileStages, kTileSync>;
+    if (plan.mb == 4 && plan.nb == 4 && plan.wk == 2 && plan.wn == 2)
+        return gemm_tile_kernel<4, 4, 2, 2, kTileStages, kTileSync>;
+    if (plan.mb == 4 && plan.nb == 4 && plan.wk == 2 && plan.wn == 4)
+        return gemm_tile_kernel<4, 4, 2, 4, kTileStages, kTileSync>;
+    if (plan.mb == 2 && plan.nb == 2 && plan.wk == 2 && plan.wn == 2)
+        return gemm_tile_kernel<2, 2, 2, 2, kTileStages, kTileSync>;
     return nullptr;
 }
 

@@ -274,15 +274,20 @@ PLANS = [
     dict(mb=8, nb=8, wn=4, wk=2, splits=1, amode=6),
     dict(mb=4, nb=8, wn=2, wk=2, splits=1, amode=6),
     dict(mb=8, nb=4, wn=2, wk=2, splits=1, amode=6),
+    dict(mb=4, nb=4, wn=2, wk=2, splits=1, amode=6),
+    dict(mb=4, nb=4, wn=4, wk=2, splits=1, amode=6),
+    dict(mb=2, nb=2, wn=2, wk=2, splits=1, amode=6),
 ]
 
 # (8192 x 8192 x 512: a 32 x 32 grid of 256 x 256 tiles, four rounds per XCD, placed per round)
-LARGE_M_SHAPES = [(1024, 4096, 4096), (2048, 7168, 2048), (384, 7168, 7168), (777, 4100, 4160), (8192, 8192, 512)]
+# M from 128 takes the 128 x 128 and 64 x 64 tiles (130 and 200: ragged M)
+LARGE_M_SHAPES = [(1024, 4096, 4096), (2048, 7168, 2048), (384, 7168, 7168), (777, 4100, 4160), (8192, 8192, 512),
+                  (256, 4096, 4096), (130, 7168, 7168), (200, 7168, 2048), (1024, 2880, 2048)]
 
 
 @pytest.mark.parametrize("shape", LARGE_M_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_large_m_takes_the_tile_mode(shape):
-    """Large-M shapes run the K-looped tile mode by the library's own plan;
+    """Shapes from M = 128 up run the K-looped tile mode by the library's own plan;
     sampled rows (the first, the last and 14 random ones) by sampled columns
     (the first 4, the last 4 and 60 random ones) of C against the oracle's
     product of exactly those rows of A and columns of B."""
@@ -377,7 +382,8 @@ STRIDE_PLANS = [None,
                 dict(mb=1, nb=2, wn=1, wk=4, splits=1, amode=4),
                 dict(mb=1, nb=1, wn=3, wk=4, splits=1, amode=5),
                 dict(mb=8, nb=4, wn=2, wk=2, splits=1, amode=6),
-                dict(mb=4, nb=8, wn=2, wk=2, splits=1, amode=6)]
+                dict(mb=4, nb=8, wn=2, wk=2, splits=1, amode=6),
+                dict(mb=2, nb=2, wn=2, wk=2, splits=1, amode=6)]
 
 
 @pytest.mark.parametrize("plan", STRIDE_PLANS, ids=lambda p: "auto" if p is None else plan_id(p))
