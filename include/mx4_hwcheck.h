@@ -54,11 +54,15 @@ int mxhw_stream_read(const void* buf_dev, unsigned bytes, int wgs, int waves, in
  * one-split grid of mtiles x ntiles workgroups (at most 2^20) whose M tile
  * costs an XCD's L2 a_tile_bytes of fetch and whose N tile b_tile_bytes,
  * with at most `conc` workgroups of an XCD running at once (0: all of them),
- * *map_out receives the placement code the kernel gets, and mt_out[lin] and
- * nt_out[lin] (host arrays of mtiles * ntiles ints) the M and N tile of the
- * workgroup with linear id lin = bx + ntiles * by.  Returns 0, or -1 for a
- * bad size, byte count or null pointer. */
-int mxhw_xcd_map(int mtiles, int ntiles, int splits, double a_tile_bytes, double b_tile_bytes, int conc,
+ * and with runs = 0 (the shared mode), 1 or 2 for whether each XCD may
+ * instead take a run of consecutive tiles in M-fastest order (placement code
+ * 128): never, in place of the dispatcher's order or of a rectangle, or only
+ * in place of a rectangle (the tile mode picks 1 or 2 by tile and K),
+ * *map_out receives the placement code the kernel gets, and
+ * mt_out[lin] and nt_out[lin] (host arrays of mtiles * ntiles ints) the M and
+ * N tile of the workgroup with linear id lin = bx + ntiles * by.  Returns 0,
+ * or -1 for a bad size, byte count, runs value or null pointer. */
+int mxhw_xcd_map(int mtiles, int ntiles, int splits, double a_tile_bytes, double b_tile_bytes, int conc, int runs,
                  int* map_out, int* mt_out, int* nt_out);
 
 #ifdef __cplusplus

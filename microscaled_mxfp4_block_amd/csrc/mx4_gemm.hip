@@ -824,8 +824,8 @@ bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
             ? p.steps_per_split |
                   (shared_xcd_map(p.mtiles, p.ntiles, p.splits, 64.0 * p.K, 32.0 * plan.nb * plan.wn * kbytes) << 8)
         : plan.amode == kAmTile
-            ? shared_xcd_map(p.mtiles, p.ntiles, 1, 32.0 * plan.mb * kbytes, 32.0 * plan.nb * kbytes,
-                             tile_wgs_per_xcd(tile_lds_bytes(plan), waves))
+            ? tile_xcd_map(p.mtiles, p.ntiles, 32.0 * plan.mb * kbytes, 32.0 * plan.nb * kbytes,
+                           tile_wgs_per_xcd(tile_lds_bytes(plan), waves), tile_runs_policy(plan.mb, plan.nb, p.K))
             : p.steps_per_split;
     *out = GemmLaunch{fn, (unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits, (unsigned)(64 * waves),
                       gemm_lds_bytes(plan, p.steps_per_split), amode_prequantises(plan.amode), steps_arg};

@@ -142,17 +142,18 @@ int mxhw_mfma_fp4(const void* a_dev, const void* b_dev, const void* sa_dev, cons
     return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
-int mxhw_xcd_map(int mtiles, int ntiles, int splits, double a_tile_bytes, double b_tile_bytes, int conc,
+int mxhw_xcd_map(int mtiles, int ntiles, int splits, double a_tile_bytes, double b_tile_bytes, int conc, int runs,
                  int* map_out, int* mt_out, int* nt_out) {
     if (mtiles < 1 || ntiles < 1 || (long long)mtiles * ntiles > (1 << 20) || splits < 1 || !(a_tile_bytes > 0.0) ||
-        !(b_tile_bytes > 0.0) || conc < 0 || !map_out || !mt_out || !nt_out)
+        !(b_tile_bytes > 0.0) || conc < 0 || runs < 0 || runs > 2 || !map_out || !mt_out || !nt_out)
         return -1;
-    const int map = mx4::shared_xcd_map(mtiles, ntiles, splits, a_tile_bytes, b_tile_bytes, conc);
+    const int map = runs ? (splits == 1 ? mx4::tile_xcd_map(mtiles, ntiles, a_tile_bytes, b_tile_bytes, conc, runs) : 0)
+                         : mx4::shared_xcd_map(mtiles, ntiles, splits, a_tile_bytes, b_tile_bytes, conc);
     *map_out = map;
     for (int by = 0; by < mtiles; ++by)
         for (int bx = 0; bx < ntiles; ++bx) {
             const int lin = bx + ntiles * by;
-            mx4::shared_tile_of(bx, by, ntiles, map, mt_out[lin], nt_out[lin]);
+            mx4::shared_tile_of(bx, by, ntiles, mtiles, map, mt_out[lin], nt_out[lin]);
         }
     return 0;
 }

@@ -169,7 +169,7 @@ gemm_shared_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* par
     const int L = tid & 63;
 
     int mt, nt;
-    shared_tile_of((int)blockIdx.x, (int)blockIdx.y, (RBn + WN * NB - 1) / (WN * NB), xcd_map, mt, nt);
+    shared_tile_of((int)blockIdx.x, (int)blockIdx.y, (RBn + WN * NB - 1) / (WN * NB), (M + 31) / 32, xcd_map, mt, nt);
     const int split = blockIdx.z;
     const int tb = split * steps_per_split;
     const int te = min(tb + steps_per_split, KS);

@@ -131,7 +131,7 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
     // the tile of this workgroup, placed on the XCDs by the placement code
     // the host passes as steps_arg (shared_tile_of; K's steps come from K)
     int mt, nt;
-    shared_tile_of((int)blockIdx.x, (int)blockIdx.y, (gb.RB + NB - 1) / NB, steps_arg, mt, nt);
+    shared_tile_of((int)blockIdx.x, (int)blockIdx.y, (gb.RB + NB - 1) / NB, (ga.RB + MB - 1) / MB, steps_arg, mt, nt);
     const int rbm0 = mt * MB, rbn0 = nt * NB;
     // Wave w loads blocks q = w LPW .. w LPW + LPW - 1 of a step, q < MB
     // being A block rbm0 + q and the rest B block rbn0 + q - MB: the 1 KiB

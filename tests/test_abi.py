@@ -576,24 +576,25 @@ def test_shared_xcd_map_places_every_tile_once_and_fetches_no_more():
         sel = np.arange(256) % 8 == x
         assert np.unique(mt[sel]).size == 4 and np.unique(nt[sel]).size == 8
     assert place(8, 32, 2, 64.0 * 1536, 96 * 816.0, 0)[0] == 0       # K splits keep the dispatcher's order
-    assert placement_hook().mxhw_xcd_map(0, 32, 1, 1.0, 1.0, 0, None, None, None) == -1
+    assert placement_hook().mxhw_xcd_map(0, 32, 1, 1.0, 1.0, 0, 0, None, None, None) == -1
+    assert placement_hook().mxhw_xcd_map(8, 32, 1, 1.0, 1.0, 0, 3, None, None, None) == -1
 
 
 def placement_hook():
     """libmx4hw.so with the argument types of its host-only placement hook."""
     hw = ctypes.CDLL(os.path.join(ROOT, "microscaled_mxfp4_block_amd", "libmx4hw.so"))
     I, P, D = ctypes.c_int, ctypes.c_void_p, ctypes.c_double
-    hw.mxhw_xcd_map.argtypes = [I, I, I, D, D, I, P, P, P]
+    hw.mxhw_xcd_map.argtypes = [I, I, I, D, D, I, I, P, P, P]
     return hw
 
 
 def xcd_placer():
     hw = placement_hook()
 
-    def place(mtiles, ntiles, splits, a_bytes, b_bytes, conc):
+    def place(mtiles, ntiles, splits, a_bytes, b_bytes, conc, runs=0):
         T = mtiles * ntiles
         mt, nt, mp = (ctypes.c_int * T)(), (ctypes.c_int * T)(), ctypes.c_int(-1)
-        assert hw.mxhw_xcd_map(mtiles, ntiles, splits, a_bytes, b_bytes, conc, ctypes.byref(mp), mt, nt) == 0
+        assert hw.mxhw_xcd_map(mtiles, ntiles, splits, a_bytes, b_bytes, conc, runs, ctypes.byref(mp), mt, nt) == 0
         return mp.value, np.frombuffer(mt, np.int32).copy(), np.frombuffer(nt, np.int32).copy()
     return place
 
@@ -613,7 +614,8 @@ def round_fetch_cost(mt, nt, a_bytes, b_bytes, conc):
 
 
 def test_tile_xcd_map_scores_rounds_when_an_xcd_runs_its_tiles_in_turn():
-    """The tile mode's placement (at most 32 workgroups of an XCD at once):
+    """The rectangles of the tile mode's placement (at most 32 workgroups of
+    an XCD at once; the runs left out):
     every tile goes to exactly one workgroup, and where the grid runs in
     several rounds per XCD the chosen rectangle fetches, round by round as
     the dispatcher runs them, no more than the rectangle chosen for an
@@ -641,6 +643,51 @@ def test_tile_xcd_map_scores_rounds_when_an_xcd_runs_its_tiles_in_turn():
         first = np.arange(1024)[sel][:32]
         assert np.unique(mt[first]).size == 8 and np.unique(nt[first]).size == 4
     assert round_fetch_cost(mt, nt, 1.0, 1.0, 32) < round_fetch_cost(*place(32, 32, 1, 1.0, 1.0, 0)[1:], 1.0, 1.0, 32)
+
+
+def test_tile_xcd_runs_cover_every_grid_and_fetch_no_more():
+    """The tile mode's placement with the runs among the candidates: for
+    every grid (tile counts not a multiple of 8 included) each tile goes to
+    exactly one workgroup; where the runs are chosen (code 128), XCD x's
+    workgroups, in dispatch order, take consecutive tiles t = nt * mtiles + mt
+    from x * q + min(x, r) on (q, r = tiles / 8, tiles mod 8); the fetches,
+    round by round as the dispatcher runs them, are never above those of the
+    placement without the runs; and 512 x 2112 (8 x 33 tiles of 64 x 64, all
+    resident) takes runs that touch at most 8 M and 5 N tiles per XCD instead
+    of 1 x 33."""
+    place = xcd_placer()
+    chosen = 0
+    for mtiles in (1, 2, 3, 4, 5, 8, 12, 16, 32):
+        for ntiles in range(1, 71):
+            for conc in (0, 32, 64, 128):
+                for a_bytes, b_bytes in ((1.0, 1.0), (2.0, 1.0), (1.0, 2.0)):
+                    T = mtiles * ntiles
+                    mp, mt, nt = place(mtiles, ntiles, 1, a_bytes, b_bytes, conc, 1)
+                    assert mt.min() >= 0 and mt.max() < mtiles and nt.min() >= 0 and nt.max() < ntiles
+                    assert np.unique(mt.astype(np.int64) * ntiles + nt).size == T, (mtiles, ntiles, mp)
+                    if mp != 128:
+                        continue
+                    chosen += 1
+                    q, r = T // 8, T % 8
+                    lin = np.arange(T)
+                    for x in range(8):
+                        t = (nt * mtiles + mt)[lin % 8 == x]
+                        start = x * q + min(x, r)
+                        assert np.array_equal(t, np.arange(start, start + t.size)), (mtiles, ntiles, x)
+                    rounds = conc if conc else T
+                    mp0, mt0, nt0 = place(mtiles, ntiles, 1, a_bytes, b_bytes, conc, 0)
+                    assert round_fetch_cost(mt, nt, a_bytes, b_bytes, rounds) <= \
+                        round_fetch_cost(mt0, nt0, a_bytes, b_bytes, rounds) + 1e-9, (mtiles, ntiles, conc, mp0)
+    assert chosen > 500
+    mp, mt, nt = place(8, 33, 1, 1.0, 1.0, 128, 1)
+    assert mp == 128
+    for x in range(8):
+        sel = np.arange(264) % 8 == x
+        assert np.unique(mt[sel]).size == 8 and np.unique(nt[sel]).size <= 5
+    assert place(8, 33, 1, 1.0, 1.0, 128, 0)[0] == 1 + 16 * 3      # 1 x 33 per XCD without the runs
+    # runs only in place of a rectangle (2): 8 x 33 takes them, 4 x 33 (no rectangle) keeps the dispatcher's order
+    assert place(8, 33, 1, 1.0, 1.0, 128, 2)[0] == 128
+    assert place(4, 33, 1, 1.0, 1.0, 128, 1)[0] == 128 and place(4, 33, 1, 1.0, 1.0, 128, 2)[0] == 0
 
 
 def test_noalloc_validates_before_any_hip_call():

@@ -280,9 +280,10 @@ PLANS = [
 ]
 
 # (8192 x 8192 x 512: a 32 x 32 grid of 256 x 256 tiles, four rounds per XCD, placed per round)
-# M from 128 takes the 128 x 128 and 64 x 64 tiles (130 and 200: ragged M)
+# M from 128 takes the 128 x 128 and 64 x 64 tiles (130 and 200: ragged M); 777 x 4100, 1024 x 2880 and
+# 512 x 2112 place runs of consecutive tiles on the XCDs (their tile counts split into no good rectangles)
 LARGE_M_SHAPES = [(1024, 4096, 4096), (2048, 7168, 2048), (384, 7168, 7168), (777, 4100, 4160), (8192, 8192, 512),
-                  (256, 4096, 4096), (130, 7168, 7168), (200, 7168, 2048), (1024, 2880, 2048)]
+                  (256, 4096, 4096), (130, 7168, 7168), (200, 7168, 2048), (1024, 2880, 2048), (512, 2112, 7168)]
 
 
 @pytest.mark.parametrize("shape", LARGE_M_SHAPES, ids=lambda s: "x".join(map(str, s)))
