@@ -143,8 +143,8 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* C, int ldc, int N, bool c
 // fourth or a half of the activation traffic).
 template <int MBLK, int NBLK, int WN, int WK, int AM, int KR, int RQ>
 __global__ void __launch_bounds__(64 * WN * WK) __attribute__((amdgpu_waves_per_eu(2)))
-gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_buf, int lda, int ldc, int M, int N, int K,
-            int steps_per_split, uint32_t* counters, int splits, int mtiles) {
+gemm_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_buf, int lda, int ldc, int M, int N,
+            int K, int steps_per_split, uint32_t* counters, int splits, int mtiles) {
     GemmParams p = {};
     {
         const OperandGeom ga = operand_geom(M, K), gb = operand_geom(N, K);
@@ -808,11 +808,13 @@ bool gemm_plan_supported(const Plan& plan) {
 
 bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
     const int per_wave = (p.steps_per_split + plan.wk - 1) / plan.wk;
+    const int stages = plan.amode == kAmTile ? tile_stages(plan, (long long)p.mtiles * p.ntiles) : 0;
     GemmFn fn = plan.amode == kAmStream   ? find_stream_kernel(plan, row_chunks(plan, p))
               : plan.amode == kAmShared ? find_shared_kernel(plan, p.steps_per_split)
-              : plan.amode == kAmTile   ? find_tile_kernel(plan)
+              : plan.amode == kAmTile   ? find_tile_kernel(plan, stages)
                                         : find_kernel(plan, gemm_kr_for(per_wave), row_chunks(plan, p));
     if (!fn) return false;
+    const size_t lds = plan.amode == kAmTile ? tile_lds_bytes(plan, stages) : gemm_lds_bytes(plan, p.steps_per_split);
     // the shared mode's workgroup is wn MFMA waves plus wk quantiser waves
     const int waves = plan.amode == kAmShared ? plan.wn + plan.wk : plan.wn * plan.wk;
     // the shared kernels take their tile placement in bits 8 and up of the
@@ -825,10 +827,10 @@ bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
                   (shared_xcd_map(p.mtiles, p.ntiles, p.splits, 64.0 * p.K, 32.0 * plan.nb * plan.wn * kbytes) << 8)
         : plan.amode == kAmTile
             ? tile_xcd_map(p.mtiles, p.ntiles, 32.0 * plan.mb * kbytes, 32.0 * plan.nb * kbytes,
-                           tile_wgs_per_xcd(tile_lds_bytes(plan), waves), tile_runs_policy(plan.mb, plan.nb, p.K))
+                           tile_wgs_per_xcd(lds, waves), tile_runs_policy(plan.mb, plan.nb, p.K))
             : p.steps_per_split;
-    *out = GemmLaunch{fn, (unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits, (unsigned)(64 * waves),
-                      gemm_lds_bytes(plan, p.steps_per_split), amode_prequantises(plan.amode), steps_arg};
+    *out = GemmLaunch{fn, (unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits, (unsigned)(64 * waves), lds,
+                      amode_prequantises(plan.amode), steps_arg};
     return true;
 }
 

@@ -132,8 +132,13 @@ size_t shared_lds_bytes(const Plan& plan, int steps_per_split);
 // The K-looped tiled kernels of the tile mode (mx4_tile.hip): a workgroup
 // tile of plan.mb x plan.nb blocks over the whole of K, plan.wk waves along
 // M and plan.wn along N, (mb, nb, wk, wn) in {(8, 8, 2, 4), (4, 8, 2, 2),
-// (8, 4, 2, 2), (4, 4, 2, 2), (4, 4, 2, 4), (2, 2, 2, 2)}; splits 1.
+// (8, 4, 2, 2), (4, 4, 2, 2), (4, 4, 2, 4), (2, 2, 2, 2)}; splits 1.  The
+// ring has 8 stages, or 16 for the 64 x 64 tile on a grid of at most 256
+// workgroups (tile_stages); the one-argument forms are the 8-stage kernels.
+int tile_stages(const Plan& plan, long long wgs);
+GemmKernelFn find_tile_kernel(const Plan& plan, int stages);
 GemmKernelFn find_tile_kernel(const Plan& plan);
+size_t tile_lds_bytes(const Plan& plan, int stages);
 size_t tile_lds_bytes(const Plan& plan);
 // Tile-mode workgroups one XCD runs at once: its 32 CUs each hold as many
 // as their 160 KiB of LDS and 32 wave slots allow (one 256 x 256 or

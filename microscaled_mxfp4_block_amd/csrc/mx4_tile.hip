@@ -339,9 +339,27 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
 // waves along N (splits 1).
 
 constexpr int kTileStages = 8;
-constexpr int kTileSync = 2;   // K steps per workgroup barrier
+constexpr int kTileDeepStages = 16;   // the 64 x 64 tile on a grid of at most one workgroup per CU
+constexpr int kTileSync = 2;          // K steps per workgroup barrier
 
-GemmKernelFn find_tile_kernel(const Plan& plan) {
+// Ring depth of a tile-mode launch of `wgs` workgroups.  The 64 x 64 tile
+// moves only 4 KiB per step, so 8 stages keep too few bytes in flight to
+// cover the load latency when a CU holds a single workgroup: there 16 stages
+// (68 KiB of LDS, two workgroups per CU) were 10-17 % faster for K >= 4096
+// and 2 % at 2048, measured against 8 over grids of 64 .. 256 workgroups.
+// With more workgroups than CUs the 8-stage ring's four workgroups per CU
+// hide the latency instead, and 16 stages were up to 9 % slower; 24 and 32
+// stages were slower than 16 everywhere, and the larger tiles gained nothing.
+int tile_stages(const Plan& plan, long long wgs) {
+    return plan.mb == 2 && plan.nb == 2 && wgs <= 256 ? kTileDeepStages : kTileStages;
+}
+
+GemmKernelFn find_tile_kernel(const Plan& plan, int stages) {
+    if (stages == kTileDeepStages)
+        return plan.mb == 2 && plan.nb == 2 && plan.wk == 2 && plan.wn == 2
+                   ? gemm_tile_kernel<2, 2, 2, 2, kTileDeepStages, kTileSync>
+                   : nullptr;
+    if (stages != kTileStages) return nullptr;
     if (plan.mb == 8 && plan.nb == 8 && plan.wk == 2 && plan.wn == 4)
         return gemm_tile_kernel<8, 8, 2, 4, kTileStages, kTileSync>;
     if (plan.mb == 4 && plan.nb == 8 && plan.wk == 2 && plan.wn == 2)
@@ -357,6 +375,10 @@ GemmKernelFn find_tile_kernel(const Plan& plan) {
     return nullptr;
 }
 
-size_t tile_lds_bytes(const Plan& plan) { return tile_lds_bytes_for(plan.mb, plan.nb, kTileStages); }
+GemmKernelFn find_tile_kernel(const Plan& plan) { return find_tile_kernel(plan, kTileStages); }
+
+size_t tile_lds_bytes(const Plan& plan, int stages) { return tile_lds_bytes_for(plan.mb, plan.nb, stages); }
+
+size_t tile_lds_bytes(const Plan& plan) { return tile_lds_bytes(plan, kTileStages); }
 
 }  // namespace mx4

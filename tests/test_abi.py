@@ -433,7 +433,7 @@ def test_tile_kernels_keep_their_ring_of_loads_in_flight():
         assert loop == expected, (name, sorted(loop), sorted(expected))
         assert not [v for k, v in waits if k > bars[-1]], name
         checked += 1
-    assert checked == 6, checked
+    assert checked == 7, checked
 
 
 def test_shapes_past_the_addressing_limit_are_refused():
@@ -707,7 +707,7 @@ def test_noalloc_validates_before_any_hip_call():
 
 @pytest.mark.parametrize("src,kname,count", [("mx4_stream.s", "gemm_stream_kernel", 42),
                                               ("mx4_shared.s", "gemm_shared_kernel", 19),
-                                              ("mx4_tile.s", "gemm_tile_kernel", 6)])
+                                              ("mx4_tile.s", "gemm_tile_kernel", 7)])
 def test_mode_kernels_preload_arguments_and_never_spill(src, kname, count):
     """The K-looped stream-mode kernels, the quantiser-wave shared-mode
     kernels and the LDS-tiled tile-mode kernels take the GEMM kernels'
