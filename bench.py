@@ -875,7 +875,8 @@ def regret_candidates(B, M, N, K):
     """Plans timed against the library's own for one grid shape: the
     register-quantising mode over wave and split counts and two N widths,
     the pre-quantising mode over its tile shapes, the LDS mode, the shared
-    mode over its MFMA and quantiser waves and splits; only those the
+    mode over its MFMA and quantiser waves and splits, the tile mode over
+    its tiles (with 2 to 4 K splits where its grid is small); only those the
     planner accepts."""
     cands = []
     for nb in (1, 2):
@@ -891,10 +892,14 @@ def regret_candidates(B, M, N, K):
         for wk in (4, 8):
             for sp in (1, 2, 4, 7, 8, 14):
                 cands.append(dict(mb=1, nb=1, wn=wn, wk=wk, splits=sp, amode=5, finish=0))
-    if M >= 32:   # the tile mode over its tiles (64 .. 256 rows)
+    if M >= 32:   # the tile mode over its tiles (64 .. 256 rows); K splits where its grid is under 256 workgroups
         for mb, nb, wk, wn in TILE_SHAPES:
             if 32 * mb <= 2 * max(M, 32):
                 cands.append(dict(mb=mb, nb=nb, wn=wn, wk=wk, splits=1, amode=6, finish=0))
+                wgs = -(-M // (32 * mb)) * -(-N // (32 * nb))
+                if K >= 2048 and wgs < 256:
+                    for sp in (2, 3, 4):
+                        cands.append(dict(mb=mb, nb=nb, wn=wn, wk=wk, splits=sp, amode=6, finish=0))
     out = []
     for p in cands:
         try:

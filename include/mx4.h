@@ -191,12 +191,13 @@ enum {
                                finish 0) */
     MX_AMODE_TILE = 6       /* a first kernel quantises A into the workspace;
                                the GEMM workgroup owns 32*mb x 32*nb of C over
-                               the whole of K and loops over K with both
+                               its K split and loops over K with both
                                operands staged in LDS, wk waves along M and
                                wn along N (the MFMA-bound regime, M from
                                64 up; (mb, nb, wk, wn) in {(8,8,2,4),
                                (4,8,2,2), (8,4,2,2), (4,4,2,2), (4,4,2,4),
-                               (2,2,2,2)}; splits 1) */
+                               (2,2,2,2)}; splits start on a multiple of 4
+                               K steps; finish 0) */
 };
 
 /* Split-K finishes of a plan (no effect when splits == 1). */

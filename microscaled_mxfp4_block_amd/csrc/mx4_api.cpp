@@ -81,18 +81,17 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
     if (plan.splits > gb.KS) return MX_EPLAN;
     Layout l;
     l.steps_per_split = (gb.KS + plan.splits - 1) / plan.splits;
-    // the shared mode's splits start on a scale word (4 steps)
-    if (plan.amode == kAmShared) l.steps_per_split = (l.steps_per_split + 3) / 4 * 4;
+    // the shared and tile modes' splits start on a scale word (4 steps)
+    if (plan.amode == kAmShared || plan.amode == kAmTile) l.steps_per_split = (l.steps_per_split + 3) / 4 * 4;
     l.splits = (gb.KS + l.steps_per_split - 1) / l.steps_per_split;  // every split non-empty
     // The stream mode loops over its K steps; the shared mode's MFMA waves
     // each hold a whole split (its kernels' own budgets, checked when the
     // kernel is resolved); the other modes hold all of a wave's steps in
     // registers at once.
     const bool stream = plan.amode == kAmStream || plan.amode == kAmShared || plan.amode == kAmTile;
-    if (plan.amode == kAmShared) {
-        if (!mx4::find_shared_kernel(plan, l.steps_per_split)) return MX_EPLAN;
-        if (plan.finish != 0 && l.splits > 1) return MX_EPLAN;   // partials go to reduce_kernel
-    }
+    if (plan.amode == kAmShared && !mx4::find_shared_kernel(plan, l.steps_per_split)) return MX_EPLAN;
+    // the shared and tile modes' partials go to reduce_kernel
+    if ((plan.amode == kAmShared || plan.amode == kAmTile) && plan.finish != 0 && l.splits > 1) return MX_EPLAN;
     if (!stream && (l.steps_per_split + plan.wk - 1) / plan.wk > mx4::kStepsPerWaveMax) return MX_EPLAN;
     // Register budget (no plan may run a kernel that spills).  kAmDirect and
     // kAmBf16 hold the raw bf16 of every fragment of the wave (16 VGPRs per K

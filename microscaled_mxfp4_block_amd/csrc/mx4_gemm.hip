@@ -802,13 +802,13 @@ size_t gemm_lds_bytes(const Plan& plan, int steps_per_split) {
 bool gemm_plan_supported(const Plan& plan) {
     if (plan.amode == kAmStream) return plan.splits >= 1 && find_stream_kernel(plan, 4) != nullptr;
     if (plan.amode == kAmShared) return plan.splits >= 1 && find_shared_kernel(plan, 8) != nullptr;
-    if (plan.amode == kAmTile) return plan.splits == 1 && find_tile_kernel(plan) != nullptr;
+    if (plan.amode == kAmTile) return plan.splits >= 1 && find_tile_kernel(plan) != nullptr;
     return plan.splits >= 1 && find_kernel(plan, 1) != nullptr;
 }
 
 bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
     const int per_wave = (p.steps_per_split + plan.wk - 1) / plan.wk;
-    const int stages = plan.amode == kAmTile ? tile_stages(plan, (long long)p.mtiles * p.ntiles) : 0;
+    const int stages = plan.amode == kAmTile ? tile_stages(plan, (long long)p.mtiles * p.ntiles * p.splits) : 0;
     GemmFn fn = plan.amode == kAmStream   ? find_stream_kernel(plan, row_chunks(plan, p))
               : plan.amode == kAmShared ? find_shared_kernel(plan, p.steps_per_split)
               : plan.amode == kAmTile   ? find_tile_kernel(plan, stages)
@@ -818,16 +818,19 @@ bool resolve_gemm(const Plan& plan, const GemmParams& p, GemmLaunch* out) {
     // the shared mode's workgroup is wn MFMA waves plus wk quantiser waves
     const int waves = plan.amode == kAmShared ? plan.wn + plan.wk : plan.wn * plan.wk;
     // the shared kernels take their tile placement in bits 8 and up of the
-    // steps-per-split argument (at most 24 steps); the tile kernels, which
-    // walk all of K, take the placement code alone
+    // steps-per-split argument (at most 24 steps); the tile kernels take the
+    // placement code in bits 0..7 (XCD placement for one split only) and the
+    // steps per split above it
     const double kbytes = p.K / 2.0 + p.K / 32.0;   // packed bytes of one row over K
     const int steps_arg =
         plan.amode == kAmShared
             ? p.steps_per_split |
                   (shared_xcd_map(p.mtiles, p.ntiles, p.splits, 64.0 * p.K, 32.0 * plan.nb * plan.wn * kbytes) << 8)
         : plan.amode == kAmTile
-            ? tile_xcd_map(p.mtiles, p.ntiles, 32.0 * plan.mb * kbytes, 32.0 * plan.nb * kbytes,
-                           tile_wgs_per_xcd(lds, waves), tile_runs_policy(plan.mb, plan.nb, p.K))
+            ? (p.splits == 1 ? tile_xcd_map(p.mtiles, p.ntiles, 32.0 * plan.mb * kbytes, 32.0 * plan.nb * kbytes,
+                                            tile_wgs_per_xcd(lds, waves), tile_runs_policy(plan.mb, plan.nb, p.K))
+                             : 0) |
+                  (p.steps_per_split << 8)
             : p.steps_per_split;
     *out = GemmLaunch{fn, (unsigned)p.ntiles, (unsigned)p.mtiles, (unsigned)p.splits, (unsigned)(64 * waves), lds,
                       amode_prequantises(plan.amode), steps_arg};

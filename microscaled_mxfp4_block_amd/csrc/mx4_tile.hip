@@ -31,7 +31,9 @@
 // of the next G steps have landed and that the stages of the steps already
 // read are free.
 // The epilogue stages each wave's bf16 tiles in the (then dead) ring and
-// stores them in 16-byte row chunks.
+// stores them in 16-byte row chunks.  Where K is split over workgroups
+// (grid z), each split walks its own run of steps and writes fp32 partials
+// that reduce_kernel sums in split order.
 #include "mx4_device.h"
 #include <type_traits>
 
@@ -104,10 +106,8 @@ template <int MB, int NB, int WM, int WN, int S, int G>
 __global__ void __launch_bounds__(64 * WM * WN)
 gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* partial_buf, int lda, int ldc, int M,
                  int N, int K, int steps_arg, uint32_t* counters, int splits, int mtiles) {
-    (void)partial_buf;
     (void)lda;
     (void)counters;
-    (void)splits;
     (void)mtiles;
     constexpr int TM = MB / WM, TN = NB / WN, NW = WM * WN;
     constexpr int OPS = MB + NB;   // operand blocks per step
@@ -122,6 +122,12 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
 
     const OperandGeom ga = operand_geom(M, K), gb = operand_geom(N, K);
     const int KS = gb.KS, KW = gb.KW;
+    // steps_arg: the placement code in bits 0..7, the K steps per split (a
+    // multiple of 4 when K is split) above them; split z takes steps
+    // t0 .. t0 + nsteps - 1 of K
+    const int xcd_map = steps_arg & 0xFF;
+    const int t0 = (int)blockIdx.z * (steps_arg >> 8);
+    const int nsteps = min(KS - t0, steps_arg >> 8);
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     uint8_t* words = lds + (size_t)S * TSTAGE;
     const int tid = threadIdx.x;
@@ -129,17 +135,18 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
     const int L = tid & 63;
     const int wm = wave / WN, wn = wave % WN;
     // the tile of this workgroup, placed on the XCDs by the placement code
-    // the host passes as steps_arg (shared_tile_of; K's steps come from K)
+    // (shared_tile_of)
     int mt, nt;
-    shared_tile_of((int)blockIdx.x, (int)blockIdx.y, (gb.RB + NB - 1) / NB, (ga.RB + MB - 1) / MB, steps_arg, mt, nt);
+    shared_tile_of((int)blockIdx.x, (int)blockIdx.y, (gb.RB + NB - 1) / NB, (ga.RB + MB - 1) / MB, xcd_map, mt, nt);
     const int rbm0 = mt * MB, rbn0 = nt * NB;
     // Wave w loads blocks q = w LPW .. w LPW + LPW - 1 of a step, q < MB
     // being A block rbm0 + q and the rest B block rbn0 + q - MB: the 1 KiB
     // tile (rb, t) of step t into tile stage t % S and, for the first step of
     // each 4-step group h, the scale word group (rb, h) into word slot
-    // h % WS, issued just before that step's tiles.  Blocks past
-    // the operand and steps past K read zeros.  Each block's resource and
-    // offsets are values set up once here.
+    // h % WS, issued just before that step's tiles (t counts the split's
+    // steps: step t is step t0 + t of K, and t0 is a multiple of 4).  Blocks
+    // past the operand and steps past the split read zeros.  Each block's
+    // resource and offsets are values set up once here.
     Rsrc rsrc[LPW];
     bool rb_live[LPW];
     uint32_t tile_base[LPW], word_base[LPW];
@@ -160,20 +167,20 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
             rsrc[i] = make_rsrc(bp, (uint32_t)gb.total_bytes);
         }
         rb_live[i] = rb < rb_end;
-        tile_base[i] = ((uint32_t)(rb * KS) * 64u + (uint32_t)L) * 16u;
-        word_base[i] = word_region + ((uint32_t)(rb * KW) * 64u + (uint32_t)L) * 4u;
+        tile_base[i] = ((uint32_t)(rb * KS + t0) * 64u + (uint32_t)L) * 16u;
+        word_base[i] = word_region + ((uint32_t)(rb * KW + (t0 >> 2)) * 64u + (uint32_t)L) * 4u;
     }
     auto issue = [&](int t, int ws) {
         if ((t & 3) == 0) {
 #pragma unroll
             for (int i = 0; i < LPW; ++i) {
-                const uint32_t woff = rb_live[i] && t < KS ? word_base[i] + (uint32_t)(t >> 2) * 256u : kOutOfRange;
+                const uint32_t woff = rb_live[i] && t < nsteps ? word_base[i] + (uint32_t)(t >> 2) * 256u : kOutOfRange;
                 bload4_lds(rsrc[i], words + (size_t)ws * WGROUP + (wave * LPW + i) * kTileWordBytes, woff);
             }
         }
 #pragma unroll
         for (int i = 0; i < LPW; ++i) {
-            const uint32_t toff = rb_live[i] && t < KS ? tile_base[i] + (uint32_t)t * 1024u : kOutOfRange;
+            const uint32_t toff = rb_live[i] && t < nsteps ? tile_base[i] + (uint32_t)t * 1024u : kOutOfRange;
             bload16_lds(rsrc[i], lds + (size_t)(t % S) * TSTAGE + (wave * LPW + i) * kTileOpBytes, toff);
         }
     };
@@ -227,7 +234,7 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
     read_tiles(0, cur);
     read_words(0, cur);
     int ws_read = 0;    // word slot of the group being read
-    const int groups = (KS + 3) / 4;
+    const int groups = (nsteps + 3) / 4;
     // one K step at position U of its 4-step group (U fixes the sync, the
     // wait count, the scale byte and whether the next group's words are read)
     auto step = [&](int t, auto uc) {
@@ -288,12 +295,32 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
     // n = 32 (rbn0 + wn TN + j) + 8 (e / 4) + 4 (L / 32) + e % 4.
     wait_vmcnt<0>();
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    const int m_lane = L & 31;
+    const int n_lane = 4 * (L >> 5);
+    if (splits > 1) {
+        // a split's fp32 partials, [split][m][n] with row stride 32 RB(N)
+        // (reduce_kernel sums them in split order): 4 consecutive n a lane
+        const int ldp = gb.RB * kRowBlock;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = (rbm0 + wm * TM + i) * kRowBlock + m_lane;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+                const int nb = rbn0 + wn * TN + j;
+                if (m >= M || nb >= gb.RB) continue;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const f32x4 v = {acc[i][j][4 * r], acc[i][j][4 * r + 1], acc[i][j][4 * r + 2], acc[i][j][4 * r + 3]};
+                    *(f32x4*)(partial_buf + ((size_t)blockIdx.z * M + m) * ldp + nb * kRowBlock + 8 * r + n_lane) = v;
+                }
+            }
+        }
+        return;
+    }
     constexpr int WC = TN * kRowBlock;   // columns of a wave's row of blocks
     constexpr int WROW = WC + 8;          // bf16 per staged row (16-byte pad)
     static_assert((size_t)NW * kRowBlock * WROW * 2 <= (size_t)S * TSTAGE, "stages fit the ring");
     uint16_t* wst = (uint16_t*)(lds + (size_t)wave * kRowBlock * WROW * 2);
-    const int m_lane = L & 31;
-    const int n_lane = 4 * (L >> 5);
     const int n_base = (rbn0 + wn * TN) * kRowBlock;
     const bool vec16 = ((uintptr_t)C % 16 == 0) && (ldc % 8 == 0);
 #pragma unroll

@@ -186,7 +186,7 @@ def test_explicit_plan_rejections():
            dict(mb=1, nb=1, wn=1, wk=4, splits=1000, amode=1),   # more splits than K steps
            dict(mb=1, nb=1, wn=1, wk=8, splits=1, amode=1),      # 14 K steps per wave > register budget
            dict(mb=2, nb=1, wn=1, wk=16, splits=1, amode=0),     # activation slice over the 160 KiB LDS
-           dict(mb=8, nb=8, wn=4, wk=2, splits=2, amode=6),      # tile mode: one split
+           dict(mb=8, nb=8, wn=4, wk=2, splits=2, amode=6, finish=1),   # tile mode: reduce_kernel finish only
            dict(mb=8, nb=8, wn=2, wk=4, splits=1, amode=6),      # tile mode: no such wave split
            dict(mb=2, nb=1, wn=1, wk=8, splits=1, amode=6)]      # tile mode: no such tile
     for p in bad:

@@ -277,6 +277,8 @@ PLANS = [
     dict(mb=4, nb=4, wn=2, wk=2, splits=1, amode=6),
     dict(mb=4, nb=4, wn=4, wk=2, splits=1, amode=6),
     dict(mb=2, nb=2, wn=2, wk=2, splits=1, amode=6),
+    dict(mb=2, nb=2, wn=2, wk=2, splits=3, amode=6),
+    dict(mb=8, nb=4, wn=2, wk=2, splits=2, amode=6),
 ]
 
 # (8192 x 8192 x 512: a 32 x 32 grid of 256 x 256 tiles, four rounds per XCD, placed per round)
@@ -384,7 +386,8 @@ STRIDE_PLANS = [None,
                 dict(mb=1, nb=1, wn=3, wk=4, splits=1, amode=5),
                 dict(mb=8, nb=4, wn=2, wk=2, splits=1, amode=6),
                 dict(mb=4, nb=8, wn=2, wk=2, splits=1, amode=6),
-                dict(mb=2, nb=2, wn=2, wk=2, splits=1, amode=6)]
+                dict(mb=2, nb=2, wn=2, wk=2, splits=1, amode=6),
+                dict(mb=4, nb=4, wn=4, wk=2, splits=2, amode=6)]
 
 
 @pytest.mark.parametrize("plan", STRIDE_PLANS, ids=lambda p: "auto" if p is None else plan_id(p))
@@ -431,6 +434,13 @@ def test_split_k_deterministic_and_consistent():
     ref = oracle.gemm(inputs.bits(A), inputs.bits(Bm))
     assert_c_close(c1, ref, "split %d" % plan["splits"])
     assert_c_close(c3, ref, "split 4")
+    # the tile mode's K splits (4 steps a split start): deterministic, and the
+    # same C as its one-split plan up to the fp32 order of the partial sums
+    tile = dict(mb=2, nb=2, wn=2, wk=2, splits=5, amode=6, finish=0)
+    c4 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=tile))
+    c5 = gpu_bits(B.mx_gemm(Ad, packed, N, plan=tile))
+    np.testing.assert_array_equal(c4, c5)
+    assert_c_close(c4, ref, "tile split 5")
 
 
 def test_gemm_streams_and_reuse_of_workspace():

@@ -162,6 +162,7 @@ PLANS = [
     dict(mb=8, nb=4, wn=2, wk=2, splits=1, amode=6),
     dict(mb=4, nb=4, wn=4, wk=2, splits=1, amode=6),
     dict(mb=2, nb=2, wn=2, wk=2, splits=1, amode=6),
+    dict(mb=2, nb=2, wn=2, wk=2, splits=2, amode=6),
 ]
 
 SHAPES = [(5, 352), (13, 1088), (40, 2048), (70, 1536)]   # (M, K); N = K
