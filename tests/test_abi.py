@@ -195,6 +195,16 @@ def test_explicit_plan_rejections():
         assert e.value.code == B.MX_EPLAN
 
 
+def test_tile_splits_take_the_reduction_kernel():
+    """The tile mode splits K at multiples of 4 steps, its partials summed by
+    reduce_kernel; its plans with the last-arrival finish are refused."""
+    plan = dict(mb=2, nb=2, wn=2, wk=2, splits=3, amode=6, finish=0)
+    assert B.mx_gemm_workspace_bytes(130, 2112, 7168, plan) >= 3 * 130 * 2112 * 4
+    with pytest.raises(B.MxError) as e:
+        B.mx_gemm_workspace_bytes(130, 2112, 7168, dict(plan, finish=1))
+    assert e.value.code == B.MX_EPLAN
+
+
 def test_binding_without_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(B, "_lib", None)
     monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
