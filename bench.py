@@ -628,12 +628,13 @@ def measure_side_ops(torch, B, inputs):
 
 # ---------------------------------------------------------------------------
 # Large M: shapes where the contraction, not the weight stream, bounds the
-# call (the tile mode's regime, from 64 x 64 tiles at 256 and 512 rows to
-# 256 x 256 tiles).  One set of buffers per shape, called back to back (at
-# these sizes a call does far more MFMA work than it moves bytes).
+# call (the tile mode's regime, from 64 x 64 tiles at 128 to 512 rows, the
+# first on a grid small enough for the 16-stage ring, to 256 x 256 tiles).
+# One set of buffers per shape, called back to back (at these sizes a call
+# does far more MFMA work than it moves bytes).
 
-LARGE_M_SHAPES = [(256, 7168, 7168), (512, 2112, 7168), (1024, 4096, 4096), (2048, 7168, 2048), (4096, 4096, 4096),
-                  (8192, 8192, 8192)]
+LARGE_M_SHAPES = [(128, 2112, 7168), (256, 7168, 7168), (512, 2112, 7168), (1024, 4096, 4096), (2048, 7168, 2048),
+                  (4096, 4096, 4096), (8192, 8192, 8192)]
 
 
 def _large_name(M, N, K):
