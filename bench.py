@@ -215,6 +215,43 @@ def stream_floor(torch, hw, st, B):
     return {"us": round(us, 3), "bytes": nbytes, "workgroups": wgs, "waves": waves, "gemm_m_tiles": mtiles}
 
 
+# Streaming-read reference on one packed weight at several grids: the HBM
+# rate a grid of that many workgroups can pull, whatever the kernel does.
+STREAM_GRIDS = ((112, 4, 4), (112, 4, 16), (224, 4, 16), (256, 4, 16), (512, 4, 8), (1024, 4, 4), (2048, 4, 4),
+                (1024, 8, 8))
+
+
+def stream_rate_by_grid(torch, B, inputs, hw, N=7168, K=7168):
+    """profiles/stream_rate_by_grid.md: graph-replay time of the streaming-read
+    reference over the packed N x K weight (copies rotating over >= 512 MiB),
+    workgroup g reading the g-th of `wgs` equal pieces with `waves` waves and
+    `lpl` 16-byte loads in flight per lane (the best of three runs)."""
+    gen = torch.Generator("cpu").manual_seed(3)
+    P0 = B.mx_pack_weight(inputs.bf16_randn(N, K, gen).to("cuda:0"))
+    nbytes = P0.numel()
+    copies = max(4, -(-(512 << 20) // nbytes))
+    Ps = [P0] + [P0.clone() for _ in range(copies - 1)]
+    lines = ["# HBM streaming rate by grid", "",
+             "`python3 bench.py --stream-rate`: the streaming-read reference kernel (`mxhw_stream_read`, 128-bit "
+             "non-temporal buffer loads, no arithmetic) over the packed %d x %d weight (%d bytes), copies rotating "
+             "over >= 512 MiB, HIP-graph replay, best of three runs. Workgroup g reads the g-th of `wgs` equal "
+             "pieces." % (N, K, nbytes), "",
+             "| workgroups | waves | loads in flight per lane | us | TB/s |", "|---|---|---|---|---|"]
+    for wgs, waves, lpl in STREAM_GRIDS:
+        chunk = -(-(-(-nbytes // wgs)) // 16) * 16
+        out = torch.empty(wgs * waves, dtype=torch.int32, device="cuda:0")
+
+        def call(i, stream):
+            if hw.mxhw_stream_read(Ps[i % copies].data_ptr(), nbytes, wgs, waves, lpl, chunk, chunk, 0,
+                                   out.data_ptr(), stream):
+                raise RuntimeError("mxhw_stream_read failed")
+        us = min(graph_time(torch, call, copies, min_seconds=0.05) for _ in range(3))
+        lines.append("| %d | %d | %d | %.2f | %.2f |" % (wgs, waves, lpl, us, nbytes / us / 1e6))
+        print(lines[-1], file=sys.stderr, flush=True)
+    with open(os.path.join(ROOT, "profiles", "stream_rate_by_grid.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def launch_floor(torch, hw):
     """A near-empty kernel (one wave reading 16 bytes), graph-replayed."""
     buf = torch.zeros(256, dtype=torch.uint8, device="cuda:0")
@@ -1060,6 +1097,9 @@ def main():
                          "instead of profiles/plan_regret.md")
     ap.add_argument("--regret-merge", nargs="+", metavar="JSON",
                     help="no GPU: profiles/plan_regret.md from --regret-out parts (in grid order)")
+    ap.add_argument("--stream-rate", action="store_true",
+                    help="the streaming-read reference over a 7168 x 7168 packed weight at several grids; writes "
+                         "profiles/stream_rate_by_grid.md")
     ap.add_argument("--stats-md", nargs=2, metavar=("STATS_CSV", "COMMAND"),
                     help="no GPU: profiles/bench_kernel_stats.md from a rocprofv3 --stats kernel_stats.csv")
     args = ap.parse_args()
@@ -1094,6 +1134,9 @@ def main():
 
     if args.profile:
         profile_run(torch, B, inputs, hw, args.profile)
+        return
+    if args.stream_rate:
+        stream_rate_by_grid(torch, B, inputs, hw)
         return
     if args.profile_large_m:
         profile_large_m(torch, B, inputs, hw, args.profile_large_m)
