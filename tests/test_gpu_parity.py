@@ -285,12 +285,13 @@ PLANS = [
 # M from 128 takes the 128 x 128 and 64 x 64 tiles (130 and 200: ragged M); 777 x 4100, 1024 x 2880 and
 # 512 x 2112 place runs of consecutive tiles on the XCDs (their tile counts split into no good rectangles)
 LARGE_M_SHAPES = [(1024, 4096, 4096), (2048, 7168, 2048), (384, 7168, 7168), (777, 4100, 4160), (8192, 8192, 512),
-                  (256, 4096, 4096), (130, 7168, 7168), (200, 7168, 2048), (1024, 2880, 2048), (512, 2112, 7168)]
+                  (256, 4096, 4096), (130, 7168, 7168), (200, 7168, 2048), (1024, 2880, 2048), (512, 2112, 7168),
+                  (96, 3072, 4096), (128, 2112, 5120)]
 
 
 @pytest.mark.parametrize("shape", LARGE_M_SHAPES, ids=lambda s: "x".join(map(str, s)))
 def test_large_m_takes_the_tile_mode(shape):
-    """Shapes from M = 128 up run the K-looped tile mode by the library's own plan;
+    """Shapes from M = 96 up run the K-looped tile mode by the library's own plan;
     sampled rows (the first, the last and 14 random ones) by sampled columns
     (the first 4, the last 4 and 60 random ones) of C against the oracle's
     product of exactly those rows of A and columns of B."""
