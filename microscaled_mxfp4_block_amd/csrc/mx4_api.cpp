@@ -156,12 +156,12 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 //     mode takes at least 2 splits: the N tiles alone leave most CUs idle.
 //   - the tile mode (activation quantised once, K-looped tiles of both
 //     operands), from the sweeps over the grid and M = 256 .. 2048 with its
-//     tiles among the candidates: from M = 64; with K >= 4096 past M = 64
+//     tiles among the candidates: from M = 64; with K > 2048 past M = 64
 //     at N >= 1536 (the 64 x 64 tile with its deeper ring on a small grid:
-//     11-42 % faster than the other modes at M = 96 .. 192, K = 4096 and
+//     11-48 % faster than the other modes at M = 96 .. 192, K = 2560 ..
 //     5120, N = 1536 .. 4096, but 25 % slower at M = 64), or at
-//     2MNK >= 5 GFLOP with N >= 7168; with K from 2048 from M = 256, or
-//     from M = 128 at N >= 7168; with a shorter K from
+//     2MNK >= 5 GFLOP with N >= 7168; at K = 2048 from M = 256, or from
+//     M = 128 at N >= 7168; with a shorter K from
 //     M = 256 at 2MNK >= 3 GFLOP + 0.5 MFLOP per unit of K.  The tile: the
 //     largest of 256 x 256, 256 x 128, 128 x 128 and 64 x 64 whose grid has
 //     at least 128 workgroups (384 for K <= 512, where a workgroup's few K
@@ -176,7 +176,7 @@ Plan model_plan(int M, int N, int K) {
     const bool deep = KS > 64;
     Layout l;
     const double flops = 2.0 * M * N * K;
-    const bool long_k = K >= 4096, mid_k = K >= 2048;
+    const bool long_k = K > 2048, mid_k = K == 2048;
     const bool tile =
         M >= 64 && (long_k  ? M >= 256 || (M > 64 && N >= 1536) || (flops >= 5e9 && N >= 7168)
                     : mid_k ? M >= 256 || (M >= 128 && N >= 7168)

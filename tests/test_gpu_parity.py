@@ -286,7 +286,7 @@ PLANS = [
 # 512 x 2112 place runs of consecutive tiles on the XCDs (their tile counts split into no good rectangles)
 LARGE_M_SHAPES = [(1024, 4096, 4096), (2048, 7168, 2048), (384, 7168, 7168), (777, 4100, 4160), (8192, 8192, 512),
                   (256, 4096, 4096), (130, 7168, 7168), (200, 7168, 2048), (1024, 2880, 2048), (512, 2112, 7168),
-                  (96, 3072, 4096), (128, 2112, 5120)]
+                  (96, 3072, 4096), (128, 2112, 5120), (160, 2880, 3072)]
 
 
 @pytest.mark.parametrize("shape", LARGE_M_SHAPES, ids=lambda s: "x".join(map(str, s)))
