@@ -54,7 +54,7 @@ const TableEntry kTable[] = {
     {32, 2880, 512, {1, 1, 1, 4, 1, 2, 0}},
     {16, 2112, 7168, {1, 1, 3, 4, 7, 5, 0}},
     {64, 7168, 2048, {1, 2, 1, 8, 1, 2, 0}},
-    {256, 3072, 1536, {1, 1, 3, 8, 1, 5, 0}},
+    {256, 3072, 1536, {1, 1, 3, 4, 1, 5, 0}},
 };
 
 int pow2_floor(int x) {
