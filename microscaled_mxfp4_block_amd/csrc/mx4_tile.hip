@@ -1,5 +1,5 @@
 // mx4_tile.hip -- K-looped, LDS-pipelined block-scaled MXFP4 GEMM for gfx950
-// (MI355X) at large M: the activation mode MX_AMODE_TILE.
+// (MI355X) on MFMA-bound shapes: the activation mode MX_AMODE_TILE.
 //
 //   C[M,N] = bf16_RNE( sum_k deq(A)[m,k] * deq(B)[n,k] )   (fp32 accumulation)
 //
@@ -11,21 +11,21 @@
 // so both operands arrive as 1 KiB MFMA operand tiles and 256-byte scale
 // words.
 //
-// Once M reaches a few hundred rows the work is MFMA-bound, not weight-bound,
-// and the kernel is the classic tiled GEMM: a workgroup owns 32 MB rows x
-// 32 NB columns of C over the whole of K and walks K one 64-K step at a time
-// (tiles from 64 x 64 to 256 x 256: the small ones give a grid of enough
-// workgroups to fill the chip where M or N is short, so the same kernel also
-// serves M from 64 up where the weight is re-read from L2 a few times
-// instead of once).  Each step's
-// operand tiles (MB of A, NB of B) and their scale words go straight from
-// memory into a ring of S LDS stages (gfx950 buffer loads to LDS, issued S
-// steps ahead); its WM x WN waves each read the fragments of their TM x TN
-// blocks (TM = MB / WM, TN = NB / WN) from the stage one step ahead, into
-// registers, and run TM x TN MFMAs, so every operand tile feeds several
-// MFMAs from LDS and a wave's LDS reads overlap its MFMAs.  Every wave issues the
-// same number of loads per step (steps past K load from an offset past the
-// buffer and read zeros), so the wait for a step is a compile-time count.
+// Where M is large the work is MFMA-bound, not weight-bound, and the kernel
+// is the classic tiled GEMM: a workgroup owns 32 MB rows x 32 NB columns of
+// C over the whole of K and walks K one 64-K step at a time.  Tiles run from
+// 64 x 64 to 256 x 256; the small ones give a grid of enough workgroups
+// where M or N is short, so the same kernel also serves M from 96 up at
+// deep K, re-reading the weight from L2 a few times instead of once.  Each
+// step's operand tiles (MB of A, NB of B) and their scale words go straight
+// from memory into a ring of S LDS stages (gfx950 buffer loads to LDS,
+// issued S steps ahead); its WM x WN waves each read the fragments of their
+// TM x TN blocks (TM = MB / WM, TN = NB / WN) from the stage one step ahead,
+// into registers, and run TM x TN MFMAs, so every operand tile feeds
+// several MFMAs from LDS and a wave's LDS reads overlap its MFMAs.  Every
+// wave issues the same number of loads per step (steps past K load from an
+// offset past the buffer and read zeros), so the wait for a step is a
+// compile-time count.
 // One barrier every G steps, with no memory fence (a fence would wait for
 // the loads of the steps in flight), tells the waves that every wave's loads
 // of the next G steps have landed and that the stages of the steps already
@@ -310,7 +310,8 @@ gemm_tile_kernel(const void* a_src, const uint8_t* bp, uint16_t* C, float* parti
                 if (m >= M || nb >= gb.RB) continue;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const f32x4 v = {acc[i][j][4 * r], acc[i][j][4 * r + 1], acc[i][j][4 * r + 2], acc[i][j][4 * r + 3]};
+                    const f32x4 v = {acc[i][j][4 * r], acc[i][j][4 * r + 1], acc[i][j][4 * r + 2],
+                                     acc[i][j][4 * r + 3]};
                     *(f32x4*)(partial_buf + ((size_t)blockIdx.z * M + m) * ldp + nb * kRowBlock + 8 * r + n_lane) = v;
                 }
             }
