@@ -169,6 +169,19 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 //     (four for K <= 512).
 // A deep-K or tile plan that the layout refuses for a shape (a split count
 // past the partials' 32-bit range, say) falls through to the rules after it.
+// The shared mode's MFMA waves (N tiles of 3 or 4 N blocks) for a grid of
+// RBm x RBn / wn workgroups that runs in one round on the 256 CUs, one a CU,
+// with no ragged N tile: three waves when they qualify, else four, else 0.
+// Measured at 160 .. 448 rows, K = 1024 and 1536: a grid that needs a
+// second round costs 1.6x (7.6-7.7 against 4.8 us at 288 x 3072 x 1536),
+// and from 5 M blocks such a plan was 35-38 % faster than the register
+// modes the model took before.
+int shared_round_wn(int RBm, int RBn) {
+    for (int wn = 3; wn <= 4; ++wn)
+        if (RBn % wn == 0 && (long long)RBm * (RBn / wn) <= 256) return wn;
+    return 0;
+}
+
 Plan model_plan(int M, int N, int K) {
     const OperandGeom ga = mx4::operand_geom(M, K);
     const OperandGeom gb = mx4::operand_geom(N, K);
@@ -210,22 +223,25 @@ Plan model_plan(int M, int N, int K) {
         if (plan_layout(q, M, N, K, &l) == MX_OK) return q;
     }
     // quantiser waves for the whole workgroup: at least 8 M blocks, or 4
-    // with a short K or a wide N, or 2 with both, when the split's K fits
-    // their budget
-    const bool shared =
-        KS <= 24 && (RBm >= 8 || (RBm >= 4 && (KS <= 8 || N >= 7168)) || (RBm >= 2 && KS <= 8 && N >= 7168));
+    // with a short K or a wide N, or 2 with both, or 5 to 7 where the grid
+    // fits one round on the 256 CUs with N tiles of 3 or 4 whole N blocks
+    // (shared_round_wn), when the split's K fits their budget
+    const int round_wn = shared_round_wn(RBm, RBn);
+    const bool shared = KS <= 24 && (RBm >= 8 || (RBm >= 5 && round_wn > 0) || (RBm >= 4 && (KS <= 8 || N >= 7168)) ||
+                                     (RBm >= 2 && KS <= 8 && N >= 7168));
     const bool pre = !shared && RBm >= 4 && KS > 8 && (RBm > 4 || N >= 7168 || KS > 32);
     Plan p;
     p.finish = 0;
     p.splits = 1;
     p.wk = KS <= 8 ? pow2_floor(KS >= 8 ? 4 : (KS + 1) / 2) : 8;
     if (shared) {
-        // three MFMA waves when the N blocks divide by 3 (no ragged tile),
-        // else four; four quantiser waves for a short K from 12 to 31 M blocks
+        // the MFMA waves of shared_round_wn, else three when the N blocks
+        // divide by 3 (no ragged tile), else four; four quantiser waves for a
+        // short K from 12 to 31 M blocks
         p.amode = kAmShared;
         p.mb = 1;
         p.nb = 1;
-        p.wn = RBn % 3 == 0 ? 3 : 4;
+        p.wn = round_wn > 0 ? round_wn : RBn % 3 == 0 ? 3 : 4;
         p.wk = KS <= 8 && RBm >= 12 && RBm < 32 ? 4 : 8;
         return p;
     }

@@ -310,6 +310,33 @@ def test_large_m_takes_the_tile_mode(shape):
     assert_c_close(C[np.ix_(rows, cols)], ref, "%s %s" % (shape, plan_id(plan)))
 
 
+# Between the grid's M values the shared mode runs where its grid fits one
+# round on the 256 CUs: three MFMA waves (160 x 3072), four (288 x 3072,
+# 200 x 4096: ragged M)
+ROUND_SHAPES = [((160, 3072, 1536), 3), ((288, 3072, 1536), 4), ((200, 4096, 1024), 4)]
+
+
+@pytest.mark.parametrize("case", ROUND_SHAPES, ids=lambda c: "x".join(map(str, c[0])))
+def test_mid_m_shared_mode_in_one_round(case):
+    """Off-grid M from 5 M blocks takes the shared mode with the MFMA waves
+    whose grid fits one round; sampled rows by sampled columns of C against
+    the oracle's product of exactly those rows and columns."""
+    (M, N, K), wn = case
+    plan = B.mx_gemm_plan(M, N, K)
+    assert plan["amode"] == B.MX_AMODE_SHARED and plan["wn"] == wn, plan
+    assert -(-M // 32) * (-(-N // 32) // wn) <= 256
+    say("one round", (M, N, K), plan_id(plan))
+    gen = torch.Generator("cpu").manual_seed(M + N + K)
+    A = inputs.bf16_randn(M, K, gen)
+    Bm = inputs.bf16_randn(N, K, gen)
+    C = gpu_bits(B.mx_gemm(to_dev(A), B.mx_pack_weight(to_dev(Bm)), N))
+    rng = np.random.default_rng(M + N)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.integers(0, M, 14)]))
+    cols = np.unique(np.concatenate([np.arange(4), np.arange(N - 4, N), rng.integers(0, N, 60)]))
+    ref = oracle.gemm(np.ascontiguousarray(inputs.bits(A)[rows]), np.ascontiguousarray(inputs.bits(Bm)[cols]))
+    assert_c_close(C[np.ix_(rows, cols)], ref, "%s %s" % ((M, N, K), plan_id(plan)))
+
+
 # The a16wfp4 product (amode 3) against its own oracle.
 PLANS_A16W4 = [
     dict(mb=1, nb=1, wn=1, wk=1, splits=1, amode=3),
