@@ -170,16 +170,18 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 // A deep-K or tile plan that the layout refuses for a shape (a split count
 // past the partials' 32-bit range, say) falls through to the rules after it.
 // The shared mode's MFMA waves (N tiles of 3 or 4 N blocks) for a grid of
-// RBm x RBn / wn workgroups that runs in one round on the 256 CUs, one a CU,
-// with no ragged N tile: three waves when they qualify, else four, else 0.
-// Measured at 160 .. 448 rows, K = 1024 and 1536: a grid that needs a
-// second round costs 1.6x (7.6-7.7 against 4.8 us at 288 x 3072 x 1536),
-// and from 5 M blocks such a plan was 35-38 % faster than the register
-// modes the model took before.
+// RBm x RBn / wn workgroups that runs in one round on the 256 CUs, one a CU:
+// three waves when they qualify with no ragged N tile, else four, else four
+// with a ragged last N tile, else 0.  Measured at 160 .. 448 rows, K = 1024
+// and 1536: a grid that needs a second round costs 1.6x (7.6-7.7 against
+// 4.8 us at 288 x 3072 x 1536); from 5 M blocks such a plan was 35-38 %
+// faster than the register modes the model took before, and the ragged
+// one 11-15 % faster than a second round (288 and 320 x 2880, 384 and
+// 448 x 2112).
 int shared_round_wn(int RBm, int RBn) {
     for (int wn = 3; wn <= 4; ++wn)
         if (RBn % wn == 0 && (long long)RBm * (RBn / wn) <= 256) return wn;
-    return 0;
+    return (long long)RBm * ((RBn + 3) / 4) <= 256 ? 4 : 0;
 }
 
 Plan model_plan(int M, int N, int K) {

@@ -312,8 +312,8 @@ def test_large_m_takes_the_tile_mode(shape):
 
 # Between the grid's M values the shared mode runs where its grid fits one
 # round on the 256 CUs: three MFMA waves (160 x 3072), four (288 x 3072,
-# 200 x 4096: ragged M)
-ROUND_SHAPES = [((160, 3072, 1536), 3), ((288, 3072, 1536), 4), ((200, 4096, 1024), 4)]
+# 200 x 4096: ragged M), four with a ragged last N tile (320 x 2880)
+ROUND_SHAPES = [((160, 3072, 1536), 3), ((288, 3072, 1536), 4), ((200, 4096, 1024), 4), ((320, 2880, 1536), 4)]
 
 
 @pytest.mark.parametrize("case", ROUND_SHAPES, ids=lambda c: "x".join(map(str, c[0])))
@@ -324,7 +324,7 @@ def test_mid_m_shared_mode_in_one_round(case):
     (M, N, K), wn = case
     plan = B.mx_gemm_plan(M, N, K)
     assert plan["amode"] == B.MX_AMODE_SHARED and plan["wn"] == wn, plan
-    assert -(-M // 32) * (-(-N // 32) // wn) <= 256
+    assert -(-M // 32) * -(-(-(-N // 32)) // wn) <= 256
     say("one round", (M, N, K), plan_id(plan))
     gen = torch.Generator("cpu").manual_seed(M + N + K)
     A = inputs.bf16_randn(M, K, gen)
