@@ -948,7 +948,21 @@ def regret_candidates(B, M, N, K):
     return out
 
 
-def plan_regret(torch, B, inputs, only=None, out=None, large=False):
+def random_regret_groups(count=40, seed=2024):
+    """Seeded off-grid shapes for the planner's regret: M in 1 .. 1024 (log
+    uniform), N in 256 .. 8192 (a multiple of 32, log uniform), K in 256 ..
+    8192 (a multiple of 256, log uniform), grouped by (N, K)."""
+    rng = np.random.default_rng(seed)
+    groups = {}
+    for _ in range(count):
+        M = int(round(2 ** rng.uniform(0, 10)))
+        N = 32 * int(round(2 ** rng.uniform(3, 8)))
+        K = 256 * int(round(2 ** rng.uniform(0, 5)))
+        groups.setdefault((N, K), []).append(M)
+    return [(nk, sorted(set(ms))) for nk, ms in sorted(groups.items())]
+
+
+def plan_regret(torch, B, inputs, only=None, out=None, large=False, random_groups=None):
     """Graph-replay GPU time per call of the library's plan and of the
     candidate plans for every grid shape (weights rotating over copies
     >= 256 MiB).  With `out`, every candidate's time goes to that JSON file
@@ -958,10 +972,12 @@ def plan_regret(torch, B, inputs, only=None, out=None, large=False):
     dev = "cuda:0"
     results = []
     pairs = GRID_DIM_PAIRS if only is None else [GRID_DIM_PAIRS[i] for i in only]
-    batches = GRID_BATCH
+    groups = [(nk, GRID_BATCH) for nk in pairs]
     if large:
-        pairs, batches = LARGE_REGRET_PAIRS, LARGE_REGRET_M
-    for (N, K) in pairs:
+        groups = [(nk, LARGE_REGRET_M) for nk in LARGE_REGRET_PAIRS]
+    if random_groups is not None:
+        groups = random_groups
+    for (N, K), batches in groups:
         gen = torch.Generator("cpu").manual_seed(5000 + N + K)
         P0 = B.mx_pack_weight(inputs.bf16_randn(N, K, gen).to(dev))
         copies = min(200, max(4, -(-(256 << 20) // P0.numel())))
@@ -996,17 +1012,30 @@ def plan_regret(torch, B, inputs, only=None, out=None, large=False):
     if out:
         with open(out, "w") as f:
             json.dump({"shapes": results}, f)
-    if large:
+    if random_groups is not None:
+        regret_summary(results, "`python3 bench.py --plan-regret-random`", random=True)
+    elif large:
         regret_summary(results, "`python3 bench.py --plan-regret-large`", large=True)
     elif not out:
         regret_summary(results, "`python3 bench.py --plan-regret`")
 
 
-def regret_summary(results, command, large=False):
+def regret_summary(results, command, large=False, random=False):
     """profiles/plan_regret.md from the timed shapes (without the
     per-candidate times); with `large`, profiles/plan_regret_large.md."""
     regrets = [r["regret"] for r in results]
     geo = float(np.exp(np.mean(np.log(regrets)))) if regrets else float("nan")
+    if random:
+        lines = ["# Planner regret on seeded off-grid shapes", "",
+                 "%s: for each of %d seeded random shapes (`random_regret_groups`: M in 1 .. 1024, N in 256 .. "
+                 "8192, K in 256 .. 8192, log uniform; off the pages' grid), the HIP-graph-replay GPU time per call "
+                 "of the plan mx_gemm picks against the fastest of up to %d candidate plans (those of the grid "
+                 "sweep), weights rotating over copies of >= 256 MiB. Regret = plan time / best time; geometric "
+                 "mean %.3f, worst %.3f." % (command, len(results), max((r["candidates"] for r in results), default=0),
+                                             geo, max(regrets, default=0)),
+                 "", "| M | N | K | plan (mb nb wn wk splits amode) | us | best plan | best us | regret |",
+                 "|---|---|---|---|---|---|---|---|"]
+        return _regret_tables(results, lines, "plan_regret_random")
     if large:
         lines = ["# Planner regret at large M", "",
                  "%s: for each of the %d shapes (M = %s x six (N, K) weight shapes of the pages' grid; the grid "
@@ -1092,6 +1121,9 @@ def main():
     ap.add_argument("--plan-regret-large", action="store_true",
                     help="the same at M = 256 .. 2048 over six of the grid's weight shapes, tile plans among the "
                          "candidates; writes profiles/plan_regret_large.md")
+    ap.add_argument("--plan-regret-random", action="store_true",
+                    help="the same over 40 seeded off-grid shapes (random_regret_groups); writes "
+                         "profiles/plan_regret_random.md")
     ap.add_argument("--regret-out", default=None, metavar="JSON",
                     help="with --plan-regret: write every candidate's time to JSON (a part for --regret-merge) "
                          "instead of profiles/plan_regret.md")
@@ -1144,6 +1176,9 @@ def main():
     if args.plan_regret:
         only = None if args.plan_regret == "all" else [int(i) for i in args.plan_regret.split(",")]
         plan_regret(torch, B, inputs, only, args.regret_out)
+        return
+    if args.plan_regret_random:
+        plan_regret(torch, B, inputs, out=args.regret_out, random_groups=random_regret_groups())
         return
     if args.plan_regret_large:
         plan_regret(torch, B, inputs, out=args.regret_out, large=True)

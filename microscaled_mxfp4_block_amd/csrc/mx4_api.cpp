@@ -210,6 +210,22 @@ Plan model_plan(int M, int N, int K) {
             if ((wgs >= min_wgs || i == 3) && plan_layout(q, M, N, K, &l) == MX_OK) return q;
         }
     }
+    // N of at most 32 blocks (off the pages' grid, whose N starts at 2112):
+    // the register mode, past K = 2048 with four waves and enough K splits
+    // (at most 8) to bring the grid towards 256 workgroups, else unsplit
+    // with eight waves (four at most 12 K steps).  Over 40 seeded off-grid
+    // shapes the other rules left such grids at 9 .. 26 workgroups (1.12-1.41x
+    // the best plan at N = 288 .. 672, K = 2816 .. 6144); at K = 1024 .. 2048
+    // the splits' reduction cost more than they saved (1.25-1.52x).
+    if (RBn <= 32) {
+        Plan q{1, 1, 1, KS > 32 || KS <= 12 ? 4 : 8, 1, kAmDirect, 0};
+        if (KS > 32) {
+            const long long wgs = (long long)RBm * RBn;
+            q.splits = wgs >= 128 ? 1 : wgs >= 64 ? 2 : wgs >= 32 ? 4 : 8;
+        }
+        while (q.splits < KS && plan_layout(q, M, N, K, &l) != MX_OK) ++q.splits;
+        if (plan_layout(q, M, N, K, &l) == MX_OK) return q;
+    }
     if (deep && (RBm == 1 || (RBm == 2 && N >= 7168) || (RBm <= 4 && N <= 2112))) {
         Plan q{1, 1, 4, 4, 1, kAmShared, 0};
         if (N >= 7168 && RBm == 2) {
@@ -235,7 +251,8 @@ Plan model_plan(int M, int N, int K) {
     Plan p;
     p.finish = 0;
     p.splits = 1;
-    p.wk = KS <= 8 ? pow2_floor(KS >= 8 ? 4 : (KS + 1) / 2) : 8;
+    // (four waves at 9 .. 12 K steps: 11 % faster than eight at K = 768)
+    p.wk = KS <= 8 ? pow2_floor(KS >= 8 ? 4 : (KS + 1) / 2) : KS <= 12 ? 4 : 8;
     if (shared) {
         // the MFMA waves of shared_round_wn, else three when the N blocks
         // divide by 3 (no ragged tile), else four; four quantiser waves for a
