@@ -195,6 +195,32 @@ def test_explicit_plan_rejections():
         assert e.value.code == B.MX_EPLAN
 
 
+@pytest.mark.parametrize("shape,expect", [
+    ((160, 3072, 1536), dict(amode=5, wn=3)),              # shared mode, one round of 5 x 32 workgroups
+    ((288, 3072, 1536), dict(amode=5, wn=4)),              # four MFMA waves: 9 x 24 fits one round, 9 x 32 not
+    ((320, 2880, 1536), dict(amode=5, wn=4)),              # a ragged last N tile when only that fits one round
+    ((4, 672, 4096), dict(amode=2, wk=4, splits=8)),       # N of 21 blocks past K = 2048: split toward 256
+    ((74, 544, 1024), dict(amode=2, wk=8, splits=1)),      # ... but not at K <= 2048
+    ((4, 3456, 768), dict(amode=2, wk=4, splits=1)),       # four register waves at 12 K steps
+    ((128, 2112, 4096), dict(amode=6, mb=2, nb=2)),        # the 64 x 64 tile past M = 64 at K > 2048
+    ((64, 4096, 4096), dict(amode=2)),                     # ... not at M = 64
+])
+def test_model_rules_off_the_grid(shape, expect):
+    """The model's rules between and beyond the grid's shapes (measured in
+    graph replay against the candidate plans; host-only plan queries)."""
+    plan = B.mx_gemm_plan(*shape)
+    assert {k: plan[k] for k in expect} == expect, (shape, plan)
+
+
+def test_random_regret_shapes_are_seeded_and_in_range():
+    import bench
+    g1, g2 = bench.random_regret_groups(), bench.random_regret_groups()
+    assert g1 == g2 and sum(len(ms) for _, ms in g1) >= 35
+    for (N, K), ms in g1:
+        assert 256 <= N <= 8192 and N % 32 == 0 and 256 <= K <= 8192 and K % 256 == 0
+        assert all(1 <= m <= 1024 for m in ms)
+
+
 def test_tile_splits_take_the_reduction_kernel():
     """The tile mode splits K at multiples of 4 steps, its partials summed by
     reduce_kernel; its plans with the last-arrival finish are refused."""
