@@ -962,7 +962,7 @@ def random_regret_groups(count=40, seed=2024):
     return [(nk, sorted(set(ms))) for nk, ms in sorted(groups.items())]
 
 
-def plan_regret(torch, B, inputs, only=None, out=None, large=False, random_groups=None):
+def plan_regret(torch, B, inputs, only=None, out=None, large=False, random_groups=None, seed=2024):
     """Graph-replay GPU time per call of the library's plan and of the
     candidate plans for every grid shape (weights rotating over copies
     >= 256 MiB).  With `out`, every candidate's time goes to that JSON file
@@ -1013,29 +1013,31 @@ def plan_regret(torch, B, inputs, only=None, out=None, large=False, random_group
         with open(out, "w") as f:
             json.dump({"shapes": results}, f)
     if random_groups is not None:
-        regret_summary(results, "`python3 bench.py --plan-regret-random`", random=True)
+        cmd = "`python3 bench.py --plan-regret-random%s`" % ("" if seed == 2024 else " --regret-seed %d" % seed)
+        regret_summary(results, cmd, random=True, seed=seed)
     elif large:
         regret_summary(results, "`python3 bench.py --plan-regret-large`", large=True)
     elif not out:
         regret_summary(results, "`python3 bench.py --plan-regret`")
 
 
-def regret_summary(results, command, large=False, random=False):
+def regret_summary(results, command, large=False, random=False, seed=2024):
     """profiles/plan_regret.md from the timed shapes (without the
     per-candidate times); with `large`, profiles/plan_regret_large.md."""
     regrets = [r["regret"] for r in results]
     geo = float(np.exp(np.mean(np.log(regrets)))) if regrets else float("nan")
     if random:
         lines = ["# Planner regret on seeded off-grid shapes", "",
-                 "%s: for each of %d seeded random shapes (`random_regret_groups`: M in 1 .. 1024, N in 256 .. "
-                 "8192, K in 256 .. 8192, log uniform; off the pages' grid), the HIP-graph-replay GPU time per call "
-                 "of the plan mx_gemm picks against the fastest of up to %d candidate plans (those of the grid "
-                 "sweep), weights rotating over copies of >= 256 MiB. Regret = plan time / best time; geometric "
-                 "mean %.3f, worst %.3f." % (command, len(results), max((r["candidates"] for r in results), default=0),
-                                             geo, max(regrets, default=0)),
+                 "%s: for each of %d seeded random shapes (`random_regret_groups`, seed %d: M in 1 .. 1024, N in "
+                 "256 .. 8192, K in 256 .. 8192, log uniform; off the pages' grid), the HIP-graph-replay GPU time "
+                 "per call of the plan mx_gemm picks against the fastest of up to %d candidate plans (those of the "
+                 "grid sweep), weights rotating over copies of >= 256 MiB. Regret = plan time / best time; "
+                 "geometric mean %.3f, worst %.3f." % (command, len(results), seed,
+                                                       max((r["candidates"] for r in results), default=0), geo,
+                                                       max(regrets, default=0)),
                  "", "| M | N | K | plan (mb nb wn wk splits amode) | us | best plan | best us | regret |",
                  "|---|---|---|---|---|---|---|---|"]
-        return _regret_tables(results, lines, "plan_regret_random")
+        return _regret_tables(results, lines, "plan_regret_random" + ("" if seed == 2024 else "_seed%d" % seed))
     if large:
         lines = ["# Planner regret at large M", "",
                  "%s: for each of the %d shapes (M = %s x six (N, K) weight shapes of the pages' grid; the grid "
@@ -1124,6 +1126,9 @@ def main():
     ap.add_argument("--plan-regret-random", action="store_true",
                     help="the same over 40 seeded off-grid shapes (random_regret_groups); writes "
                          "profiles/plan_regret_random.md")
+    ap.add_argument("--regret-seed", type=int, default=2024,
+                    help="with --plan-regret-random: the seed of the shapes (other than 2024: "
+                         "profiles/plan_regret_random_seedSEED.md)")
     ap.add_argument("--regret-out", default=None, metavar="JSON",
                     help="with --plan-regret: write every candidate's time to JSON (a part for --regret-merge) "
                          "instead of profiles/plan_regret.md")
@@ -1178,7 +1183,8 @@ def main():
         plan_regret(torch, B, inputs, only, args.regret_out)
         return
     if args.plan_regret_random:
-        plan_regret(torch, B, inputs, out=args.regret_out, random_groups=random_regret_groups())
+        plan_regret(torch, B, inputs, out=args.regret_out, random_groups=random_regret_groups(seed=args.regret_seed),
+                    seed=args.regret_seed)
         return
     if args.plan_regret_large:
         plan_regret(torch, B, inputs, out=args.regret_out, large=True)

@@ -129,7 +129,7 @@ int plan_layout(const Plan& plan, int M, int N, int K, Layout* out) {
 // over the pages' shape grid (19 (N, K) weight shapes x M = 1 .. 256, up to
 // 69 candidate plans each) and to a sweep of M = 256 .. 2048 over six of its
 // weight shapes with the tile mode's plans among the candidates:
-//   - deep K (more than 64 steps) with one 32-row block of M, or up to four
+//   - deep K (more than 32 steps) with one 32-row block of M, or up to four
 //     at N <= 2112: the quantiser-wave mode with 4 quantiser waves and K
 //     split into pieces of at most 16 steps (7 splits at K = 7168), three
 //     MFMA waves when the N blocks divide by 3 and the grid stays within one
@@ -188,7 +188,7 @@ Plan model_plan(int M, int N, int K) {
     const OperandGeom ga = mx4::operand_geom(M, K);
     const OperandGeom gb = mx4::operand_geom(N, K);
     const int RBm = ga.RB, RBn = gb.RB, KS = gb.KS;
-    const bool deep = KS > 64;
+    const bool deep = KS > 32;   // K past 2048
     Layout l;
     const double flops = 2.0 * M * N * K;
     const bool long_k = K > 2048, mid_k = K == 2048;

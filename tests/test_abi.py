@@ -212,6 +212,22 @@ def test_model_rules_off_the_grid(shape, expect):
     assert {k: plan[k] for k in expect} == expect, (shape, plan)
 
 
+def test_random_regret_summary_from_synthetic_results(tmp_path, monkeypatch):
+    """The off-grid regret summary renders from synthetic sweep results, for
+    the default seed and another (its own file), without a GPU."""
+    import bench
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    (tmp_path / "profiles").mkdir()
+    plan = dict(mb=1, nb=1, wn=1, wk=4, splits=1, amode=2, finish=0)
+    res = [{"M": 4, "N": 672, "K": 4096, "plan": plan, "us": 5.0, "best_plan": plan, "best_us": 4.0, "regret": 1.25,
+            "candidates": 3, "all": []}]
+    bench.regret_summary(res, "`cmd`", random=True)
+    bench.regret_summary(res, "`cmd`", random=True, seed=7)
+    text = (tmp_path / "profiles" / "plan_regret_random.md").read_text()
+    assert "seed 2024" in text and "geometric mean 1.250, worst 1.250" in text and "| 4 | 672 | 4096 |" in text
+    assert "seed 7" in (tmp_path / "profiles" / "plan_regret_random_seed7.md").read_text()
+
+
 def test_random_regret_shapes_are_seeded_and_in_range():
     import bench
     g1, g2 = bench.random_regret_groups(), bench.random_regret_groups()
